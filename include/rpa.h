@@ -1,0 +1,191 @@
+/*
+ * rpa.h -- C ABI of a gfx950 (MI355X) library for batched attention over a
+ * paged KV cache with a ragged batch of sequences.
+ *
+ * The operation (flashinfer issue #323, "How are prefill and decode kernels
+ * different?": the BatchPrefillWithPagedKVCacheWrapper repro, its tensors and
+ * its begin_forward / forward / end_forward lifecycle):
+ *
+ *   A batch of `batch` sequences.  Sequence b brings q_len[b] new query tokens
+ *   (1 for decode, more for prefill or for a suffix after a cached prefix),
+ *   packed in Q at rows qo_indptr[b] .. qo_indptr[b+1]-1.  Its kv_len[b]
+ *   cached tokens live in pages of `page_size` (16) token slots:
+ *     n_pages = kv_page_indptr[b+1] - kv_page_indptr[b]
+ *     kv_len  = n_pages == 0 ? 0 : (n_pages - 1) * page_size + kv_last_page_len[b]
+ *     token t < kv_len is in page kv_page_indices[kv_page_indptr[b] + t / page_size],
+ *     slot t % page_size.
+ *   The cache is [num_pages][2][page_size][num_kv_heads][head_dim] (per page:
+ *   K then V, each "NHD"), in the same dtype as Q.
+ *
+ *   The queries are the last q_len tokens of the sequence: query i is at
+ *   position kv_len - q_len + i, and with causal != 0 it sees keys 0..that
+ *   position (llama.cpp discussion #15958, "Pad for prefill stage?": real
+ *   tokens first, fully masked tails skipped); with causal == 0 it sees all
+ *   kv_len keys.  qo head h reads kv head h / (num_qo_heads / num_kv_heads).
+ *
+ *   O[row][h][:] = sum_j softmax_j(sm_scale * <Q[row][h], K_j>) * V_j   (input dtype,
+ *                  rounded to nearest-even from fp32)
+ *   LSE[row][h]  = ln sum_j exp(sm_scale * <Q[row][h], K_j>)             (fp32, optional)
+ *
+ * Conventions for every entry point:
+ *   - Every call returns an rpa_status; RPA_OK is 0.  rpa_last_error() returns
+ *     a thread-local message for the last non-OK status.  No C++ exception
+ *     crosses this ABI.
+ *   - "host" pointers are CPU memory read during the call only.  "device"
+ *     pointers are GPU memory the caller owns; the library borrows them and
+ *     never allocates or frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   - Kernel faults are asynchronous and surface at the caller's next
+ *     synchronisation, as usual for HIP.
+ */
+#ifndef RPA_H
+#define RPA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RPA_OK = 0,
+    RPA_E_ARG = 1,             /* NULL pointer, bad enum, negative size          */
+    RPA_E_SHAPE = 2,           /* heads / head_dim / page_size not supported      */
+    RPA_E_INDPTR = 3,          /* an indptr does not start at 0 or decreases      */
+    RPA_E_LAST_PAGE_LEN = 4,   /* kv_last_page_len outside [1, page_size]         */
+    RPA_E_QLEN_GT_KVLEN = 5,   /* a sequence has more queries than cached tokens  */
+    RPA_E_WORKSPACE = 6,       /* workspace too small or misaligned               */
+    RPA_E_UNSUPPORTED = 7,     /* valid request this build does not implement     */
+    RPA_E_HIP = 8,             /* a HIP runtime call failed (message has details) */
+    RPA_E_PAGE_OOB = 9         /* a page index outside [0, num_pages)             */
+} rpa_status;
+
+typedef enum { RPA_F16 = 0, RPA_BF16 = 1 } rpa_dtype;
+
+typedef struct {
+    int32_t num_qo_heads;   /* H_qo >= 1                                          */
+    int32_t num_kv_heads;   /* H_kv >= 1, H_qo % H_kv == 0                        */
+    int32_t head_dim;       /* 64 or 128                                          */
+    int32_t page_size;      /* 16                                                 */
+    int32_t dtype;          /* rpa_dtype of Q, the cache and O                    */
+    int32_t causal;         /* 1: queries are the last q_len positions, causal    */
+    float sm_scale;         /* <= 0 selects 1/sqrt(head_dim)                      */
+    int32_t max_kv_splits;  /* 0: planner decides; 1: never split; n: at most n   */
+    int32_t num_cus;        /* compute units the schedule targets; 0 selects 256  */
+} rpa_params;
+
+typedef struct rpa_plan rpa_plan;
+
+typedef struct {
+    int64_t num_tiles;         /* attention work items (including split pieces)   */
+    int64_t num_split_groups;  /* query tiles whose key range is split            */
+    int32_t max_splits;        /* largest split count of any query tile           */
+    int32_t block_m;           /* query rows (token, head) per tile               */
+    int32_t block_n;           /* keys per inner block                            */
+    int32_t tokens_per_tile;   /* query tokens per tile                           */
+    int64_t partial_rows;      /* fp32 partial rows the workspace holds           */
+    size_t workspace_bytes;    /* bytes rpa_plan_bind needs                       */
+    int64_t total_q;           /* query tokens of the batch                       */
+    int64_t visible_pairs;     /* sum over rows and qo heads of visible keys      */
+    int64_t kv_tokens;         /* sum of kv_len over sequences with queries       */
+} rpa_plan_info_t;
+
+/*
+ * Plan (the host half of begin_forward): validate the ragged lengths and build
+ * the work schedule.  Host-only: no HIP call is made, so it also runs where no
+ * GPU is present.  The schedule depends only on the lengths and parameters,
+ * never on page ids, so equal lengths give equal schedules.
+ *   qo_indptr_h        host int32 [batch+1]; [0] == 0, non-decreasing
+ *   kv_page_indptr_h   host int32 [batch+1]; [0] == 0, non-decreasing
+ *   kv_last_page_len_h host int32 [batch]; in [1, page_size] for a sequence with pages
+ *   out                receives a plan the caller frees with rpa_plan_destroy
+ * Errors: E_ARG, E_SHAPE, E_INDPTR, E_LAST_PAGE_LEN, E_QLEN_GT_KVLEN.
+ */
+rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                           const int32_t* kv_page_indptr_h, const int32_t* kv_last_page_len_h,
+                           rpa_plan** out);
+
+/* Summary of a plan (sizes, tile shape, work counts). */
+rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
+
+/*
+ * Copy of the plan's work items for inspection: up to `cap` records of 16
+ * int32 each into `out_h` (host), in launch order.  Fields per record:
+ *   [0] first query row, [1] query tokens, [2] position of the first query,
+ *   [3] kv_len, [4] kv_page_indptr[b], [5] kv head, [6] first key, [7] end key,
+ *   [8] first partial row (-1: writes O directly), [9] sequence, [10] split
+ *   index, [11] split count, [12..15] reserved.
+ * *n_out receives the number of records in the plan.
+ */
+rpa_status rpa_plan_tiles(const rpa_plan* plan, int32_t* out_h, int64_t cap, int64_t* n_out);
+
+/*
+ * Bind (the device half of begin_forward): upload the schedule into the
+ * caller's workspace and remember the page-index array.
+ *   kv_page_indices_d  device int32 [kv_page_indptr[batch]], borrowed until the
+ *                      plan is destroyed or bound again
+ *   num_pages          pages in the cache (rows of its leading axis); a page index
+ *                      outside [0, num_pages) is never dereferenced: the kernel
+ *                      reads zeros instead and raises the plan's error flag
+ *   workspace_d        device buffer of at least rpa_plan_info().workspace_bytes,
+ *                      256-byte aligned, borrowed until destroy or the next bind
+ *   stream             the upload is enqueued here; rpa_run must be ordered after it
+ * Errors: E_ARG, E_WORKSPACE (message states the size needed), E_HIP.
+ */
+rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64_t num_pages,
+                         void* workspace_d, size_t workspace_bytes, void* stream);
+
+/*
+ * Run (forward): attention for every query row of the plan.
+ *   q         device [total_q][num_qo_heads][head_dim], dtype of the plan
+ *   kv_cache  device [num_pages][2][page_size][num_kv_heads][head_dim], same dtype
+ *   o         device [total_q][num_qo_heads][head_dim], same dtype (written)
+ *   lse       device fp32 [total_q][num_qo_heads] (written), or NULL
+ * Enqueues one attention kernel, plus one merge kernel when the plan splits
+ * key ranges, on `stream`.  No allocation, no host<->device synchronisation.
+ * One run at a time per (plan, workspace): the partial-result region is shared.
+ * Errors: E_ARG (unbound plan, NULL pointer), E_HIP (launch failure).
+ */
+rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, void* o, float* lse,
+                   void* stream);
+
+/*
+ * Error flag of a bound plan: synchronises `stream`, then reports whether any
+ * run since the last bind met a page index outside [0, num_pages)
+ * (*flag_out = 1, and RPA_E_PAGE_OOB is returned) or not (*flag_out = 0).
+ */
+rpa_status rpa_plan_check(const rpa_plan* plan, void* stream, int32_t* flag_out);
+
+/* Free a plan's host memory.  The caller first makes sure no run using it is
+ * still in flight.  NULL is ignored. */
+void rpa_plan_destroy(rpa_plan* plan);
+
+/*
+ * Host-side check of a page table (tests and debugging): every index of every
+ * sequence inside [0, num_pages).  Host pointers only.
+ * Errors: E_ARG, E_INDPTR, E_PAGE_OOB.
+ */
+rpa_status rpa_validate_page_table(int32_t batch, const int32_t* kv_page_indptr_h,
+                                   const int32_t* kv_page_indices_h, int64_t num_pages);
+
+/* Thread-local message describing the last non-OK status ("" if none). */
+const char* rpa_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* rpa_version(void);
+
+/*
+ * Kernel timing (benchmarks): while enabled, rpa_run records a HIP event pair
+ * around each kernel it enqueues.  rpa_prof_stop synchronises those events and
+ * returns, per kernel kind (0 = attention, 1 = split merge), the number of
+ * launches and their summed duration in milliseconds.
+ */
+rpa_status rpa_prof_start(void);
+rpa_status rpa_prof_stop(int64_t counts_out[2], double ms_out[2]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RPA_H */

@@ -1,0 +1,249 @@
+"""Ragged batched attention over a paged KV cache on MI355X (gfx950).
+
+A thin ctypes binding over librpa.so (include/rpa.h): it marshals arguments
+and takes device memory and the current stream from PyTorch; every step of
+the computation runs in the library's HIP kernels.  If the library is not
+built, importing works but any call raises: there is no fallback path.
+
+Lifecycle (mirrors begin_forward / forward / end_forward of the batch
+prefill wrapper in flashinfer issue #323):
+
+    plan = Plan(qo_indptr, kv_page_indptr, kv_last_page_len,
+                num_qo_heads=64, num_kv_heads=8, head_dim=128, dtype=torch.bfloat16)
+    plan.bind(kv_page_indices_gpu, num_pages=kv_cache.shape[0])   # upload schedule
+    o, lse = plan.run(q, kv_cache, return_lse=True)                # repeatable
+    plan.close()
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librpa.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "rpa.h")
+
+STATUS = {0: "RPA_OK", 1: "RPA_E_ARG", 2: "RPA_E_SHAPE", 3: "RPA_E_INDPTR", 4: "RPA_E_LAST_PAGE_LEN",
+          5: "RPA_E_QLEN_GT_KVLEN", 6: "RPA_E_WORKSPACE", 7: "RPA_E_UNSUPPORTED", 8: "RPA_E_HIP",
+          9: "RPA_E_PAGE_OOB"}
+
+
+class RPAError(RuntimeError):
+    """A non-OK rpa_status; .status holds its name."""
+
+    def __init__(self, status: int, message: str):
+        self.status = STATUS.get(status, str(status))
+        super().__init__("%s: %s" % (self.status, message))
+
+
+class _Params(ctypes.Structure):
+    _fields_ = [("num_qo_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("max_kv_splits", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32)]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("num_tiles", ctypes.c_int64), ("num_split_groups", ctypes.c_int64),
+                ("max_splits", ctypes.c_int32), ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32),
+                ("tokens_per_tile", ctypes.c_int32), ("partial_rows", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t), ("total_q", ctypes.c_int64),
+                ("visible_pairs", ctypes.c_int64), ("kv_tokens", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load():
+    """The ctypes handle of librpa.so; raises if the library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("librpa.so is not built (python -m paged_kv_attention_ragged_amd.build); "
+                               "there is no fallback implementation")
+        lib = ctypes.CDLL(LIB_PATH)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        st = ctypes.c_int
+        sig = {
+            "rpa_plan_create": (st, [ctypes.POINTER(_Params), i32, P, P, P, ctypes.POINTER(P)]),
+            "rpa_plan_info": (st, [P, ctypes.POINTER(_Info)]),
+            "rpa_plan_tiles": (st, [P, P, i64, ctypes.POINTER(i64)]),
+            "rpa_plan_bind": (st, [P, P, i64, P, ctypes.c_size_t, P]),
+            "rpa_run": (st, [P, P, P, P, P, P]),
+            "rpa_plan_check": (st, [P, P, ctypes.POINTER(i32)]),
+            "rpa_plan_destroy": (None, [P]),
+            "rpa_validate_page_table": (st, [i32, P, P, i64]),
+            "rpa_last_error": (ctypes.c_char_p, []),
+            "rpa_version": (ctypes.c_char_p, []),
+            "rpa_prof_start": (st, []),
+            "rpa_prof_stop": (st, [P, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def declared_functions(header: str = HEADER):
+    """Names of the functions include/rpa.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rpa_[a-z_]+)\s*\(", text)))
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise RPAError(rc, load().rpa_last_error().decode())
+
+
+def _host_i32(a) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            a = a.detach().cpu().numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _dtype_code(dtype) -> int:
+    if isinstance(dtype, str):
+        return {"f16": 0, "fp16": 0, "float16": 0, "bf16": 1, "bfloat16": 1}[dtype]
+    import torch
+    return {torch.float16: 0, torch.bfloat16: 1}[dtype]
+
+
+def version() -> str:
+    return load().rpa_version().decode()
+
+
+def validate_page_table(kv_page_indptr, kv_page_indices, num_pages: int):
+    """Host check that every page index is inside [0, num_pages)."""
+    ip = _host_i32(kv_page_indptr)
+    ix = _host_i32(kv_page_indices)
+    _check(load().rpa_validate_page_table(len(ip) - 1, ip.ctypes.data, ix.ctypes.data if ix.size else None,
+                                          int(num_pages)))
+
+
+class Plan:
+    """A schedule for one ragged batch (host page-table lengths), reusable across runs."""
+
+    def __init__(self, qo_indptr, kv_page_indptr, kv_last_page_len, *, num_qo_heads: int, num_kv_heads: int,
+                 head_dim: int, page_size: int = 16, dtype="f16", causal: bool = True,
+                 sm_scale: Optional[float] = None, max_kv_splits: int = 0, num_cus: int = 0):
+        lib = load()
+        self._qo = _host_i32(qo_indptr)
+        self._kp = _host_i32(kv_page_indptr)
+        self._kl = _host_i32(kv_last_page_len)
+        self.batch = len(self._qo) - 1
+        self.params = _Params(num_qo_heads, num_kv_heads, head_dim, page_size, _dtype_code(dtype),
+                              1 if causal else 0, 0.0 if sm_scale is None else float(sm_scale),
+                              max_kv_splits, num_cus)
+        h = ctypes.c_void_p()
+        p = lambda a: a.ctypes.data if a.size else None
+        _check(lib.rpa_plan_create(ctypes.byref(self.params), self.batch, p(self._qo), p(self._kp), p(self._kl),
+                                   ctypes.byref(h)))
+        self._h = h
+        self._keep = ()
+        self.workspace = None
+
+    # -- inspection --------------------------------------------------------------------------
+    @property
+    def info(self) -> dict:
+        inf = _Info()
+        _check(load().rpa_plan_info(self._h, ctypes.byref(inf)))
+        return {k: getattr(inf, k) for k, _ in _Info._fields_}
+
+    def tiles(self) -> np.ndarray:
+        """Work items in launch order, int32 [n, 16] (fields documented in rpa.h)."""
+        n = ctypes.c_int64()
+        _check(load().rpa_plan_tiles(self._h, None, 0, ctypes.byref(n)))
+        out = np.zeros((n.value, 16), dtype=np.int32)
+        if n.value:
+            _check(load().rpa_plan_tiles(self._h, out.ctypes.data, n.value, ctypes.byref(n)))
+        return out
+
+    # -- device side -------------------------------------------------------------------------
+    def bind(self, kv_page_indices, num_pages: int, workspace=None, stream=None):
+        """Upload the schedule into `workspace` (a uint8 CUDA tensor; allocated here
+        with torch if None) and borrow `kv_page_indices` (int32 CUDA tensor)."""
+        import torch
+        if not (isinstance(kv_page_indices, torch.Tensor) and kv_page_indices.is_cuda
+                and kv_page_indices.dtype == torch.int32 and kv_page_indices.is_contiguous()):
+            raise ValueError("kv_page_indices must be a contiguous int32 CUDA tensor")
+        need = self.info["workspace_bytes"]
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=kv_page_indices.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(kv_page_indices.device)
+        _check(load().rpa_plan_bind(self._h, kv_page_indices.data_ptr() if kv_page_indices.numel() else None,
+                                    int(num_pages), workspace.data_ptr(), workspace.numel(), stream.cuda_stream))
+        self._keep = (kv_page_indices,)
+        self.workspace = workspace
+        self.num_pages = int(num_pages)
+        return self
+
+    def run(self, q, kv_cache, out=None, return_lse: bool = False, lse=None, stream=None):
+        """O (and LSE if asked) for every query row: q [total_q, H_qo, D],
+        kv_cache [num_pages, 2, 16, H_kv, D], both CUDA tensors of the plan's dtype."""
+        import torch
+        P = self.params
+        dt = torch.float16 if P.dtype == 0 else torch.bfloat16
+        T = int(self._qo[-1]) if self.batch > 0 else 0
+        if q.dtype != dt or kv_cache.dtype != dt:
+            raise ValueError("q and kv_cache must be %s" % dt)
+        if tuple(q.shape) != (T, P.num_qo_heads, P.head_dim) or not q.is_contiguous() or not q.is_cuda:
+            raise ValueError("q must be a contiguous CUDA tensor of shape %s" % ((T, P.num_qo_heads, P.head_dim),))
+        if (kv_cache.dim() != 5 or tuple(kv_cache.shape[1:]) != (2, P.page_size, P.num_kv_heads, P.head_dim)
+                or not kv_cache.is_contiguous() or not kv_cache.is_cuda or kv_cache.shape[0] != self.num_pages):
+            raise ValueError("kv_cache must be a contiguous CUDA tensor [%d, 2, %d, %d, %d]"
+                             % (self.num_pages, P.page_size, P.num_kv_heads, P.head_dim))
+        if out is None:
+            out = torch.empty_like(q)
+        elif out.shape != q.shape or out.dtype != dt or not out.is_contiguous():
+            raise ValueError("out must match q")
+        if return_lse and lse is None:
+            lse = torch.empty((T, P.num_qo_heads), dtype=torch.float32, device=q.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        _check(load().rpa_run(self._h, q.data_ptr(), kv_cache.data_ptr(), out.data_ptr(),
+                              lse.data_ptr() if lse is not None else None, stream.cuda_stream))
+        return (out, lse) if return_lse else out
+
+    def check(self, stream=None) -> bool:
+        """Synchronise and report whether a run met an out-of-range page index (raises)."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        flag = ctypes.c_int32()
+        _check(load().rpa_plan_check(self._h, stream.cuda_stream, ctypes.byref(flag)))
+        return True
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            load().rpa_plan_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def prof_start():
+    _check(load().rpa_prof_start())
+
+
+def prof_stop():
+    """{'attention': (launches, ms), 'merge': (launches, ms)} since prof_start()."""
+    counts = (ctypes.c_int64 * 2)()
+    ms = (ctypes.c_double * 2)()
+    _check(load().rpa_prof_stop(counts, ms))
+    return {"attention": (counts[0], ms[0]), "merge": (counts[1], ms[1])}

@@ -1,0 +1,313 @@
+// rpa_api.cpp -- the C ABI declared in include/rpa.h: argument checks, plan
+// lifecycle, schedule upload into the caller's workspace, kernel launches and
+// error reporting.  Host code only; the kernels live in rpa_kernels.hip.
+#include "rpa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "rpa_launch.h"
+#include "rpa_schedule.h"
+
+
+struct rpa_plan {
+    rpa_params params{};
+    int32_t batch = 0;
+    rpa::Schedule sched;
+    // layout of the workspace image (byte offsets)
+    size_t off_tiles = 0, off_merges = 0, off_err = 0, off_part_lse = 0, off_part_o = 0, ws_bytes = 0;
+    // bound state
+    const int32_t* page_idx_d = nullptr;
+    int64_t num_pages = 0;
+    char* ws = nullptr;
+    void* staging = nullptr;  // pinned host image of the schedule
+    size_t staging_bytes = 0;
+    bool bound = false;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+rpa_status set_err(rpa_status s, const std::string& msg) {
+    g_err = msg;
+    return s;
+}
+
+rpa_status hip_err(hipError_t e, const char* what) {
+    return set_err(RPA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- kernel timing (benchmarks only) ----
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+struct ProfEv { hipEvent_t a, b; int kind; };
+std::vector<ProfEv> g_prof_events;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rpa_last_error(void) { return g_err.c_str(); }
+
+const char* rpa_version(void) { return "0.1.0"; }
+
+rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                           const int32_t* kv_page_indptr_h, const int32_t* kv_last_page_len_h,
+                           rpa_plan** out) {
+    if (!params || !out) return set_err(RPA_E_ARG, "params and out must be non-NULL");
+    *out = nullptr;
+    if (params->dtype != RPA_F16 && params->dtype != RPA_BF16)
+        return set_err(RPA_E_ARG, "dtype must be RPA_F16 (0) or RPA_BF16 (1)");
+    if (params->causal != 0 && params->causal != 1) return set_err(RPA_E_ARG, "causal must be 0 or 1");
+    if (!std::isfinite(params->sm_scale)) return set_err(RPA_E_ARG, "sm_scale must be finite");
+    rpa::PlanParams pp{params->num_qo_heads, params->num_kv_heads, params->head_dim, params->page_size,
+                       params->causal, params->max_kv_splits, params->num_cus};
+    rpa_plan* plan = new (std::nothrow) rpa_plan();
+    if (!plan) return set_err(RPA_E_ARG, "out of host memory");
+    std::string err;
+    int rc = 0;
+    try {
+        rc = rpa::build_schedule(pp, batch, qo_indptr_h, kv_page_indptr_h, kv_last_page_len_h, &plan->sched, &err);
+    } catch (const std::bad_alloc&) {
+        rc = RPA_E_ARG;
+        err = "out of host memory while planning";
+    }
+    if (rc != 0) {
+        delete plan;
+        return set_err(rpa_status(rc), err);
+    }
+    plan->params = *params;
+    plan->batch = batch;
+    const auto& S = plan->sched;
+    plan->off_tiles = 0;
+    plan->off_merges = align256(S.tiles.size() * sizeof(rpa::Tile));
+    plan->off_err = plan->off_merges + align256(S.merges.size() * sizeof(rpa::Merge));
+    plan->off_part_lse = plan->off_err + 256;
+    plan->off_part_o = plan->off_part_lse + align256(size_t(S.partial_rows) * sizeof(float));
+    plan->ws_bytes = plan->off_part_o + align256(size_t(S.partial_rows) * params->head_dim * sizeof(float));
+    plan->staging_bytes = plan->off_part_lse;  // tiles + merges + zeroed error flag
+    *out = plan;
+    return RPA_OK;
+}
+
+rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out) {
+    if (!plan || !out) return set_err(RPA_E_ARG, "plan and out must be non-NULL");
+    const auto& S = plan->sched;
+    out->num_tiles = int64_t(S.tiles.size());
+    out->num_split_groups = int64_t(S.merges.size());
+    out->max_splits = S.max_splits;
+    out->block_m = rpa::kBlockM;
+    out->block_n = S.block_n;
+    out->tokens_per_tile = S.tokens_per_tile;
+    out->partial_rows = S.partial_rows;
+    out->workspace_bytes = plan->ws_bytes;
+    out->total_q = S.total_q;
+    out->visible_pairs = S.visible_pairs;
+    out->kv_tokens = S.kv_tokens;
+    return RPA_OK;
+}
+
+rpa_status rpa_plan_tiles(const rpa_plan* plan, int32_t* out_h, int64_t cap, int64_t* n_out) {
+    if (!plan || !n_out || cap < 0 || (cap > 0 && !out_h))
+        return set_err(RPA_E_ARG, "plan and n_out must be non-NULL, cap >= 0");
+    const auto& tiles = plan->sched.tiles;
+    *n_out = int64_t(tiles.size());
+    const int64_t n = std::min<int64_t>(cap, int64_t(tiles.size()));
+    if (n > 0) std::memcpy(out_h, tiles.data(), size_t(n) * sizeof(rpa::Tile));
+    return RPA_OK;
+}
+
+rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64_t num_pages, void* workspace_d,
+                         size_t workspace_bytes, void* stream) {
+    if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
+    const auto& S = plan->sched;
+    if (num_pages < 0 || num_pages > INT32_MAX) return set_err(RPA_E_ARG, "num_pages outside [0, 2^31)");
+    if (!S.tiles.empty() && !kv_page_indices_d) return set_err(RPA_E_ARG, "kv_page_indices must be non-NULL");
+    if (!workspace_d) return set_err(RPA_E_ARG, "workspace must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(workspace_d) % 256 != 0)
+        return set_err(RPA_E_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < plan->ws_bytes) {
+        char buf[160];
+        std::snprintf(buf, sizeof(buf), "workspace of %zu bytes is too small: this plan needs %zu bytes",
+                      workspace_bytes, plan->ws_bytes);
+        return set_err(RPA_E_WORKSPACE, buf);
+    }
+    if (!plan->staging) {
+        hipError_t e = hipHostMalloc(&plan->staging, plan->staging_bytes, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            plan->staging = nullptr;
+            return hip_err(e, "hipHostMalloc(schedule staging)");
+        }
+        char* img = static_cast<char*>(plan->staging);
+        std::memset(img, 0, plan->staging_bytes);
+        if (!S.tiles.empty()) std::memcpy(img + plan->off_tiles, S.tiles.data(), S.tiles.size() * sizeof(rpa::Tile));
+        if (!S.merges.empty())
+            std::memcpy(img + plan->off_merges, S.merges.data(), S.merges.size() * sizeof(rpa::Merge));
+    }
+    hipError_t e = hipMemcpyAsync(workspace_d, plan->staging, plan->staging_bytes, hipMemcpyHostToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(schedule upload)");
+    plan->page_idx_d = kv_page_indices_d;
+    plan->num_pages = num_pages;
+    plan->ws = static_cast<char*>(workspace_d);
+    plan->bound = true;
+    return RPA_OK;
+}
+
+rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, void* o, float* lse, void* stream) {
+    if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
+    if (!plan->bound) return set_err(RPA_E_ARG, "plan is not bound to a workspace (rpa_plan_bind)");
+    const auto& S = plan->sched;
+    if (S.tiles.empty()) return RPA_OK;
+    if (!q || !kv_cache || !o) return set_err(RPA_E_ARG, "q, kv_cache and o must be non-NULL");
+    const rpa_params& P = plan->params;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const float scale = P.sm_scale > 0.f ? P.sm_scale : 1.f / std::sqrt(float(P.head_dim));
+    rpa::LaunchAttn L{};
+    L.a.tiles = reinterpret_cast<const rpa::Tile*>(plan->ws + plan->off_tiles);
+    L.a.page_idx = plan->page_idx_d;
+    L.a.num_pages = int32_t(plan->num_pages);
+    L.a.q = static_cast<const uint16_t*>(q);
+    L.a.kv = static_cast<const uint16_t*>(kv_cache);
+    L.a.o = static_cast<uint16_t*>(o);
+    L.a.lse = lse;
+    L.a.part_o = reinterpret_cast<float*>(plan->ws + plan->off_part_o);
+    L.a.part_lse = reinterpret_cast<float*>(plan->ws + plan->off_part_lse);
+    L.a.H = P.num_qo_heads;
+    L.a.Hkv = P.num_kv_heads;
+    L.a.G = P.num_qo_heads / P.num_kv_heads;
+    L.a.c_log2 = float(double(scale) * 1.4426950408889634);
+    L.a.causal = P.causal;
+    L.a.err_flag = reinterpret_cast<int32_t*>(plan->ws + plan->off_err);
+    L.head_dim = P.head_dim;
+    L.bf16 = P.dtype == RPA_BF16;
+    L.n_tiles = int64_t(S.tiles.size());
+
+    const bool prof = g_prof_on;
+    auto record = [&](int kind, bool begin, ProfEv& ev) {
+        if (!prof) return;
+        if (begin) { ev.a = prof_event(); ev.kind = kind; if (ev.a) (void)hipEventRecord(ev.a, st); }
+        else {
+            ev.b = prof_event();
+            if (ev.a && ev.b) {
+                (void)hipEventRecord(ev.b, st);
+                std::lock_guard<std::mutex> lk(g_prof_mu);
+                g_prof_events.push_back(ev);
+            }
+        }
+    };
+    ProfEv e0{}, e1{};
+    record(0, true, e0);
+    hipError_t e = rpa::launch_attention(L, st);
+    if (e != hipSuccess) return hip_err(e, "attention kernel launch");
+    record(0, false, e0);
+    if (!S.merges.empty()) {
+        rpa::MergeArgs M{};
+        M.merges = reinterpret_cast<const rpa::Merge*>(plan->ws + plan->off_merges);
+        M.part_o = L.a.part_o;
+        M.part_lse = L.a.part_lse;
+        M.o = L.a.o;
+        M.lse = lse;
+        M.H = L.a.H;
+        M.G = L.a.G;
+        record(1, true, e1);
+        e = rpa::launch_merge(M, P.head_dim, L.bf16, int64_t(S.merges.size()), st);
+        if (e != hipSuccess) return hip_err(e, "merge kernel launch");
+        record(1, false, e1);
+    }
+    return RPA_OK;
+}
+
+rpa_status rpa_plan_check(const rpa_plan* plan, void* stream, int32_t* flag_out) {
+    if (!plan || !flag_out) return set_err(RPA_E_ARG, "plan and flag_out must be non-NULL");
+    if (!plan->bound) return set_err(RPA_E_ARG, "plan is not bound");
+    int32_t flag = 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(&flag, plan->ws + plan->off_err, sizeof(flag), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_err(e, "reading the error flag");
+    *flag_out = flag;
+    if (flag) return set_err(RPA_E_PAGE_OOB, "a page index outside [0, num_pages) was met; its keys read as zero");
+    return RPA_OK;
+}
+
+void rpa_plan_destroy(rpa_plan* plan) {
+    if (!plan) return;
+    if (plan->staging) (void)hipHostFree(plan->staging);
+    delete plan;
+}
+
+rpa_status rpa_validate_page_table(int32_t batch, const int32_t* kv_page_indptr_h, const int32_t* kv_page_indices_h,
+                                   int64_t num_pages) {
+    if (batch < 0 || (batch > 0 && !kv_page_indptr_h)) return set_err(RPA_E_ARG, "bad batch or NULL indptr");
+    if (batch > 0 && kv_page_indptr_h[0] != 0) return set_err(RPA_E_INDPTR, "kv_page_indptr[0] must be 0");
+    for (int32_t b = 0; b < batch; ++b) {
+        if (kv_page_indptr_h[b + 1] < kv_page_indptr_h[b])
+            return set_err(RPA_E_INDPTR, "kv_page_indptr decreases at " + std::to_string(b));
+    }
+    const int32_t nnz = batch > 0 ? kv_page_indptr_h[batch] : 0;
+    if (nnz > 0 && !kv_page_indices_h) return set_err(RPA_E_ARG, "kv_page_indices must be non-NULL");
+    for (int32_t i = 0; i < nnz; ++i)
+        if (kv_page_indices_h[i] < 0 || kv_page_indices_h[i] >= num_pages)
+            return set_err(RPA_E_PAGE_OOB, "kv_page_indices[" + std::to_string(i) + "] = " +
+                                               std::to_string(kv_page_indices_h[i]) + " outside [0, " +
+                                               std::to_string(num_pages) + ")");
+    return RPA_OK;
+}
+
+rpa_status rpa_prof_start(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = true;
+    return RPA_OK;
+}
+
+rpa_status rpa_prof_stop(int64_t counts_out[2], double ms_out[2]) {
+    std::vector<ProfEv> evs;
+    {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        g_prof_on = false;
+        evs.swap(g_prof_events);
+    }
+    if (counts_out) counts_out[0] = counts_out[1] = 0;
+    if (ms_out) ms_out[0] = ms_out[1] = 0.0;
+    rpa_status st = RPA_OK;
+    for (auto& ev : evs) {
+        hipError_t e = hipEventSynchronize(ev.b);
+        float ms = 0.f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev.a, ev.b);
+        if (e != hipSuccess) st = hip_err(e, "kernel timing event");
+        else {
+            if (counts_out) counts_out[ev.kind] += 1;
+            if (ms_out) ms_out[ev.kind] += ms;
+        }
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        g_prof_pool.push_back(ev.a);
+        g_prof_pool.push_back(ev.b);
+    }
+    return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// rpa_launch.h -- kernel argument blocks and launchers (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rpa_schedule.h"
+
+namespace rpa {
+
+struct AttnArgs {
+    const Tile* tiles;
+    const int32_t* page_idx;  // kv_page_indices
+    int32_t num_pages;
+    const uint16_t* q;        // [total_q][H][D]
+    const uint16_t* kv;       // [num_pages][2][16][Hkv][D]
+    uint16_t* o;              // [total_q][H][D]
+    float* lse;               // [total_q][H] or NULL
+    float* part_o;            // [partial_rows][D]
+    float* part_lse;          // [partial_rows]
+    int32_t H, Hkv, G;
+    float c_log2;             // sm_scale * log2(e)
+    int32_t causal;
+    int32_t* err_flag;        // set to 1 when a page index is out of range
+};
+
+struct LaunchAttn {
+    AttnArgs a;
+    int head_dim;
+    bool bf16;
+    int64_t n_tiles;
+};
+
+struct MergeArgs {
+    const Merge* merges;
+    const float* part_o;
+    const float* part_lse;
+    uint16_t* o;
+    float* lse;
+    int32_t H, G;
+};
+
+hipError_t launch_attention(const LaunchAttn& L, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, bool bf16, int64_t n_merges, hipStream_t stream);
+
+}  // namespace rpa

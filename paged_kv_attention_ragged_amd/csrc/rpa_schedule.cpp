@@ -1,0 +1,181 @@
+// rpa_schedule.cpp -- host planner: ragged lengths in, work tiles and the
+// split-KV schedule out.  Plain C++17, no HIP: it builds and runs anywhere.
+//
+// The plan is the host half of the pages' begin_forward (flashinfer issue
+// #323, "How are prefill and decode kernels different?": auxiliary data built
+// once per batch and reused by every forward call).  It depends only on the
+// lengths, never on page ids, so two batches with equal lengths get the same
+// schedule and therefore the same rounding.
+#include "rpa_schedule.h"
+
+#include <algorithm>
+#include <cstdio>
+#include <numeric>
+
+namespace rpa {
+namespace {
+
+enum { OK = 0, E_ARG = 1, E_SHAPE = 2, E_INDPTR = 3, E_LAST_PAGE_LEN = 4, E_QLEN_GT_KVLEN = 5 };
+
+int fail(std::string* err, int code, const char* fmt, long a = 0, long b = 0, long c = 0) {
+    char buf[256];
+    std::snprintf(buf, sizeof(buf), fmt, a, b, c);
+    if (err) *err = buf;
+    return code;
+}
+
+struct QTile {
+    int32_t seq, kv_head, q_row0, q_count, pos0, kv_len, page_base, kv_end, nblk;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
+                   const int32_t* kv_page_indptr, const int32_t* kv_last_page_len, Schedule* out,
+                   std::string* err) {
+    if (!out || batch < 0) return fail(err, E_ARG, "batch must be >= 0 and out non-NULL");
+    if (batch > 0 && (!qo_indptr || !kv_page_indptr || !kv_last_page_len))
+        return fail(err, E_ARG, "qo_indptr, kv_page_indptr and kv_last_page_len must be non-NULL");
+    if (p.num_qo_heads < 1 || p.num_kv_heads < 1 || p.num_qo_heads % p.num_kv_heads != 0)
+        return fail(err, E_SHAPE, "num_qo_heads (%ld) must be a positive multiple of num_kv_heads (%ld)",
+                    p.num_qo_heads, p.num_kv_heads);
+    if (p.head_dim != 64 && p.head_dim != 128)
+        return fail(err, E_SHAPE, "head_dim %ld not supported (64 or 128)", p.head_dim);
+    if (p.page_size != kPageSize) return fail(err, E_SHAPE, "page_size %ld not supported (16)", p.page_size);
+    const int32_t G = p.num_qo_heads / p.num_kv_heads;
+    if (G > kBlockM) return fail(err, E_SHAPE, "query group %ld exceeds %ld heads per kv head", G, kBlockM);
+    if (p.max_kv_splits < 0) return fail(err, E_ARG, "max_kv_splits must be >= 0");
+
+    Schedule S;
+    S.block_n = block_n_for(p.head_dim);
+    S.tokens_per_tile = kBlockM / G;
+    const int32_t BN = S.block_n, TQ = S.tokens_per_tile;
+
+    if (batch > 0 && (qo_indptr[0] != 0 || kv_page_indptr[0] != 0))
+        return fail(err, E_INDPTR, "qo_indptr[0] (%ld) and kv_page_indptr[0] (%ld) must be 0", qo_indptr[0],
+                    kv_page_indptr[0]);
+    std::vector<QTile> base;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (qo_indptr[b + 1] < qo_indptr[b]) return fail(err, E_INDPTR, "qo_indptr decreases at %ld", b);
+        if (kv_page_indptr[b + 1] < kv_page_indptr[b])
+            return fail(err, E_INDPTR, "kv_page_indptr decreases at %ld", b);
+        const int32_t q_len = qo_indptr[b + 1] - qo_indptr[b];
+        const int32_t n_pages = kv_page_indptr[b + 1] - kv_page_indptr[b];
+        if (n_pages > 0 && (kv_last_page_len[b] < 1 || kv_last_page_len[b] > kPageSize))
+            return fail(err, E_LAST_PAGE_LEN, "kv_last_page_len[%ld] = %ld outside [1, 16]", b,
+                        kv_last_page_len[b]);
+        const int64_t kv_len64 = n_pages == 0 ? 0 : int64_t(n_pages - 1) * kPageSize + kv_last_page_len[b];
+        if (kv_len64 > INT32_MAX / 2) return fail(err, E_ARG, "sequence %ld too long", b);
+        const int32_t kv_len = int32_t(kv_len64);
+        if (q_len > kv_len)
+            return fail(err, E_QLEN_GT_KVLEN, "sequence %ld: q_len %ld > kv_len %ld", b, q_len, kv_len);
+        if (q_len == 0) continue;
+        S.total_q += q_len;
+        S.kv_tokens += kv_len;
+        const int64_t d = kv_len - q_len;
+        S.visible_pairs += p.causal ? (int64_t(q_len) * d + int64_t(q_len) * (q_len + 1) / 2) * p.num_qo_heads
+                                    : int64_t(q_len) * kv_len * p.num_qo_heads;
+        for (int32_t hk = 0; hk < p.num_kv_heads; ++hk)
+            for (int32_t t0 = 0; t0 < q_len; t0 += TQ) {
+                QTile t;
+                t.seq = b;
+                t.kv_head = hk;
+                t.q_row0 = qo_indptr[b] + t0;
+                t.q_count = std::min(TQ, q_len - t0);
+                t.pos0 = kv_len - q_len + t0;
+                t.kv_len = kv_len;
+                t.page_base = kv_page_indptr[b];
+                // keys past the last query's position are masked for every row: skip them
+                t.kv_end = p.causal ? std::min(kv_len, t.pos0 + t.q_count) : kv_len;
+                t.nblk = int32_t(ceil_div(t.kv_end, BN));
+                base.push_back(t);
+            }
+    }
+    if (batch > 0 && int64_t(qo_indptr[batch]) * p.num_qo_heads * p.head_dim > (int64_t(1) << 40))
+        return fail(err, E_ARG, "batch too large");
+
+    // ---- split-KV decision -------------------------------------------------------------
+    // Two 256-thread workgroups fit one CU.  When the query tiles alone cannot fill the
+    // machine, cut the longest key ranges into chunks of C blocks (chunk starts at absolute
+    // key positions that are multiples of C*block_n), choosing the largest C that still
+    // gives enough work items, but never less than kMinChunk blocks per piece.
+    const int32_t num_cus = p.num_cus > 0 ? p.num_cus : 256;
+    const int64_t target = 2LL * num_cus;
+    const int32_t kMinChunk = 4;
+    int32_t max_nblk = 1;
+    for (auto& t : base) max_nblk = std::max(max_nblk, t.nblk);
+    auto units = [&](int32_t C) {
+        int64_t u = 0;
+        for (auto& t : base) u += std::max<int64_t>(1, ceil_div(t.nblk, C));
+        return u;
+    };
+    int32_t C = max_nblk;
+    if (p.max_kv_splits != 1 && int64_t(base.size()) < target && max_nblk > kMinChunk) {
+        if (units(kMinChunk) < target) {
+            C = kMinChunk;
+        } else {  // largest C in [kMinChunk, max_nblk] with units(C) >= target
+            int32_t lo = kMinChunk, hi = max_nblk;
+            while (lo < hi) {
+                int32_t mid = lo + (hi - lo + 1) / 2;
+                if (units(mid) >= target) lo = mid; else hi = mid - 1;
+            }
+            C = lo;
+        }
+    }
+
+    // ---- expand into pieces ------------------------------------------------------------
+    struct Piece { Tile t; int64_t cost; int64_t order; };
+    std::vector<Piece> pieces;
+    pieces.reserve(base.size());
+    int64_t part_next = 0;
+    for (size_t i = 0; i < base.size(); ++i) {
+        const QTile& q = base[i];
+        int32_t ns = int32_t(std::max<int64_t>(1, ceil_div(q.nblk, C)));
+        if (p.max_kv_splits > 0) ns = std::min(ns, p.max_kv_splits);
+        const int32_t chunk = int32_t(ceil_div(q.nblk, ns));  // blocks per piece
+        ns = int32_t(std::max<int64_t>(1, ceil_div(q.nblk, chunk)));
+        const int32_t rows = q.q_count * G;
+        if (ns > 1) {
+            Merge m{};
+            m.q_row0 = q.q_row0;
+            m.q_count = q.q_count;
+            m.kv_head = q.kv_head;
+            m.part0 = int32_t(part_next);
+            m.n_splits = ns;
+            S.merges.push_back(m);
+            S.max_splits = std::max(S.max_splits, ns);
+        }
+        for (int32_t s = 0; s < ns; ++s) {
+            Tile t{};
+            t.q_row0 = q.q_row0;
+            t.q_count = q.q_count;
+            t.pos0 = q.pos0;
+            t.kv_len = q.kv_len;
+            t.page_base = q.page_base;
+            t.kv_head = q.kv_head;
+            t.kv_begin = s * chunk * BN;
+            t.kv_end = std::min(q.kv_end, (s + 1) * chunk * BN);
+            t.part = ns > 1 ? int32_t(part_next + int64_t(s) * rows) : -1;
+            t.seq = q.seq;
+            t.split = s;
+            t.n_splits = ns;
+            const int64_t blocks = ceil_div(t.kv_end - t.kv_begin, BN);
+            pieces.push_back({t, blocks + 1, int64_t(pieces.size())});
+        }
+        if (ns > 1) part_next += int64_t(ns) * rows;
+    }
+    if (part_next > INT32_MAX) return fail(err, E_ARG, "too many partial rows");
+    S.partial_rows = part_next;
+
+    // ---- launch order: longest first (LPT), ties in natural order --------------------------
+    std::stable_sort(pieces.begin(), pieces.end(),
+                     [](const Piece& a, const Piece& b) { return a.cost > b.cost; });
+    S.tiles.reserve(pieces.size());
+    for (auto& pc : pieces) S.tiles.push_back(pc.t);
+    *out = std::move(S);
+    return OK;
+}
+
+}  // namespace rpa

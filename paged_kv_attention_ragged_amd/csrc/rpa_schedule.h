@@ -1,0 +1,72 @@
+// rpa_schedule.h -- work items shared by the host planner and the gfx950
+// kernels.  Internal to the library (not part of the C ABI).
+#pragma once
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+namespace rpa {
+
+constexpr int kPageSize = 16;
+constexpr int kBlockM = 128;  // query rows (token x qo head of one kv group) per tile
+constexpr int kWaves = 4;     // wavefronts per workgroup, 32 query rows each
+
+// Keys per inner block: one K block plus one V block fill 16 KiB each.
+constexpr int block_n_for(int head_dim) { return 8192 / head_dim; }
+
+// One unit of attention work: the rows (tokens q_row0 .. q_row0+q_count-1, all
+// qo heads of kv head `kv_head`) against keys [kv_begin, kv_end) of one sequence.
+struct Tile {
+    int32_t q_row0;     // token row in Q / O of the first query
+    int32_t q_count;    // query tokens (1 .. tokens_per_tile)
+    int32_t pos0;       // position of the first query: kv_len - q_len + first token
+    int32_t kv_len;     // tokens cached for the sequence
+    int32_t page_base;  // kv_page_indptr[seq]
+    int32_t kv_head;
+    int32_t kv_begin;   // first key (a multiple of block_n)
+    int32_t kv_end;     // one past the last key
+    int32_t part;       // -1: write O / LSE; else first fp32 partial row of this piece
+    int32_t seq;
+    int32_t split;      // piece index within its query tile
+    int32_t n_splits;   // pieces of its query tile
+    int32_t reserved[4];
+};
+static_assert(sizeof(Tile) == 64, "Tile is 16 int32");
+
+// Combine the pieces of one split query tile.  Rows r < q_count*G of piece s
+// are at partial row part0 + s*(q_count*G) + r.
+struct Merge {
+    int32_t q_row0;
+    int32_t q_count;
+    int32_t kv_head;
+    int32_t part0;
+    int32_t n_splits;
+    int32_t reserved[3];
+};
+static_assert(sizeof(Merge) == 32, "Merge is 8 int32");
+
+struct PlanParams {
+    int32_t num_qo_heads, num_kv_heads, head_dim, page_size, causal;
+    int32_t max_kv_splits;  // 0 = decide, 1 = never, n = cap
+    int32_t num_cus;
+};
+
+struct Schedule {
+    std::vector<Tile> tiles;    // launch order
+    std::vector<Merge> merges;
+    int64_t partial_rows = 0;
+    int32_t tokens_per_tile = 0;
+    int32_t block_n = 0;
+    int32_t max_splits = 1;
+    int64_t total_q = 0;
+    int64_t visible_pairs = 0;  // per qo head, summed over heads
+    int64_t kv_tokens = 0;
+};
+
+// Status codes match rpa_status in rpa.h.
+int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
+                   const int32_t* kv_page_indptr, const int32_t* kv_last_page_len, Schedule* out,
+                   std::string* err);
+
+}  // namespace rpa

@@ -1,0 +1,203 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle, on the
+five workloads at full size and on smaller ragged cases, plus the bitwise
+invariances the schedule guarantees (page placement, prefix sharing, padding,
+decode row = prefill row, run-to-run determinism).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import assert_close, on_device, run, say
+
+pytestmark = pytest.mark.gpu
+
+
+def ref(b, rows=None):
+    return oracle.run(**b.oracle_kwargs(), rows=rows)
+
+
+# ----------------------------------------------------------------------------------------------
+# Small and mid-size ragged batches: every row compared.
+# ----------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("poison", [False, True])
+def test_tiny_ragged_prefill(poison):
+    b = W.tiny_ragged_prefill(poison=poison, spare_pages=4 if poison else 0)
+    ro, rl = ref(b)
+    for splits in (1, 0):
+        o, l, _ = run(b, max_kv_splits=splits)
+        assert_close(o, l, ro, rl, what="tiny splits=%d" % splits)
+
+
+SHAPES = [  # (H_qo, H_kv, D, dtype, causal)
+    (8, 1, 128, "f16", True),
+    (32, 8, 128, "bf16", True),
+    (64, 8, 128, "bf16", True),
+    (8, 8, 64, "f16", True),
+    (12, 1, 128, "bf16", True),   # G = 12: 10 tokens x 12 heads per 128-row tile
+    (16, 2, 64, "bf16", False),
+    (4, 4, 128, "f16", False),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "h%d_kv%d_d%d_%s_%s" % (s[0], s[1], s[2], s[3],
+                                                                                    "causal" if s[4] else "full"))
+def test_ragged_shapes(shape):
+    H, Hk, D, dt, causal = shape
+    q_lens = [1, 17, 64, 3, 130, 0, 1]
+    kv_lens = [1, 40, 300, 700, 130, 9, 333]
+    b = W.make_batch("ragged", q_lens, kv_lens, num_qo_heads=H, num_kv_heads=Hk, head_dim=D, dtype=dt,
+                     seed=31, spare_pages=5, poison=True, causal=causal)
+    ro, rl = ref(b)
+    for splits, cus in ((1, 0), (0, 0), (0, 4096)):
+        o, l, info = run(b, max_kv_splits=splits, num_cus=cus)
+        assert_close(o, l, ro, rl, what="%s splits=%d cus=%d" % (shape, splits, cus))
+        if cus == 4096:
+            assert info["num_split_groups"] > 0  # the split path really ran
+
+
+def test_long_single_sequence_splits():
+    b = W.make_batch("long1", [5], [4000], num_qo_heads=8, num_kv_heads=1, head_dim=128, dtype="bf16", seed=32)
+    ro, rl = ref(b)
+    o, l, info = run(b)
+    assert info["max_splits"] > 1
+    assert_close(o, l, ro, rl, what="long single")
+
+
+def test_sm_scale_and_no_lse():
+    b = W.make_batch("scale", [7, 1], [50, 90], num_qo_heads=8, num_kv_heads=2, head_dim=64, dtype="f16", seed=33)
+    ro, rl = oracle.run(**b.oracle_kwargs(), sm_scale=0.05)
+    o, l, _ = run(b, sm_scale=0.05)
+    assert_close(o, l, ro, rl, what="sm_scale")
+    o2, l2, _ = run(b, sm_scale=0.05, return_lse=False)
+    assert l2 is None and np.array_equal(o, o2)
+
+
+# ----------------------------------------------------------------------------------------------
+# The five workloads at full size.
+# ----------------------------------------------------------------------------------------------
+
+def test_decode_b128_kv1024():
+    b = W.decode_b128_kv1024()
+    ro, rl = ref(b)
+    for splits in (0, 1):
+        o, l, info = run(b, max_kv_splits=splits)
+        assert_close(o, l, ro, rl, what="decode splits=%d" % splits)
+    assert info["num_tiles"] == 128
+
+
+def test_short_prompt_prefill_and_padded_twin():
+    b = W.short_prompt_prefill()
+    p = W.short_prompt_prefill(padded=True)
+    ro, rl = ref(b)
+    o, l, _ = run(b, max_kv_splits=1)
+    assert_close(o, l, ro, rl, what="short prompts")
+    po, pl, _ = run(p, max_kv_splits=1)
+    pro, prl = ref(p)
+    assert_close(po, pl, pro, prl, what="short prompts padded")
+    # un-padded rows of the padded run are bit-identical to the ragged run
+    for s in range(b.batch):
+        L = int(b.q_lens[s])
+        a, c = b.qo_indptr[s], p.qo_indptr[s]
+        assert np.array_equal(o[a:a + L], po[c:c + L]), "sequence %d" % s
+        assert np.array_equal(l[a:a + L], pl[c:c + L]), "sequence %d" % s
+
+
+def test_shared_prefix_suffix_prefill_and_decode_steps():
+    sh = W.shared_prefix_suffix()
+    du = W.shared_prefix_suffix(duplicated=True)
+    ro, rl = ref(sh)
+    o, l, _ = run(sh)
+    assert_close(o, l, ro, rl, what="shared prefix prefill")
+    od, ld, _ = run(du)
+    assert np.array_equal(o, od) and np.array_equal(l, ld), "shared and duplicated prefix differ"
+    # 50 decode steps, appending one token per request per step
+    dev_kv = sh.kv_cache.to("cuda")
+    for step in range(1, 51):
+        d = W.decode_step(sh, step)
+        pos = 229 + step
+        pages = torch.from_numpy(d.kv_page_indices.reshape(sh.batch, -1)[:, pos // 16].astype(np.int64))
+        dev_kv[pages.cuda(), :, pos % 16] = sh.kv_cache[pages, :, pos % 16].cuda()
+        dev = (d.q.cuda(), dev_kv, torch.from_numpy(d.kv_page_indices).cuda())
+        o, l, _ = run(d, dev=dev, label="step %d" % step)
+        if step in (1, 2, 17, 50):
+            rro, rrl = ref(d)
+            assert_close(o, l, rro, rrl, what="decode step %d" % step)
+
+
+def mixed_long_sample_rows(b):
+    """All decode rows, plus the last 64 rows and a stride-61 sample of every prompt."""
+    rows = []
+    for s in range(b.batch):
+        a, e = int(b.qo_indptr[s]), int(b.qo_indptr[s + 1])
+        if e - a == 1:
+            rows.append(a)
+        else:
+            rows.extend(range(a, e, 61))
+            rows.extend(range(e - 64, e))
+    return sorted(set(rows))
+
+
+def test_mixed_long_batch_sampled():
+    say("generate mixed_long_batch on cuda")
+    b = W.mixed_long_batch(device="cuda")
+    rows = mixed_long_sample_rows(b)
+    o, l, info = run(b, dev=(b.q, b.kv_cache, torch.from_numpy(b.kv_page_indices).cuda()))
+    say("oracle on %d sampled rows" % len(rows))
+    ro, rl = ref(b, rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="mixed long (sampled)")
+
+
+# ----------------------------------------------------------------------------------------------
+# Bitwise invariances and error handling.
+# ----------------------------------------------------------------------------------------------
+
+def test_page_permutation_is_bitwise_invisible():
+    b = W.make_batch("perm", [1, 40, 9], [700, 40, 300], num_qo_heads=16, num_kv_heads=2, head_dim=128,
+                     dtype="bf16", seed=34, spare_pages=7)
+    p = W.permute_pages(b, seed=35)
+    o1, l1, _ = run(b)
+    o2, l2, _ = run(p)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_decode_row_equals_prefill_row_bitwise():
+    b = W.make_batch("pf", [21], [337], num_qo_heads=8, num_kv_heads=2, head_dim=128, dtype="f16", seed=36)
+    o, l, _ = run(b, max_kv_splits=1)
+    for i in (0, 5, 16, 20):
+        pos = 337 - 21 + i
+        npg = W.pages_for(pos + 1)
+        d = W.Batch("dec", np.array([0, 1], np.int32), np.array([0, npg], np.int32), b.kv_page_indices[:npg].copy(),
+                    np.array([W.last_page_len_for(pos + 1)], np.int32), b.q[i:i + 1].clone(), b.kv_cache, 8, 2,
+                    128, "f16")
+        od, ld, _ = run(d, max_kv_splits=1, label="row %d" % i)
+        assert np.array_equal(od[0], o[i]) and np.array_equal(ld[0], l[i]), "row %d" % i
+
+
+def test_runs_are_deterministic():
+    b = W.make_batch("det", [1, 100, 7, 1], [2000, 100, 900, 64], num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                     dtype="bf16", seed=37)
+    dev = on_device(b)
+    o1, l1, info = run(b, dev=dev)
+    assert info["num_split_groups"] > 0
+    o2, l2, _ = run(b, dev=dev)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_out_of_range_page_index_is_flagged_not_read():
+    import paged_kv_attention_ragged_amd as rpa
+    b = W.make_batch("oob", [3, 1], [40, 20], num_qo_heads=8, num_kv_heads=1, head_dim=64, dtype="f16", seed=38)
+    q, kv, idx = on_device(b)
+    say("oob flag: page index %d with num_pages declared %d" % (int(b.kv_page_indices.max()), int(b.kv_page_indices.max())))
+    plan = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=8, num_kv_heads=1,
+                    head_dim=64, dtype="f16")
+    # declare fewer pages than the table references: the kernel must not read them
+    plan.bind(idx, num_pages=int(b.kv_page_indices.max()))
+    plan.num_pages = kv.shape[0]  # the binding checks kv_cache against its declared size
+    plan.run(q, kv)
+    with pytest.raises(rpa.RPAError) as e:
+        plan.check()
+    assert e.value.status == "RPA_E_PAGE_OOB"
+    plan.close()

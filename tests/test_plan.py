@@ -1,0 +1,219 @@
+"""CPU tests of the C-ABI library: exported symbols, the host planner and its
+error codes.  Nothing here launches a kernel (no GPU needed): the planner is
+host-only and the library loads without a device.
+"""
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_ragged_amd as rpa
+import workloads as W
+
+F = dict(q_row0=0, q_count=1, pos0=2, kv_len=3, page_base=4, kv_head=5, kv_begin=6, kv_end=7, part=8,
+         seq=9, split=10, n_splits=11)
+
+
+def make_plan(b: W.Batch, **kw):
+    return rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
+                    num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal, **kw)
+
+
+def lengths_batch(q_lens, kv_lens, H=8, Hk=1, D=128, causal=True):
+    """Page table only (no tensors needed by the planner)."""
+    q_lens, kv_lens = list(q_lens), list(kv_lens)
+    B = len(q_lens)
+    qo = np.zeros(B + 1, np.int32)
+    qo[1:] = np.cumsum(q_lens)
+    npg = [W.pages_for(k) for k in kv_lens]
+    kp = np.zeros(B + 1, np.int32)
+    kp[1:] = np.cumsum(npg)
+    last = np.array([W.last_page_len_for(k) for k in kv_lens], np.int32)
+    return W.Batch("lengths", qo, kp, np.arange(kp[-1], dtype=np.int32), last, None, None, H, Hk, D, "f16", causal)
+
+
+def test_library_exports_every_declared_function():
+    lib = rpa.load()
+    names = rpa.declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+    assert rpa.version().count(".") == 2
+
+
+def check_schedule(b: W.Batch, plan):
+    """Properties every schedule must have, whatever the split decisions."""
+    t = plan.tiles()
+    info = plan.info
+    G = b.num_qo_heads // b.num_kv_heads
+    TQ = info["tokens_per_tile"]
+    BN = info["block_n"]
+    assert TQ == 128 // G and BN == 8192 // b.head_dim
+    q_lens, kv_lens = b.q_lens, b.kv_lens
+    # 1. every (sequence, kv head, token) appears in exactly one query tile, and each query
+    #    tile's pieces cover [0, kv_end) exactly once, in order, block-aligned
+    seen = {}
+    for rec in t:
+        key = (rec[F["seq"]], rec[F["kv_head"]], rec[F["q_row0"]])
+        seen.setdefault(key, []).append(rec)
+    covered = np.zeros((b.total_q, b.num_kv_heads), np.int32)
+    n_part_rows = 0
+    part_ranges = []
+    for (s, hk, r0), recs in seen.items():
+        recs = sorted(recs, key=lambda r: r[F["split"]])
+        qc = recs[0][F["q_count"]]
+        assert all(r[F["q_count"]] == qc for r in recs)
+        assert qo_row_in_seq(b, s, r0) and r0 + qc <= b.qo_indptr[s + 1]
+        assert (r0 - b.qo_indptr[s]) % TQ == 0 and 1 <= qc <= TQ
+        covered[r0:r0 + qc, hk] += 1
+        ql, kl = int(q_lens[s]), int(kv_lens[s])
+        pos0 = kl - ql + (r0 - b.qo_indptr[s])
+        assert recs[0][F["pos0"]] == pos0 and recs[0][F["kv_len"]] == kl
+        assert recs[0][F["page_base"]] == b.kv_page_indptr[s]
+        want_end = min(kl, pos0 + qc) if b.causal else kl  # causal tail skipped
+        ns = len(recs)
+        assert all(r[F["n_splits"]] == ns for r in recs)
+        assert [r[F["split"]] for r in recs] == list(range(ns))
+        assert recs[0][F["kv_begin"]] == 0 and recs[-1][F["kv_end"]] == want_end
+        for a, c in zip(recs, recs[1:]):
+            assert a[F["kv_end"]] == c[F["kv_begin"]]
+        for r in recs:
+            assert r[F["kv_begin"]] % BN == 0 and r[F["kv_begin"]] < r[F["kv_end"]] or want_end == 0
+        if ns == 1:
+            assert recs[0][F["part"]] == -1
+        else:
+            rows = qc * G
+            for i, r in enumerate(recs):
+                assert r[F["part"]] == recs[0][F["part"]] + i * rows
+            part_ranges.append((recs[0][F["part"]], recs[0][F["part"]] + ns * rows))
+            n_part_rows += ns * rows
+    want = np.zeros_like(covered)
+    for s in range(b.batch):
+        want[b.qo_indptr[s]:b.qo_indptr[s + 1], :] = 1
+    assert np.array_equal(covered, want)
+    # 2. partial rows of different split tiles never overlap
+    part_ranges.sort()
+    for (a0, a1), (c0, c1) in zip(part_ranges, part_ranges[1:]):
+        assert a1 <= c0
+    assert info["partial_rows"] == n_part_rows
+    # 3. longest-first launch order
+    cost = [(r[F["kv_end"]] - r[F["kv_begin"]] + BN - 1) // BN for r in t]
+    assert all(x >= y for x, y in zip(cost, cost[1:]))
+    # 4. work counts
+    vis = sum((int(kv_lens[s]) - int(q_lens[s])) * int(q_lens[s]) + int(q_lens[s]) * (int(q_lens[s]) + 1) // 2
+              if b.causal else int(q_lens[s]) * int(kv_lens[s]) for s in range(b.batch))
+    assert info["visible_pairs"] == vis * b.num_qo_heads
+    assert info["total_q"] == b.total_q
+    return t
+
+
+def qo_row_in_seq(b, s, r0):
+    return b.qo_indptr[s] <= r0 < b.qo_indptr[s + 1]
+
+
+@pytest.mark.parametrize("case", [
+    lengths_batch([17, 3, 5, 1], [17, 30, 5, 48], H=8, Hk=1, D=64),
+    lengths_batch([1] * 128, [1024] * 128),
+    lengths_batch([200, 1, 37, 0, 64], [200, 999, 300, 5, 64], H=32, Hk=8),
+    lengths_batch([30] * 256, [230] * 256, H=32, Hk=8),
+    lengths_batch([1] * 7, [5000, 17, 1, 16, 33, 4096, 64], H=64, Hk=8),
+    lengths_batch([8192] * 4 + [1] * 256, [8192] * 4 + list(range(512, 8192, 30))[:256], H=64, Hk=8),
+    lengths_batch([3, 9], [40, 9], H=6, Hk=2, D=64, causal=False),
+    lengths_batch([5, 1], [5, 1], H=12, Hk=1),  # G = 12 does not divide 128
+], ids=["tiny", "decode", "ragged", "suffix", "decode_mixed", "mixed_long", "noncausal", "g12"])
+@pytest.mark.parametrize("max_kv_splits", [0, 1, 3])
+def test_schedule_properties(case, max_kv_splits):
+    plan = make_plan(case, max_kv_splits=max_kv_splits)
+    t = check_schedule(case, plan)
+    if max_kv_splits == 1:
+        assert (t[:, F["n_splits"]] == 1).all()
+    if max_kv_splits == 3:
+        assert (t[:, F["n_splits"]] <= 3).all()
+
+
+def test_decode_batch_is_split_to_fill_the_machine():
+    b = lengths_batch([1] * 128, [1024] * 128)
+    info = make_plan(b).info
+    assert info["num_tiles"] >= 512 and info["num_split_groups"] == 128
+    assert make_plan(b, max_kv_splits=1).info["num_tiles"] == 128
+
+
+def test_schedule_depends_only_on_lengths():
+    b = W.tiny_ragged_prefill(spare_pages=4)
+    p = W.permute_pages(b, seed=5)
+    assert np.array_equal(make_plan(b).tiles(), make_plan(p).tiles())
+
+
+def test_fully_masked_tail_blocks_are_never_scheduled():
+    # a 4096-token prompt: tile i covers tokens [16i, 16i+16) and must stop at key 16i+16
+    b = lengths_batch([4096], [4096], H=64, Hk=8)
+    t = make_plan(b, max_kv_splits=1).tiles()
+    ends = t[:, F["kv_end"]] - (t[:, F["pos0"]] + t[:, F["q_count"]])
+    assert (ends == 0).all()
+    # total blocks walked ~ half of the dense square
+    BN = 64
+    blocks = ((t[:, F["kv_end"]] + BN - 1) // BN).sum()
+    dense = len(t) * (4096 // BN)
+    assert blocks < 0.53 * dense
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(qo_indptr=[1, 17, 20, 25, 26]), "RPA_E_INDPTR"),
+    (dict(qo_indptr=[0, 17, 16, 25, 26]), "RPA_E_INDPTR"),
+    (dict(kv_page_indptr=[0, 2, 1, 5, 8]), "RPA_E_INDPTR"),
+    (dict(kv_last_page_len=[1, 0, 5, 16]), "RPA_E_LAST_PAGE_LEN"),
+    (dict(kv_last_page_len=[1, 17, 5, 16]), "RPA_E_LAST_PAGE_LEN"),
+    (dict(kv_last_page_len=[1, 14, 4, 16]), "RPA_E_QLEN_GT_KVLEN"),
+    (dict(num_kv_heads=3), "RPA_E_SHAPE"),
+    (dict(head_dim=96), "RPA_E_SHAPE"),
+    (dict(page_size=32), "RPA_E_SHAPE"),
+    (dict(dtype=7), "RPA_E_ARG"),
+    (dict(max_kv_splits=-1), "RPA_E_ARG"),
+])
+def test_plan_rejects_bad_input(bad, code):
+    b = W.tiny_ragged_prefill()
+    kw = dict(qo_indptr=b.qo_indptr, kv_page_indptr=b.kv_page_indptr, kv_last_page_len=b.kv_last_page_len,
+              num_qo_heads=8, num_kv_heads=1, head_dim=64, page_size=16, dtype="f16", max_kv_splits=0)
+    kw.update(bad)
+    if isinstance(kw["dtype"], int):
+        p = rpa._Params(kw["num_qo_heads"], kw["num_kv_heads"], kw["head_dim"], 16, kw["dtype"], 1, 0.0, 0, 0)
+        h = ctypes.c_void_p()
+        qo, kp, kl = (rpa._host_i32(kw[k]) for k in ("qo_indptr", "kv_page_indptr", "kv_last_page_len"))
+        rc = rpa.load().rpa_plan_create(ctypes.byref(p), 4, qo.ctypes.data, kp.ctypes.data, kl.ctypes.data,
+                                        ctypes.byref(h))
+        assert rpa.STATUS[rc] == code and rpa.load().rpa_last_error()
+        return
+    with pytest.raises(rpa.RPAError) as e:
+        rpa.Plan(kw.pop("qo_indptr"), kw.pop("kv_page_indptr"), kw.pop("kv_last_page_len"), **kw)
+    assert e.value.status == code
+    assert len(str(e.value)) > len(code) + 5
+
+
+def test_validate_page_table():
+    b = W.tiny_ragged_prefill(spare_pages=2)
+    rpa.validate_page_table(b.kv_page_indptr, b.kv_page_indices, b.num_pages)
+    bad = b.kv_page_indices.copy()
+    bad[-1] = b.num_pages
+    with pytest.raises(rpa.RPAError) as e:
+        rpa.validate_page_table(b.kv_page_indptr, bad, b.num_pages)
+    assert e.value.status == "RPA_E_PAGE_OOB"
+    bad[-1] = -1
+    with pytest.raises(rpa.RPAError):
+        rpa.validate_page_table(b.kv_page_indptr, bad, b.num_pages)
+
+
+def test_run_rejects_unbound_plan():
+    b = W.tiny_ragged_prefill()
+    plan = make_plan(b)
+    lib = rpa.load()
+    rc = lib.rpa_run(plan._h, 1, 1, 1, None, None)
+    assert rpa.STATUS[rc] == "RPA_E_ARG" and b"bind" in lib.rpa_last_error()
+
+
+def test_empty_batch_and_zero_query_sequences():
+    b = lengths_batch([], [])
+    assert make_plan(b).info["num_tiles"] == 0
+    b = lengths_batch([0, 0], [5, 0])
+    info = make_plan(b).info
+    assert info["num_tiles"] == 0 and info["total_q"] == 0

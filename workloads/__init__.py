@@ -89,22 +89,38 @@ def last_page_len_for(kv_len: int, page_size: int = PAGE_SIZE) -> int:
 
 
 def _randn(gen: torch.Generator, shape, dtype: str, chunk_rows: int = 4096) -> torch.Tensor:
-    """N(0,1) fp32 draws rounded to `dtype`, generated in leading-axis chunks of
-    `chunk_rows` so that very large pools never need an fp32 copy in memory."""
-    out = torch.empty(shape, dtype=_DT[dtype])
+    """N(0,1) fp32 draws rounded to `dtype`, on the generator's device, generated
+    in leading-axis chunks of `chunk_rows` so that very large pools never need a
+    whole fp32 copy in memory."""
+    out = torch.empty(shape, dtype=_DT[dtype], device=gen.device)
     n0 = shape[0] if len(shape) else 1
     for s in range(0, n0, chunk_rows):
         e = min(n0, s + chunk_rows)
-        out[s:e] = torch.randn((e - s,) + tuple(shape[1:]), generator=gen, dtype=torch.float32).to(_DT[dtype])
+        out[s:e] = torch.randn((e - s,) + tuple(shape[1:]), generator=gen, dtype=torch.float32,
+                               device=gen.device).to(_DT[dtype])
     return out
+
+
+def value_generator(gen: torch.Generator, device=None) -> torch.Generator:
+    """Generator for Q / K / V values.  On the CPU it is `gen` itself; on another
+    device it is that device's generator, seeded by the next draw of `gen` (so
+    the draw order stays lengths -> placement -> values).  CPU and GPU generators
+    give different values for the same seed; a run on a device reads its values
+    back from that device."""
+    if device is None or torch.device(device).type == "cpu":
+        return gen
+    seed = int(torch.randint(0, 2 ** 62, (1,), generator=gen))
+    return torch.Generator(torch.device(device)).manual_seed(seed)
 
 
 def make_batch(name: str, q_lens: Sequence[int], kv_lens: Sequence[int], *, num_qo_heads: int,
                num_kv_heads: int, head_dim: int, dtype: str, seed: int = 0,
                gen: Optional[torch.Generator] = None, permute: bool = True, spare_pages: int = 0,
-               poison: bool = False, causal: bool = True, page_size: int = PAGE_SIZE) -> Batch:
+               poison: bool = False, causal: bool = True, page_size: int = PAGE_SIZE,
+               device=None) -> Batch:
     """Ragged batch with private pages per sequence, placed at random physical
-    pages of a pool of (owned + spare_pages) pages when `permute`, else in order."""
+    pages of a pool of (owned + spare_pages) pages when `permute`, else in order.
+    Q / K / V are drawn on `device` (CPU when None)."""
     q_lens = [int(x) for x in q_lens]
     kv_lens = [int(x) for x in kv_lens]
     assert len(q_lens) == len(kv_lens)
@@ -124,8 +140,9 @@ def make_batch(name: str, q_lens: Sequence[int], kv_lens: Sequence[int], *, num_
     kv_page_indptr[1:] = np.cumsum(n_pages)
     last = np.array([last_page_len_for(k, page_size) for k in kv_lens], dtype=np.int32)
     T = int(qo_indptr[-1])
-    q = _randn(gen, (T, num_qo_heads, head_dim), dtype)
-    kv = _randn(gen, (pool, 2, page_size, num_kv_heads, head_dim), dtype)
+    vgen = value_generator(gen, device)
+    q = _randn(vgen, (T, num_qo_heads, head_dim), dtype)
+    kv = _randn(vgen, (pool, 2, page_size, num_kv_heads, head_dim), dtype)
     if poison:
         _poison_unowned(kv, phys, kv_page_indptr, last)
     return Batch(name, qo_indptr, kv_page_indptr, phys, last, q, kv, num_qo_heads, num_kv_heads,
@@ -145,7 +162,7 @@ def _poison_unowned(kv: torch.Tensor, phys: np.ndarray, kv_page_indptr: np.ndarr
         owned[pages[-1], :last[b]] = True
     pg, sl = np.nonzero(~owned)
     if len(pg):
-        kv[torch.from_numpy(pg), :, torch.from_numpy(sl)] = float("nan")
+        kv[torch.from_numpy(pg).to(kv.device), :, torch.from_numpy(sl).to(kv.device)] = float("nan")
 
 
 def poison_unowned(batch: Batch) -> Batch:
@@ -165,12 +182,12 @@ def tiny_ragged_prefill(poison: bool = False, spare_pages: int = 0) -> Batch:
                       spare_pages=spare_pages)
 
 
-def decode_b128_kv1024(batch: int = 128, kv_len: int = 1024, dtype: str = "f16") -> Batch:
+def decode_b128_kv1024(batch: int = 128, kv_len: int = 1024, dtype: str = "f16", device=None) -> Batch:
     """batch 128 x q_len 1 x kv_len 1024, 8 qo / 1 kv heads, D 128, fp16; 64 pages
     per sequence laid out contiguously (kv_page_indices = arange)."""
     return make_batch("decode_b%d_kv%d" % (batch, kv_len), [1] * batch, [kv_len] * batch,
                       num_qo_heads=8, num_kv_heads=1, head_dim=128, dtype=dtype, seed=1002,
-                      permute=False)
+                      permute=False, device=device)
 
 
 def short_prompt_lengths(n: int = 64, lo: int = 1, hi: int = 200, seed: int = 1003) -> List[int]:
@@ -309,7 +326,7 @@ def mixed_long_lengths(n_prompts: int = 4, prompt_len: int = 8192, n_decode: int
 
 
 def mixed_long_batch(n_prompts: int = 4, prompt_len: int = 8192, n_decode: int = 256,
-                     lo: int = 512, hi: int = 8192, part: str = "all") -> Batch:
+                     lo: int = 512, hi: int = 8192, part: str = "all", device=None) -> Batch:
     """4 causal prompts of 8192 tokens plus 256 decode rows (q_len 1, kv_len uniform
     in [512, 8192]) in one ragged batch; 64 qo / 8 kv heads, D 128, bf16, random
     page placement.  part='prompts' or 'decode' keeps only that part of the same
@@ -320,7 +337,7 @@ def mixed_long_batch(n_prompts: int = 4, prompt_len: int = 8192, n_decode: int =
     elif part == "decode":
         q_lens, kv_lens = q_lens[n_prompts:], kv_lens[n_prompts:]
     return make_batch("mixed_long_" + part, q_lens, kv_lens, num_qo_heads=64, num_kv_heads=8,
-                      head_dim=128, dtype="bf16", gen=gen)
+                      head_dim=128, dtype="bf16", gen=gen, device=device)
 
 
 # ----------------------------------------------------------------------------------------------

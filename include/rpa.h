@@ -115,7 +115,8 @@ rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
  *   [0] first query row, [1] query tokens, [2] position of the first query,
  *   [3] kv_len, [4] kv_page_indptr[b], [5] kv head, [6] first key, [7] end key,
  *   [8] first partial row (-1: writes O directly), [9] sequence, [10] split
- *   index, [11] split count, [12..15] reserved.
+ *   index, [11] split count, [12] kind (0: wide, up to 128 rows; 1: narrow, up to
+ *   16 rows), [13] split group (-1 if not split), [14..15] reserved.
  * *n_out receives the number of records in the plan.
  */
 rpa_status rpa_plan_tiles(const rpa_plan* plan, int32_t* out_h, int64_t cap, int64_t* n_out);
@@ -142,9 +143,11 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
  *   kv_cache  device [num_pages][2][page_size][num_kv_heads][head_dim], same dtype
  *   o         device [total_q][num_qo_heads][head_dim], same dtype (written)
  *   lse       device fp32 [total_q][num_qo_heads] (written), or NULL
- * Enqueues one attention kernel, plus one merge kernel when the plan splits
- * key ranges, on `stream`.  No allocation, no host<->device synchronisation.
- * One run at a time per (plan, workspace): the partial-result region is shared.
+ * Enqueues one kernel on `stream`; when the plan splits key ranges, the piece
+ * of each split group that finishes last merges the group inside that kernel.
+ * No allocation, no host<->device synchronisation.  One run at a time per
+ * (plan, workspace): the partial-result region and the split counters are
+ * shared by all runs of a plan.
  * Errors: E_ARG (unbound plan, NULL pointer), E_HIP (launch failure).
  */
 rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, void* o, float* lse,
@@ -176,10 +179,11 @@ const char* rpa_last_error(void);
 const char* rpa_version(void);
 
 /*
- * Kernel timing (benchmarks): while enabled, rpa_run records a HIP event pair
- * around each kernel it enqueues.  rpa_prof_stop synchronises those events and
- * returns, per kernel kind (0 = attention, 1 = split merge), the number of
- * launches and their summed duration in milliseconds.
+ * Kernel timing (benchmarks): while enabled, rpa_run has a HIP event pair
+ * stamped by each kernel dispatch it enqueues (start and end of the kernel).
+ * rpa_prof_stop synchronises those events and returns, per kernel kind
+ * (0 = attention, 1 = reserved, always 0), the number of launches and their
+ * summed duration in milliseconds.
  */
 rpa_status rpa_prof_start(void);
 rpa_status rpa_prof_stop(int64_t counts_out[2], double ms_out[2]);

@@ -22,7 +22,8 @@ struct rpa_plan {
     int32_t batch = 0;
     rpa::Schedule sched;
     // layout of the workspace image (byte offsets)
-    size_t off_tiles = 0, off_merges = 0, off_err = 0, off_part_lse = 0, off_part_o = 0, ws_bytes = 0;
+    // [tiles][error flag, split-group counters][partial LSE][partial O]
+    size_t off_tiles = 0, off_err = 0, off_counters = 0, off_part_lse = 0, off_part_o = 0, ws_bytes = 0;
     // bound state
     const int32_t* page_idx_d = nullptr;
     int64_t num_pages = 0;
@@ -103,12 +104,12 @@ rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_
     plan->batch = batch;
     const auto& S = plan->sched;
     plan->off_tiles = 0;
-    plan->off_merges = align256(S.tiles.size() * sizeof(rpa::Tile));
-    plan->off_err = plan->off_merges + align256(S.merges.size() * sizeof(rpa::Merge));
-    plan->off_part_lse = plan->off_err + 256;
+    plan->off_err = align256(S.tiles.size() * sizeof(rpa::Tile));
+    plan->off_counters = plan->off_err + 64;
+    plan->off_part_lse = plan->off_counters + align256(S.merges.size() * sizeof(int32_t) + 1);
     plan->off_part_o = plan->off_part_lse + align256(size_t(S.partial_rows) * sizeof(float));
     plan->ws_bytes = plan->off_part_o + align256(size_t(S.partial_rows) * params->head_dim * sizeof(float));
-    plan->staging_bytes = plan->off_part_lse;  // tiles + merges + zeroed error flag
+    plan->staging_bytes = plan->off_part_lse;  // tiles, then the zeroed flag and counters
     *out = plan;
     return RPA_OK;
 }
@@ -164,8 +165,6 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
         char* img = static_cast<char*>(plan->staging);
         std::memset(img, 0, plan->staging_bytes);
         if (!S.tiles.empty()) std::memcpy(img + plan->off_tiles, S.tiles.data(), S.tiles.size() * sizeof(rpa::Tile));
-        if (!S.merges.empty())
-            std::memcpy(img + plan->off_merges, S.merges.data(), S.merges.size() * sizeof(rpa::Merge));
     }
     hipError_t e = hipMemcpyAsync(workspace_d, plan->staging, plan->staging_bytes, hipMemcpyHostToDevice,
                                   static_cast<hipStream_t>(stream));
@@ -202,41 +201,25 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
     L.a.c_log2 = float(double(scale) * 1.4426950408889634);
     L.a.causal = P.causal;
     L.a.err_flag = reinterpret_cast<int32_t*>(plan->ws + plan->off_err);
+    L.a.counters = reinterpret_cast<int32_t*>(plan->ws + plan->off_counters);
     L.head_dim = P.head_dim;
     L.bf16 = P.dtype == RPA_BF16;
     L.n_tiles = int64_t(S.tiles.size());
 
+    L.has_narrow = S.narrow_tiles > 0;
+    // Profiling: an event pair stamped by each dispatch itself (start and end of the kernel).
     const bool prof = g_prof_on;
-    auto record = [&](int kind, bool begin, ProfEv& ev) {
-        if (!prof) return;
-        if (begin) { ev.a = prof_event(); ev.kind = kind; if (ev.a) (void)hipEventRecord(ev.a, st); }
-        else {
-            ev.b = prof_event();
-            if (ev.a && ev.b) {
-                (void)hipEventRecord(ev.b, st);
-                std::lock_guard<std::mutex> lk(g_prof_mu);
-                g_prof_events.push_back(ev);
-            }
-        }
-    };
-    ProfEv e0{}, e1{};
-    record(0, true, e0);
-    hipError_t e = rpa::launch_attention(L, st);
+    ProfEv e0{nullptr, nullptr, 0}, e1{nullptr, nullptr, 1};
+    if (prof) {
+        e0.a = prof_event();
+        e0.b = prof_event();
+    }
+    hipError_t e = rpa::launch_attention(L, st, e0.a, e0.b);
     if (e != hipSuccess) return hip_err(e, "attention kernel launch");
-    record(0, false, e0);
-    if (!S.merges.empty()) {
-        rpa::MergeArgs M{};
-        M.merges = reinterpret_cast<const rpa::Merge*>(plan->ws + plan->off_merges);
-        M.part_o = L.a.part_o;
-        M.part_lse = L.a.part_lse;
-        M.o = L.a.o;
-        M.lse = lse;
-        M.H = L.a.H;
-        M.G = L.a.G;
-        record(1, true, e1);
-        e = rpa::launch_merge(M, P.head_dim, L.bf16, int64_t(S.merges.size()), st);
-        if (e != hipSuccess) return hip_err(e, "merge kernel launch");
-        record(1, false, e1);
+    if (prof) {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (e0.a && e0.b) g_prof_events.push_back(e0);
+        if (e1.a && e1.b) g_prof_events.push_back(e1);
     }
     return RPA_OK;
 }

@@ -21,9 +21,11 @@
 //     v_mfma_f32_32x32x16_f16 with P rounded to fp16 (10 fraction bits);
 //   * epilogue: O / l rounded to nearest-even into the input dtype and
 //     LSE = ln(l) + max, or fp32 partial rows when the key range is split.
-// Merge kernel: one workgroup per split query tile combines the pieces'
-// (O_s, LSE_s) by weights exp(LSE_s - max LSE) (flashinfer issue #323 speaks of
+// Split KV: a long key range is cut into pieces that run as separate work items;
+// the last piece to finish merges the pieces' (O_s, LSE_s) by weights
+// exp(LSE_s - max LSE) inside the same launch (flashinfer issue #323 speaks of
 // kv-parallelism / split-k in the prefill kernel).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,6 +53,28 @@ __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c, bool bf16)
 __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                    0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16_qk(u32x4 a, u32x4 b, f32x4 c, bool bf16) {
+    if (bf16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                   c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16_pv(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                   0, 0, 0);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 from an LDS address (4 x 16-bit, transposed across 16 lanes).
+__device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 // Two fp32 -> packed 16-bit, round to nearest-even.
@@ -92,22 +116,122 @@ __device__ __forceinline__ uint32_t v_pair(u32x4 vi, u32x4 vj, int e) {
 __device__ __forceinline__ int vt_swz(int d) { return (d + (d >> 3)) & 7; }
 
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_tile_kernel(AttnArgs A) {
-    constexpr int BN = 8192 / D;  // keys per block
-    constexpr int CH = D / 8;     // 16-byte chunks per K/V row
-    constexpr int KS = D + 8;     // K row stride in LDS (elements), 16-byte pad
-    constexpr int SB = BN / 32;   // 32-key score blocks
-    constexpr int DK = D / 16;    // k-steps of Q K^T
-    constexpr int DB = D / 32;    // 32-wide d blocks of O
-    constexpr int KC = BN / 16;   // 16-key steps of P V
-    static_assert(CH * (BN / 4) == 256, "each thread gathers 4 keys x 16 bytes");
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KS];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * BN];
+// Device-coherent fp32 accesses for the split partials: agent-scope relaxed
+// atomics, which gfx950 performs as global_store/global_load with sc1 (device
+// scope) -- written through to, and read from, the point of coherence shared by
+// all XCDs, so no L2 writeback or invalidate is needed to exchange them.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev4(float* p, f32x4 v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st_dev(p + i, v[i]);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-    const Tile T = A.tiles[blockIdx.x];
-    if (T.q_count <= 0) return;
+// Split-KV merge, fused: every piece of a split query tile has written its fp32
+// partial rows (O_s normalised by its own sum, and LSE_s) with device-coherent
+// stores; once they are complete (s_waitcnt, then a workgroup barrier) one thread
+// counts the piece done with an agent-scope atomic on the tile's split group.  The
+// piece that arrives last reads the partials back with device-coherent loads,
+// combines them with weights exp(LSE_s - max_s LSE_s), writes O and LSE, and resets
+// the counter to 0 for the next run.  The combine order is fixed (s = 0, 1, ...), so
+// the result does not depend on which piece arrives last.
+template <int D, bool BF16>
+__device__ __forceinline__ void finish_split(const AttnArgs& A, const Tile& T) {
+    __shared__ int is_last;
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are acknowledged
+    __syncthreads();                // ... and every other thread's
+    if (threadIdx.x == 0) {
+        const int done = __hip_atomic_fetch_add(A.counters + T.group, 1, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+        is_last = done == T.n_splits - 1;
+    }
+    __syncthreads();
+    if (!is_last) return;
+    const int G = A.G;
+    const int R = T.q_count * G;
+    const int part0 = T.part - T.split * R;
+    constexpr int D4 = D / 4;
+    constexpr int NB = 8;  // pieces whose partials are loaded together (one memory round trip)
+    for (int idx = threadIdx.x; idx < R * D4; idx += 256) {
+        const int r = idx / D4, c4 = idx - r * D4;
+        float mx = -INFINITY, wsum = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int sp0 = 0; sp0 < T.n_splits; sp0 += NB) {
+            float l[NB];
+            f32x4 v[NB];
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                l[k] = -INFINITY;
+                v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (sp0 + k < T.n_splits) {
+                    const int pr = part0 + (sp0 + k) * R + r;
+                    const float* src = A.part_o + (int64_t)pr * D + 4 * c4;
+                    l[k] = ld_dev(A.part_lse + pr);
+                    v[k] = f32x4{ld_dev(src), ld_dev(src + 1), ld_dev(src + 2), ld_dev(src + 3)};
+                }
+            }
+            float bm = mx;
+#pragma unroll
+            for (int k = 0; k < NB; ++k) bm = fmaxf(bm, l[k]);
+            if (bm == -INFINITY) continue;
+            const float sc = __expf(mx - bm);  // 0 while nothing has been merged yet
+            acc *= sc;
+            wsum *= sc;
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {
+                const float w = __expf(l[k] - bm);  // 0 for a piece with no visible key
+                acc += w * v[k];
+                wsum += w;
+            }
+            mx = bm;
+        }
+        const float inv = 1.f / wsum;
+        const int tok = r / G, g = r - tok * G;
+        const int64_t orow = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
+        u32x2 w2;
+        w2[0] = pack_out<BF16>(acc[0] * inv, acc[1] * inv);
+        w2[1] = pack_out<BF16>(acc[2] * inv, acc[3] * inv);
+        *(u32x2*)(A.o + orow * D + 4 * c4) = w2;
+        if (A.lse && c4 == 0) A.lse[orow] = mx + __logf(wsum);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(A.counters + T.group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int D>
+struct WideLds {
+    static constexpr int BN = 8192 / D;  // keys per block
+    static constexpr int KS = D + 8;     // K row stride in LDS (elements), 16-byte pad
+    static constexpr int bytes = (BN * KS + D * BN) * 2;
+};
+
+template <int D>
+struct NarrowLds {
+    static constexpr int KW = kWaveKeys;  // keys per wave step
+    static constexpr int VS = D + 16;     // V row stride (elements), 32-byte pad
+    static constexpr int stage_bytes = kWaves * KW * VS * 2;
+    static constexpr int combine_bytes = kWaves * 16 * (D + 4) * 4 + 2 * kWaves * 16 * 4;
+    static constexpr int bytes = stage_bytes > combine_bytes ? stage_bytes : combine_bytes;
+};
+
+// Wide tile: up to 128 rows (4 waves x 32 rows), keys walked block by block by the
+// whole workgroup; see the file comment.
+template <int D, bool BF16>
+__device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char* smem) {
+    constexpr int BN = WideLds<D>::BN;  // keys per block
+    constexpr int CH = D / 8;           // 16-byte chunks per K/V row
+    constexpr int KS = WideLds<D>::KS;  // K row stride in LDS (elements)
+    constexpr int SB = BN / 32;         // 32-key score blocks
+    constexpr int DK = D / 16;          // k-steps of Q K^T
+    constexpr int DB = D / 32;          // 32-wide d blocks of O
+    constexpr int KC = BN / 16;         // 16-key steps of P V
+    static_assert(CH * (BN / 4) == 256, "each thread gathers 4 keys x 16 bytes");
+    uint16_t* k_lds = reinterpret_cast<uint16_t*>(smem);
+    uint16_t* vt_lds = k_lds + BN * KS;
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
     const int G = A.G;
@@ -252,95 +376,316 @@ void attn_tile_kernel(AttnArgs A) {
         }
     }
 
-    if (!wave_active) return;
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    if (!row_ok) return;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse_val = ltot > 0.f ? (m + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
-    if (T.part < 0) {
-        uint16_t* op = A.o + orow * D + 4 * half;
+    if (wave_active && row_ok) {
+        if (T.part < 0) {
+            uint16_t* op = A.o + orow * D + 4 * half;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                u32x2 w;
-                w[0] = pack_out<BF16>(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-                w[1] = pack_out<BF16>(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-                *(u32x2*)(op + 32 * db + 8 * j) = w;
-            }
-        if (A.lse && half == 0) A.lse[orow] = lse_val;
-    } else {
-        float* pp = A.part_o + ((int64_t)T.part + row) * D + 4 * half;
+                for (int j = 0; j < 4; ++j) {
+                    u32x2 w;
+                    w[0] = pack_out<BF16>(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
+                    w[1] = pack_out<BF16>(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
+                    *(u32x2*)(op + 32 * db + 8 * j) = w;
+                }
+            if (A.lse && half == 0) A.lse[orow] = lse_val;
+        } else {
+            float* pp = A.part_o + ((int64_t)T.part + row) * D + 4 * half;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f32x4 w = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv, oacc[db][4 * j + 2] * inv,
-                           oacc[db][4 * j + 3] * inv};
-                *(f32x4*)(pp + 32 * db + 8 * j) = w;
-            }
-        if (half == 0) A.part_lse[T.part + row] = lse_val;
+                for (int j = 0; j < 4; ++j) {
+                    f32x4 w = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv, oacc[db][4 * j + 2] * inv,
+                               oacc[db][4 * j + 3] * inv};
+                    st_dev4(pp + 32 * db + 8 * j, w);
+                }
+            if (half == 0) st_dev(A.part_lse + T.part + row, lse_val);
+        }
     }
+    if (T.part >= 0) finish_split<D, BF16>(A, T);
 }
 
 
+// Narrow tile (decode-like): at most 16 rows (q_count * G <= 16), all in one
+// 16-column MFMA block.  The 4 waves split the key range: wave w takes the 64-key
+// steps w, w+4, w+8, ... of [kv_begin, kv_end), each with its own running max,
+// sum and O, and the waves are combined through LDS at the end.
+//   * K goes from the cache straight into the A operand of
+//     v_mfma_f32_16x16x32 (lane l: key 16b + l%16, 8 consecutive d), so only V
+//     passes through LDS;
+//   * V is staged in its natural [key][d] layout (fp16; bf16 is converted on the
+//     way) and read back transposed with ds_read_b64_tr_b16: within each 16-lane
+//     group, lane j receives element j%4 of the 8-byte rows addressed by lanes
+//     j/4 + 4m (m = 0..3), which turns 4 rows of 4 consecutive d into 4 keys of
+//     one d per lane -- the V^T operand layout;
+//   * S^T = K Q^T gives each lane one row (column l%16) and 4 consecutive keys per
+//     16-key block; the running max needs two cross-lane exchanges per step.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs A) {
-    constexpr int D4 = D / 4;
-    const Merge M = A.merges[blockIdx.x];
-    const int R = M.q_count * A.G;
-    for (int idx = threadIdx.x; idx < R * D4; idx += 256) {
-        const int r = idx / D4, d4 = idx - r * D4;
-        float mx = -INFINITY;
-        for (int s = 0; s < M.n_splits; ++s) mx = fmaxf(mx, A.part_lse[M.part0 + s * R + r]);
-        float wsum = 0.f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < M.n_splits; ++s) {
-            const int pr = M.part0 + s * R + r;
-            const float l = A.part_lse[pr];
-            const float w = l == -INFINITY ? 0.f : __expf(l - mx);
-            const f32x4 v = *(const f32x4*)(A.part_o + (int64_t)pr * D + 4 * d4);
-            acc += w * v;
-            wsum += w;
-        }
-        const float inv = 1.f / wsum;
-        const int tok = r / A.G, g = r - tok * A.G;
-        const int64_t orow = (int64_t)(M.q_row0 + tok) * A.H + M.kv_head * A.G + g;
-        u32x2 w2;
-        w2[0] = pack_out<BF16>(acc[0] * inv, acc[1] * inv);
-        w2[1] = pack_out<BF16>(acc[2] * inv, acc[3] * inv);
-        *(u32x2*)(A.o + orow * D + 4 * d4) = w2;
-        if (A.lse && d4 == 0) A.lse[orow] = mx + __logf(wsum);
+__device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, char* smem) {
+    constexpr int KW = NarrowLds<D>::KW;  // keys per wave step
+    constexpr int VS = NarrowLds<D>::VS;  // V staging row stride (elements)
+    constexpr int DK = D / 32;            // 32-d k-steps of Q K^T
+    constexpr int DB = D / 16;            // 16-d blocks of O^T
+    constexpr int CH = D / 8;             // 16-byte chunks per row
+    constexpr int KPJ = 64 / CH;          // keys per V load instruction
+    constexpr int VJ = KW / KPJ;          // V loads per lane per step
+    constexpr int KB = KW / 16;           // 16-key blocks per step
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int G = A.G;
+    const int rows_valid = T.q_count * G;
+    const int row = col;
+    const int tok = row / G, g = row - tok * G;
+    const bool row_ok = row < rows_valid;
+    const int pos = T.pos0 + tok;
+    const int pos_min = T.pos0;
+    const int64_t orow = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
+    uint16_t* v_lds = reinterpret_cast<uint16_t*>(smem) + wave * KW * VS;
+
+    // Q^T operand (B of 16x16x32): row `col`, d = 32kk + 8grp .. +8.
+    u32x4 qf[DK];
+    {
+        const uint16_t* qp = A.q + orow * D + 8 * grp;
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk)
+            qf[kk] = row_ok ? *(const u32x4*)(qp + 32 * kk) : u32x4{0, 0, 0, 0};
     }
+
+    f32x4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, lsum = 0.f;
+
+    const int64_t ss = (int64_t)A.Hkv * D;  // elements between token slots
+    const uint16_t* kvh = A.kv + (int64_t)T.kv_head * D;
+    const int vkey = lane / CH, vch = lane % CH;  // V gather: key j*KPJ + vkey, chunk vch
+
+    // Gathers for one step at key `kb0`: page ids, then K into MFMA-layout registers and
+    // V into natural-layout registers.  Keys at or past kv_len read as zero.
+    int pages[KB];
+    auto load_pages = [&](int kb0) {
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            int pg = -1;
+            if (kb0 + 16 * b < T.kv_len) {
+                pg = A.page_idx[T.page_base + (kb0 >> 4) + b];
+                if ((unsigned)pg >= (unsigned)A.num_pages) {
+                    *A.err_flag = 1;
+                    pg = -1;
+                }
+            }
+            pages[b] = pg;
+        }
+    };
+    u32x4 kf[KB][DK];
+    u32x4 vf[VJ];
+    auto load_k = [&](int kb0) {
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const bool ok = pages[b] >= 0 && kb0 + 16 * b + col < T.kv_len;
+            const uint16_t* src = kvh + ((int64_t)pages[b] * 32 + col) * ss + 8 * grp;
+#pragma unroll
+            for (int kk = 0; kk < DK; ++kk) kf[b][kk] = ok ? *(const u32x4*)(src + 32 * kk) : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto load_v = [&](int kb0) {
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) {
+            const int key = j * KPJ + vkey;  // key within the step; its page is pages[key / 16]
+            const int pg = pages[(j * KPJ) >> 4];
+            const bool ok = pg >= 0 && kb0 + key < T.kv_len;
+            vf[j] = ok ? *(const u32x4*)(kvh + ((int64_t)pg * 32 + 16 + (key & 15)) * ss + 8 * vch)
+                       : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    // Software pipeline: while step n is computed, step n+1's K (issued right after
+    // step n's Q K^T) and V (issued right after step n's V is staged) are in flight.
+    constexpr int STRIDE = kWaves * KW;
+    int kbase = T.kv_begin + wave * KW;
+    if (kbase < T.kv_end) {
+        load_pages(kbase);
+        load_k(kbase);
+        load_v(kbase);
+    }
+    for (; kbase < T.kv_end; kbase += STRIDE) {
+        const int knext = kbase + STRIDE;
+        const bool more = knext < T.kv_end;
+
+        // ---- S^T = K Q^T ----
+        f32x4 s[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            s[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < DK; ++kk) s[b] = mfma16_qk(kf[b][kk], qf[kk], s[b], BF16);
+        }
+        if (more) {
+            load_pages(knext);
+            load_k(knext);
+        }
+
+        // ---- stage V (fp16, natural layout) ----
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) {
+            u32x4 w = vf[j];
+            if (BF16) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_elem(vf[j], 2 * e),
+                                                                                   bf16_elem(vf[j], 2 * e + 1)));
+            }
+            *(u32x4*)(v_lds + (j * KPJ + vkey) * VS + 8 * vch) = w;
+        }
+        if (more) load_v(knext);
+
+        // ---- online softmax (lane: row `col`, keys 16b + 4grp + i) ----
+        const bool need_mask = (kbase + KW > T.kv_len) || (A.causal && kbase + KW - 1 > pos_min);
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x = s[b][i] * A.c_log2;
+                if (need_mask) {
+                    const int key = kbase + 16 * b + 4 * grp + i;
+                    if (key >= T.kv_len || (A.causal && key > pos)) x = -INFINITY;
+                }
+                s[b][i] = x;
+                bmax = fmaxf(bmax, x);
+            }
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+        const float m_new = fmaxf(m, bmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        m = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = __builtin_amdgcn_exp2f(s[b][i] - m_use);
+                lsum += p;
+                s[b][i] = p;
+            }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+
+        // ---- O^T += V^T P^T, 32 keys per MFMA ----
+#pragma unroll
+        for (int h = 0; h < KW / 32; ++h) {
+            // P^T operand: logical k = 8grp + e <-> key 32h + 16(e/4) + 4grp + e%4
+            u32x4 pf;
+            pf[0] = pack_p(s[2 * h][0], s[2 * h][1]);
+            pf[1] = pack_p(s[2 * h][2], s[2 * h][3]);
+            pf[2] = pack_p(s[2 * h + 1][0], s[2 * h + 1][1]);
+            pf[3] = pack_p(s[2 * h + 1][2], s[2 * h + 1][3]);
+            const uint16_t* vrow0 = v_lds + (32 * h + 4 * grp + (col >> 2)) * VS + 4 * (col & 3);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                u32x4 va;
+                const u32x2 lo = ds_read_tr16(vrow0 + 16 * db);
+                const u32x2 hi = ds_read_tr16(vrow0 + 16 * VS + 16 * db);
+                va[0] = lo[0];
+                va[1] = lo[1];
+                va[2] = hi[0];
+                va[3] = hi[1];
+                oacc[db] = mfma16_pv(va, pf, oacc[db]);
+            }
+        }
+    }
+
+    // ---- combine the 4 waves ----
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    __syncthreads();  // every wave is done with its V staging area
+    constexpr int OS = D + 4;  // fp32 row stride of the combine area
+    float* c_o = reinterpret_cast<float*>(smem);
+    float* c_m = c_o + kWaves * 16 * OS;
+    float* c_l = c_m + kWaves * 16;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) *(f32x4*)(c_o + (wave * 16 + col) * OS + 16 * db + 4 * grp) = oacc[db];
+    if (grp == 0) {
+        c_m[wave * 16 + col] = m;
+        c_l[wave * 16 + col] = lsum;
+    }
+    __syncthreads();
+    constexpr int D4 = D / 4;
+    for (int idx = tid; idx < 16 * D4; idx += 256) {
+        const int r = idx / D4, c4 = idx - r * D4;
+        if (r >= rows_valid) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, c_m[w * 16 + r]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float L = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float wt = __builtin_amdgcn_exp2f(c_m[w * 16 + r] - Mu);
+            L += wt * c_l[w * 16 + r];
+            acc += wt * *(const f32x4*)(c_o + (w * 16 + r) * OS + 4 * c4);
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const float lse_val = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
+        const int rt = r / G, rg = r - rt * G;
+        const int64_t orow_r = (int64_t)(T.q_row0 + rt) * A.H + T.kv_head * G + rg;
+        if (T.part < 0) {
+            u32x2 w2;
+            w2[0] = pack_out<BF16>(acc[0] * inv, acc[1] * inv);
+            w2[1] = pack_out<BF16>(acc[2] * inv, acc[3] * inv);
+            *(u32x2*)(A.o + orow_r * D + 4 * c4) = w2;
+            if (A.lse && c4 == 0) A.lse[orow_r] = lse_val;
+        } else {
+            st_dev4(A.part_o + ((int64_t)T.part + r) * D + 4 * c4, acc * inv);
+            if (c4 == 0) st_dev(A.part_lse + T.part + r, lse_val);
+        }
+    }
+    if (T.part >= 0) finish_split<D, BF16>(A, T);
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_tile_kernel(AttnArgs A) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const Tile T = A.tiles[blockIdx.x];
+    if (T.q_count <= 0) return;
+    if (T.kind == kNarrow) narrow_tile<D, BF16>(A, T, smem);
+    else wide_tile<D, BF16>(A, T, smem);
 }
 
 // ---- host-side launchers -----------------------------------------------------------------
 
-
-hipError_t launch_attention(const LaunchAttn& L, hipStream_t stream) {
-    if (L.n_tiles <= 0) return hipSuccess;
-    dim3 grid((unsigned)L.n_tiles), block(256);
-    if (L.head_dim == 128) {
-        if (L.bf16) hipLaunchKernelGGL((attn_tile_kernel<128, true>), grid, block, 0, stream, L.a);
-        else hipLaunchKernelGGL((attn_tile_kernel<128, false>), grid, block, 0, stream, L.a);
-    } else {
-        if (L.bf16) hipLaunchKernelGGL((attn_tile_kernel<64, true>), grid, block, 0, stream, L.a);
-        else hipLaunchKernelGGL((attn_tile_kernel<64, false>), grid, block, 0, stream, L.a);
+template <int D, bool BF16>
+hipError_t launch_attention_t(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    const size_t lds = L.has_narrow ? size_t(NarrowLds<D>::bytes > WideLds<D>::bytes ? NarrowLds<D>::bytes
+                                                                                     : WideLds<D>::bytes)
+                                    : size_t(WideLds<D>::bytes);
+    static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation
+    if (!attr_set) {
+        const int max_lds = NarrowLds<D>::bytes > WideLds<D>::bytes ? NarrowLds<D>::bytes : WideLds<D>::bytes;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_tile_kernel<D, BF16>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
     }
+    hipExtLaunchKernelGGL((attn_tile_kernel<D, BF16>), dim3((unsigned)L.n_tiles), dim3(256), (uint32_t)lds, stream,
+                          ev0, ev1, 0, L.a);
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& a, int head_dim, bool bf16, int64_t n_merges, hipStream_t stream) {
-    if (n_merges <= 0) return hipSuccess;
-    dim3 grid((unsigned)n_merges), block(256);
-    if (head_dim == 128) {
-        if (bf16) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, stream, a);
-    } else {
-        if (bf16) hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, stream, a);
-    }
-    return hipGetLastError();
+hipError_t launch_attention(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    if (L.n_tiles <= 0) return hipSuccess;
+    if (L.head_dim == 128)
+        return L.bf16 ? launch_attention_t<128, true>(L, stream, ev0, ev1)
+                      : launch_attention_t<128, false>(L, stream, ev0, ev1);
+    return L.bf16 ? launch_attention_t<64, true>(L, stream, ev0, ev1)
+                  : launch_attention_t<64, false>(L, stream, ev0, ev1);
 }
 
 }  // namespace rpa

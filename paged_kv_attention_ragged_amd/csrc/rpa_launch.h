@@ -21,25 +21,19 @@ struct AttnArgs {
     float c_log2;             // sm_scale * log2(e)
     int32_t causal;
     int32_t* err_flag;        // set to 1 when a page index is out of range
+    int32_t* counters;        // one per split group: pieces finished (reset to 0 by the last)
 };
 
 struct LaunchAttn {
     AttnArgs a;
     int head_dim;
     bool bf16;
+    bool has_narrow;  // the plan has narrow tiles: reserve their LDS
     int64_t n_tiles;
 };
 
-struct MergeArgs {
-    const Merge* merges;
-    const float* part_o;
-    const float* part_lse;
-    uint16_t* o;
-    float* lse;
-    int32_t H, G;
-};
 
-hipError_t launch_attention(const LaunchAttn& L, hipStream_t stream);
-hipError_t launch_merge(const MergeArgs& a, int head_dim, bool bf16, int64_t n_merges, hipStream_t stream);
+// ev0 / ev1: optional events stamped at the start and end of the dispatch (NULL: none).
+hipError_t launch_attention(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace rpa

@@ -25,7 +25,7 @@ int fail(std::string* err, int code, const char* fmt, long a = 0, long b = 0, lo
 }
 
 struct QTile {
-    int32_t seq, kv_head, q_row0, q_count, pos0, kv_len, page_base, kv_end, nblk;
+    int32_t seq, kv_head, q_row0, q_count, pos0, kv_len, page_base, kv_end, kind;
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -89,7 +89,7 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
                 t.page_base = kv_page_indptr[b];
                 // keys past the last query's position are masked for every row: skip them
                 t.kv_end = p.causal ? std::min(kv_len, t.pos0 + t.q_count) : kv_len;
-                t.nblk = int32_t(ceil_div(t.kv_end, BN));
+                t.kind = t.q_count * G <= kNarrowRows ? kNarrow : kWide;
                 base.push_back(t);
             }
     }
@@ -98,44 +98,45 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
 
     // ---- split-KV decision -------------------------------------------------------------
     // Two 256-thread workgroups fit one CU.  When the query tiles alone cannot fill the
-    // machine, cut the longest key ranges into chunks of C blocks (chunk starts at absolute
-    // key positions that are multiples of C*block_n), choosing the largest C that still
-    // gives enough work items, but never less than kMinChunk blocks per piece.
+    // machine, cut the longest key ranges into pieces of C keys (C a multiple of
+    // kChunkKeys; pieces start at absolute key positions that are multiples of C),
+    // choosing the largest C that still gives enough work items.
     const int32_t num_cus = p.num_cus > 0 ? p.num_cus : 256;
     const int64_t target = 2LL * num_cus;
-    const int32_t kMinChunk = 4;
-    int32_t max_nblk = 1;
-    for (auto& t : base) max_nblk = std::max(max_nblk, t.nblk);
-    auto units = [&](int32_t C) {
+    int32_t max_keys = kChunkKeys;
+    for (auto& t : base) max_keys = std::max(max_keys, t.kv_end);
+    const int32_t max_chunks = int32_t(ceil_div(max_keys, kChunkKeys));
+    auto units = [&](int64_t chunk_keys) {
         int64_t u = 0;
-        for (auto& t : base) u += std::max<int64_t>(1, ceil_div(t.nblk, C));
+        for (auto& t : base) u += std::max<int64_t>(1, ceil_div(t.kv_end, chunk_keys));
         return u;
     };
-    int32_t C = max_nblk;
-    if (p.max_kv_splits != 1 && int64_t(base.size()) < target && max_nblk > kMinChunk) {
-        if (units(kMinChunk) < target) {
-            C = kMinChunk;
-        } else {  // largest C in [kMinChunk, max_nblk] with units(C) >= target
-            int32_t lo = kMinChunk, hi = max_nblk;
+    int64_t C = int64_t(max_chunks) * kChunkKeys;
+    if (p.max_kv_splits != 1 && int64_t(base.size()) < target && max_chunks > 1) {
+        if (units(kChunkKeys) < target) {
+            C = kChunkKeys;
+        } else {  // largest c in [1, max_chunks] with units(c * kChunkKeys) >= target
+            int32_t lo = 1, hi = max_chunks;
             while (lo < hi) {
                 int32_t mid = lo + (hi - lo + 1) / 2;
-                if (units(mid) >= target) lo = mid; else hi = mid - 1;
+                if (units(int64_t(mid) * kChunkKeys) >= target) lo = mid; else hi = mid - 1;
             }
-            C = lo;
+            C = int64_t(lo) * kChunkKeys;
         }
     }
 
     // ---- expand into pieces ------------------------------------------------------------
-    struct Piece { Tile t; int64_t cost; int64_t order; };
+    struct Piece { Tile t; int64_t cost; };
     std::vector<Piece> pieces;
     pieces.reserve(base.size());
     int64_t part_next = 0;
     for (size_t i = 0; i < base.size(); ++i) {
         const QTile& q = base[i];
-        int32_t ns = int32_t(std::max<int64_t>(1, ceil_div(q.nblk, C)));
+        const int64_t nchunks = std::max<int64_t>(1, ceil_div(q.kv_end, kChunkKeys));
+        int32_t ns = int32_t(std::max<int64_t>(1, ceil_div(q.kv_end, C)));
         if (p.max_kv_splits > 0) ns = std::min(ns, p.max_kv_splits);
-        const int32_t chunk = int32_t(ceil_div(q.nblk, ns));  // blocks per piece
-        ns = int32_t(std::max<int64_t>(1, ceil_div(q.nblk, chunk)));
+        const int64_t per = ceil_div(nchunks, ns) * kChunkKeys;  // keys per piece
+        ns = int32_t(std::max<int64_t>(1, ceil_div(q.kv_end, per)));
         const int32_t rows = q.q_count * G;
         if (ns > 1) {
             Merge m{};
@@ -155,14 +156,18 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
             t.kv_len = q.kv_len;
             t.page_base = q.page_base;
             t.kv_head = q.kv_head;
-            t.kv_begin = s * chunk * BN;
-            t.kv_end = std::min(q.kv_end, (s + 1) * chunk * BN);
+            t.kv_begin = int32_t(s * per);
+            t.kv_end = int32_t(std::min<int64_t>(q.kv_end, (s + 1) * per));
             t.part = ns > 1 ? int32_t(part_next + int64_t(s) * rows) : -1;
             t.seq = q.seq;
             t.split = s;
             t.n_splits = ns;
-            const int64_t blocks = ceil_div(t.kv_end - t.kv_begin, BN);
-            pieces.push_back({t, blocks + 1, int64_t(pieces.size())});
+            t.kind = q.kind;
+            t.group = ns > 1 ? int32_t(S.merges.size()) - 1 : -1;
+            if (t.kind == kNarrow) ++S.narrow_tiles;
+            // cost ~ keys walked (wide tiles: rounded up to whole blocks) plus a fixed overhead
+            const int64_t gran = t.kind == kWide ? BN : kWaveKeys;
+            pieces.push_back({t, ceil_div(t.kv_end - t.kv_begin, gran) * gran + 64});
         }
         if (ns > 1) part_next += int64_t(ns) * rows;
     }

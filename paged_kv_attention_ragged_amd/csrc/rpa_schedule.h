@@ -12,8 +12,17 @@ constexpr int kPageSize = 16;
 constexpr int kBlockM = 128;  // query rows (token x qo head of one kv group) per tile
 constexpr int kWaves = 4;     // wavefronts per workgroup, 32 query rows each
 
-// Keys per inner block: one K block plus one V block fill 16 KiB each.
+constexpr int kNarrowRows = 16;  // tiles with at most this many rows take the narrow path
+constexpr int kWaveKeys = 64;     // keys one wave handles per step on the narrow path
+constexpr int kChunkKeys = 256;   // split pieces start at multiples of this many keys
+
+// Keys per inner block of the wide path: one K block plus one V block fill 16 KiB each.
 constexpr int block_n_for(int head_dim) { return 8192 / head_dim; }
+
+enum TileKind : int32_t {
+    kWide = 0,    // up to 128 rows; 4 waves split the rows, walk keys together
+    kNarrow = 1,  // up to 16 rows (decode-like); 4 waves split the keys
+};
 
 // One unit of attention work: the rows (tokens q_row0 .. q_row0+q_count-1, all
 // qo heads of kv head `kv_head`) against keys [kv_begin, kv_end) of one sequence.
@@ -30,7 +39,9 @@ struct Tile {
     int32_t seq;
     int32_t split;      // piece index within its query tile
     int32_t n_splits;   // pieces of its query tile
-    int32_t reserved[4];
+    int32_t kind;       // TileKind
+    int32_t group;      // split group (index of its counter) when n_splits > 1, else -1
+    int32_t reserved[2];
 };
 static_assert(sizeof(Tile) == 64, "Tile is 16 int32");
 
@@ -59,6 +70,7 @@ struct Schedule {
     int32_t tokens_per_tile = 0;
     int32_t block_n = 0;
     int32_t max_splits = 1;
+    int64_t narrow_tiles = 0;
     int64_t total_q = 0;
     int64_t visible_pairs = 0;  // per qo head, summed over heads
     int64_t kv_tokens = 0;

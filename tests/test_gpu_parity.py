@@ -58,6 +58,24 @@ def test_ragged_shapes(shape):
             assert info["num_split_groups"] > 0  # the split path really ran
 
 
+@pytest.mark.parametrize("shape", [(8, 1, 128, "f16"), (8, 2, 128, "bf16"), (16, 1, 64, "bf16"), (8, 8, 128, "f16")],
+                         ids=lambda s: "h%d_kv%d_d%d_%s" % s)
+def test_narrow_tiles(shape):
+    """Tiles of at most 16 rows take the decode path: multi-token causal rows (q_len * G
+    <= 16), several 64-key steps per wave, key ranges that end mid-step and mid-page."""
+    H, Hk, D, dt = shape
+    G = H // Hk
+    tq = max(1, 16 // G)
+    q_lens = [1, tq, 1, tq, 1]
+    kv_lens = [1, 77, 1000, 2049, 5000]
+    b = W.make_batch("narrow", q_lens, kv_lens, num_qo_heads=H, num_kv_heads=Hk, head_dim=D, dtype=dt, seed=39,
+                     spare_pages=3, poison=True)
+    ro, rl = ref(b)
+    for splits, cus in ((1, 0), (0, 0), (0, 4096)):
+        o, l, info = run(b, max_kv_splits=splits, num_cus=cus)
+        assert_close(o, l, ro, rl, what="narrow %s splits=%d cus=%d" % (shape, splits, cus))
+
+
 def test_long_single_sequence_splits():
     b = W.make_batch("long1", [5], [4000], num_qo_heads=8, num_kv_heads=1, head_dim=128, dtype="bf16", seed=32)
     ro, rl = ref(b)
@@ -97,12 +115,28 @@ def test_short_prompt_prefill_and_padded_twin():
     po, pl, _ = run(p, max_kv_splits=1)
     pro, prl = ref(p)
     assert_close(po, pl, pro, prl, what="short prompts padded")
-    # un-padded rows of the padded run are bit-identical to the ragged run
+    # Un-padded rows of the padded run are bit-identical to the ragged run when both
+    # runs put the row in a tile of the same path.  A ragged sequence's last tile can
+    # hold so few tokens (q_count * G <= 16) that it takes the narrow path while its
+    # padded twin's tile is wide: those rows round differently and are held to the
+    # oracle tolerance against each other.
+    G = b.num_qo_heads // b.num_kv_heads
+    TQ = 128 // G
+    n_bitwise = n_close = 0
     for s in range(b.batch):
         L = int(b.q_lens[s])
         a, c = b.qo_indptr[s], p.qo_indptr[s]
-        assert np.array_equal(o[a:a + L], po[c:c + L]), "sequence %d" % s
-        assert np.array_equal(l[a:a + L], pl[c:c + L]), "sequence %d" % s
+        for t0 in range(0, L, TQ):
+            n = min(TQ, L - t0)
+            ra, rc = slice(a + t0, a + t0 + n), slice(c + t0, c + t0 + n)
+            if n * G > 16:
+                assert np.array_equal(o[ra], po[rc]), "sequence %d tile at %d" % (s, t0)
+                assert np.array_equal(l[ra], pl[rc]), "sequence %d tile at %d" % (s, t0)
+                n_bitwise += n
+            else:
+                assert_close(po[rc], pl[rc], o[ra], l[ra], what="padded vs ragged seq %d" % s)
+                n_close += n
+    assert n_bitwise > 0.95 * b.total_q
 
 
 def test_shared_prefix_suffix_prefill_and_decode_steps():
@@ -163,17 +197,35 @@ def test_page_permutation_is_bitwise_invisible():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_decode_row_equals_prefill_row_bitwise():
-    b = W.make_batch("pf", [21], [337], num_qo_heads=8, num_kv_heads=2, head_dim=128, dtype="f16", seed=36)
+@pytest.mark.parametrize("case", [
+    # (H_qo, H_kv, prefill q_len, same tile path for both calls?)
+    (32, 1, 21, True),   # G = 32: a single decode token already fills a wide tile
+    (8, 1, 2, True),     # 2 tokens x 8 heads = 16 rows: both calls take the narrow path
+    (8, 2, 21, False),   # prefill tile wide, decode tile narrow
+], ids=["wide_wide", "narrow_narrow", "wide_narrow"])
+def test_decode_row_equals_prefill_row(case):
+    """A prefill row at position p against a q_len = 1 call over the first p + 1
+    tokens: bit-identical when both calls use the same tile path; otherwise within the
+    allclose(atol=1e-3, rtol=1e-3) that flashinfer issue #323's repro asserts between
+    its decode and prefill outputs (and each within the oracle tolerance)."""
+    H, Hk, ql, same_path = case
+    kvl = 337
+    b = W.make_batch("pf", [ql], [kvl], num_qo_heads=H, num_kv_heads=Hk, head_dim=128, dtype="f16", seed=36)
     o, l, _ = run(b, max_kv_splits=1)
-    for i in (0, 5, 16, 20):
-        pos = 337 - 21 + i
+    ro, rl = ref(b)
+    assert_close(o, l, ro, rl, what="prefill")
+    for i in sorted({0, ql // 2, ql - 1}):
+        pos = kvl - ql + i
         npg = W.pages_for(pos + 1)
         d = W.Batch("dec", np.array([0, 1], np.int32), np.array([0, npg], np.int32), b.kv_page_indices[:npg].copy(),
-                    np.array([W.last_page_len_for(pos + 1)], np.int32), b.q[i:i + 1].clone(), b.kv_cache, 8, 2,
+                    np.array([W.last_page_len_for(pos + 1)], np.int32), b.q[i:i + 1].clone(), b.kv_cache, H, Hk,
                     128, "f16")
         od, ld, _ = run(d, max_kv_splits=1, label="row %d" % i)
-        assert np.array_equal(od[0], o[i]) and np.array_equal(ld[0], l[i]), "row %d" % i
+        if same_path:
+            assert np.array_equal(od[0], o[i]) and np.array_equal(ld[0], l[i]), "row %d" % i
+        else:
+            np.testing.assert_allclose(od[0], o[i], atol=1e-3, rtol=1e-3)
+            assert_close(od[:1], ld[:1], ro[i:i + 1], rl[i:i + 1], what="decode row %d" % i)
 
 
 def test_runs_are_deterministic():

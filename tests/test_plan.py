@@ -12,7 +12,7 @@ import paged_kv_attention_ragged_amd as rpa
 import workloads as W
 
 F = dict(q_row0=0, q_count=1, pos0=2, kv_len=3, page_base=4, kv_head=5, kv_begin=6, kv_end=7, part=8,
-         seq=9, split=10, n_splits=11)
+         seq=9, split=10, n_splits=11, kind=12)
 
 
 def make_plan(b: W.Batch, **kw):
@@ -97,10 +97,15 @@ def check_schedule(b: W.Batch, plan):
     for (a0, a1), (c0, c1) in zip(part_ranges, part_ranges[1:]):
         assert a1 <= c0
     assert info["partial_rows"] == n_part_rows
-    # 3. longest-first launch order
-    cost = [(r[F["kv_end"]] - r[F["kv_begin"]] + BN - 1) // BN for r in t]
+    # 3. tile kind: narrow (decode-like path) exactly when a tile has at most 16 rows
+    assert all((r[F["kind"]] == 1) == (r[F["q_count"]] * G <= 16) for r in t)
+    # 4. longest-first launch order (keys walked, rounded to the path's step)
+    gran = [BN if r[F["kind"]] == 0 else 64 for r in t]
+    cost = [-(-(r[F["kv_end"]] - r[F["kv_begin"]]) // q) * q for r, q in zip(t, gran)]
     assert all(x >= y for x, y in zip(cost, cost[1:]))
-    # 4. work counts
+    # 5. split pieces start at multiples of 256 keys
+    assert all(r[F["kv_begin"]] % 256 == 0 for r in t)
+    # 6. work counts
     vis = sum((int(kv_lens[s]) - int(q_lens[s])) * int(q_lens[s]) + int(q_lens[s]) * (int(q_lens[s]) + 1) // 2
               if b.causal else int(q_lens[s]) * int(kv_lens[s]) for s in range(b.batch))
     assert info["visible_pairs"] == vis * b.num_qo_heads

@@ -116,16 +116,22 @@ __device__ __forceinline__ uint32_t v_pair(u32x4 vi, u32x4 vj, int e) {
 __device__ __forceinline__ int vt_swz(int d) { return (d + (d >> 3)) & 7; }
 
 
-// Device-coherent fp32 accesses for the split partials: agent-scope relaxed
-// atomics, which gfx950 performs as global_store/global_load with sc1 (device
-// scope) -- written through to, and read from, the point of coherence shared by
-// all XCDs, so no L2 writeback or invalidate is needed to exchange them.
+// Device-coherent fp32 accesses for the split partials.  Agent-scope relaxed
+// atomics are performed by gfx950 as global_store / global_load with sc1 (device
+// scope): written through to, and read from, the point of coherence shared by all
+// XCDs, so no L2 writeback or invalidate is needed to exchange them.  A 16-byte row
+// is stored with that same instruction written out (one dwordx4 store instead of
+// four dword stores: a quarter of the write transactions); stores return nothing,
+// so the compiler's wait counters need not track them (finish_split waits for all
+// of them before publishing).  A store of more than 8 bytes reads its data VGPRs
+// after issue, so the asm ends with wait states before anything may overwrite them
+// (the compiler adds these only after its own stores).  Loads stay
+// compiler-generated, 4 bytes at a time.
 __device__ __forceinline__ void st_dev(float* p, float v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_dev4(float* p, f32x4 v) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st_dev(p + i, v[i]);
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" : : "v"(p), "v"(v) : "memory");
 }
 __device__ __forceinline__ float ld_dev(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

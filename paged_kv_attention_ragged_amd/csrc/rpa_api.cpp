@@ -147,6 +147,7 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
     const auto& S = plan->sched;
     if (num_pages < 0 || num_pages > INT32_MAX) return set_err(RPA_E_ARG, "num_pages outside [0, 2^31)");
     if (!S.tiles.empty() && !kv_page_indices_d) return set_err(RPA_E_ARG, "kv_page_indices must be non-NULL");
+    if (!S.tiles.empty() && num_pages < 1) return set_err(RPA_E_ARG, "num_pages must be >= 1 for a non-empty batch");
     if (!workspace_d) return set_err(RPA_E_ARG, "workspace must be non-NULL");
     if (reinterpret_cast<uintptr_t>(workspace_d) % 256 != 0)
         return set_err(RPA_E_WORKSPACE, "workspace must be 256-byte aligned");

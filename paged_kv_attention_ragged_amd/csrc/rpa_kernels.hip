@@ -111,6 +111,19 @@ __device__ __forceinline__ uint32_t v_pair(u32x4 vi, u32x4 vj, int e) {
     return __builtin_amdgcn_perm(vj[e >> 1], vi[e >> 1], sel);
 }
 
+// Value of lane l ^ 32: v_permlane32_swap exchanges the two 32-lane halves of a
+// register pair; given x twice, each lane ends up holding {x[l], x[l ^ 32]}.
+__device__ __forceinline__ float xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    const float a = __builtin_bit_cast(float, (uint32_t)r[0]), b = __builtin_bit_cast(float, (uint32_t)r[1]);
+    // one of a, b is x itself; the other is the partner's value
+    return __builtin_bit_cast(uint32_t, a) == __builtin_bit_cast(uint32_t, x) ? b : a;
+}
+
+// Lazy-rescale threshold (log2 units): P never exceeds 2^kLazy = 256.
+constexpr float kLazy = 8.0f;
+
 // XOR swizzle of the 16-byte groups of a transposed-V row, so that both the
 // 8-byte transposing writes and the 16-byte MFMA operand reads spread over banks.
 __device__ __forceinline__ int vt_swz(int d) { return (d + (d >> 3)) & 7; }
@@ -209,9 +222,10 @@ __device__ __forceinline__ void finish_split(const AttnArgs& A, const Tile& T) {
 
 template <int D>
 struct WideLds {
-    static constexpr int BN = 8192 / D;  // keys per block
-    static constexpr int KS = D + 8;     // K row stride in LDS (elements), 16-byte pad
-    static constexpr int bytes = (BN * KS + D * BN) * 2;
+    static constexpr int BN = 8192 / D;                 // keys per block
+    static constexpr int KS = D + 8;                    // K row stride in LDS (elements), 16-byte pad
+    static constexpr int stage = BN * KS + D * BN;      // elements of one K + V^T block
+    static constexpr int bytes = 2 * stage * 2;         // double buffered
 };
 
 template <int D>
@@ -235,8 +249,10 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     constexpr int DB = D / 32;          // 32-wide d blocks of O
     constexpr int KC = BN / 16;         // 16-key steps of P V
     static_assert(CH * (BN / 4) == 256, "each thread gathers 4 keys x 16 bytes");
-    uint16_t* k_lds = reinterpret_cast<uint16_t*>(smem);
-    uint16_t* vt_lds = k_lds + BN * KS;
+    // Two stages of [K block | V^T block]: block n is computed from stage n % 2 while
+    // block n+1 is written into the other, so one barrier per block suffices.
+    uint16_t* const lds0 = reinterpret_cast<uint16_t*>(smem);
+    constexpr int STAGE = WideLds<D>::stage;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
@@ -268,26 +284,30 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     const uint16_t* kv_base = A.kv + (int64_t)T.kv_head * D + 8 * ch;
     u32x4 kreg[4], vreg[4];
 
+    // Gather of one block: always from a valid address (a key past kv_len, or a bad
+    // page, reads page `safe` instead), then the rare invalid keys are zeroed in a
+    // wave-uniform branch, so full blocks run without per-key branches.
     auto gather = [&](int kv0) {
         const int key0 = kv0 + 4 * kg;  // 4-aligned: the 4 keys share a page
-        int page = -1;
-        if (key0 < T.kv_len) {
-            page = A.page_idx[T.page_base + (key0 >> 4)];
-            if ((unsigned)page >= (unsigned)A.num_pages) {
-                *A.err_flag = 1;
-                page = -1;
-            }
-        }
+        int page = 0;
+        if (key0 < T.kv_len) page = A.page_idx[T.page_base + (key0 >> 4)];
+        const bool page_ok = (unsigned)page < (unsigned)A.num_pages;
+        if (!page_ok) *A.err_flag = 1;
+        const int pg = page_ok ? page : 0;
+        const uint16_t* src = kv_base + ((int64_t)pg * 32 + (key0 & 15)) * slot_stride;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            if (page >= 0 && key0 + i < T.kv_len) {
-                const uint16_t* src = kv_base + ((int64_t)page * 32 + ((key0 + i) & 15)) * slot_stride;
-                kreg[i] = *(const u32x4*)src;
-                vreg[i] = *(const u32x4*)(src + 16 * slot_stride);
-            } else {
-                kreg[i] = u32x4{0, 0, 0, 0};
-                vreg[i] = u32x4{0, 0, 0, 0};
-            }
+            kreg[i] = *(const u32x4*)(src + i * slot_stride);
+            vreg[i] = *(const u32x4*)(src + (16 + i) * slot_stride);
+        }
+        const bool tail = kv0 + BN > T.kv_len;
+        if (__builtin_amdgcn_ballot_w64(tail || !page_ok)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!page_ok || key0 + i >= T.kv_len) {
+                    kreg[i] = u32x4{0, 0, 0, 0};
+                    vreg[i] = u32x4{0, 0, 0, 0};
+                }
         }
     };
 
@@ -295,7 +315,9 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     // swapped, so the 8 keys one lane feeds to a P V step are contiguous.
     const int kb = 4 * kg;
     const int vslot = (kb & ~15) | (((kb >> 2) & 1) << 3) | (((kb >> 3) & 1) << 2);
-    auto stage = [&]() {
+    auto stage = [&](int buf) {
+        uint16_t* k_lds = lds0 + buf * STAGE;
+        uint16_t* vt_lds = k_lds + BN * KS;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *(u32x4*)(k_lds + (kb + i) * KS + 8 * ch) = kreg[i];
 #pragma unroll
@@ -316,63 +338,74 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
 
     const int nblk = (T.kv_end - T.kv_begin + BN - 1) / BN;
     gather(T.kv_begin);
+    stage(0);
+    if (nblk > 1) gather(T.kv_begin + BN);
+    __syncthreads();
     for (int blk = 0; blk < nblk; ++blk) {
         const int kv0 = T.kv_begin + blk * BN;
-        __syncthreads();
-        stage();
-        if (blk + 1 < nblk) gather(kv0 + BN);
-        __syncthreads();
-        if (!wave_active) continue;
-        if (A.causal && kv0 > wpos_max) continue;  // every row of this wave is masked
+        const uint16_t* k_lds = lds0 + (blk & 1) * STAGE;
+        const uint16_t* vt_lds = k_lds + BN * KS;
+        // every row of this wave is masked for this block: nothing to compute
+        const bool skip = !wave_active || (A.causal && kv0 > wpos_max);
+        if (!skip) {
 
         f32x16 s[SB];
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-            s[sb] = f32x16{};
-            const uint16_t* kp = k_lds + (32 * sb + col) * KS + 8 * half;
+        for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16{};
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk) s[sb] = mfma_qk(*(const u32x4*)(kp + 16 * kk), qf[kk], s[sb], BF16);
-        }
+        for (int kk = 0; kk < DK; ++kk)
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb)
+                s[sb] = mfma_qk(*(const u32x4*)(k_lds + (32 * sb + col) * KS + 8 * half + 16 * kk), qf[kk], s[sb],
+                                BF16);
 
         const bool need_mask = (kv0 + BN > T.kv_len) || (A.causal && kv0 + BN - 1 > wpos_min);
+        if (need_mask) {
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (key >= T.kv_len || (A.causal && key > pos)) s[sb][r] = -INFINITY;
+                }
+        }
+        // Row max of the raw scores (the scale is positive, so it commutes with max).
         float bmax = -INFINITY;
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = s[sb][r] * A.c_log2;
-                if (need_mask) {
-                    const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (key >= T.kv_len || (A.causal && key > pos)) x = -INFINITY;
-                }
-                s[sb][r] = x;
-                bmax = fmaxf(bmax, x);
-            }
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-        const float m_new = fmaxf(m, bmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-        m = m_new;
-        lsum *= alpha;
+            for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[sb][r]);
+        bmax = fmaxf(bmax, xor32(bmax));
+        // Lazy rescaling: a row's reference m (log2 units) moves only when the block's
+        // max exceeds it by more than kLazy, so P = 2^(x - m) <= 2^kLazy (exact in
+        // fp16) and the O / l rescale is skipped unless some row of the wave moved.
+        const float bx = bmax * A.c_log2;
+        const bool upd = bx > m + kLazy;  // always true for a row's first visible block
+        if (__builtin_amdgcn_ballot_w64(upd)) {
+            const float m_new = upd ? bx : m;
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+            m = m_new;
+            lsum *= alpha;
 #pragma unroll
-        for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = __builtin_amdgcn_exp2f(s[sb][r] - m_use);
-                lsum += p;
-                s[sb][r] = p;
-            }
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        }
+        const float nm = m == -INFINITY ? 0.f : -m;  // a row with no visible key yet: P = 0
 
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
             const int sb = kc >> 1, r0 = (kc & 1) * 8;
+            // P = 2^(scale*log2(e)*s - m), rounded toward zero to fp16; the row sum is
+            // taken from the same rounded values, so the weights and their normaliser
+            // agree exactly.
             u32x4 pf;
-            pf[0] = pack_p(s[sb][r0 + 0], s[sb][r0 + 1]);
-            pf[1] = pack_p(s[sb][r0 + 2], s[sb][r0 + 3]);
-            pf[2] = pack_p(s[sb][r0 + 4], s[sb][r0 + 5]);
-            pf[3] = pack_p(s[sb][r0 + 6], s[sb][r0 + 7]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r0 + 2 * e], A.c_log2, nm)),
+                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r0 + 2 * e + 1], A.c_log2, nm)));
+                lsum = __builtin_amdgcn_fdot2(h, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum, false);
+                pf[e] = __builtin_bit_cast(uint32_t, h);
+            }
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int d = 32 * db + col;
@@ -380,9 +413,15 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
                 oacc[db] = mfma_pv(vf, pf, oacc[db]);
             }
         }
+        }  // !skip
+        if (blk + 1 < nblk) {
+            stage((blk + 1) & 1);
+            if (blk + 2 < nblk) gather(kv0 + 2 * BN);
+        }
+        __syncthreads();
     }
 
-    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float ltot = lsum + xor32(lsum);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse_val = ltot > 0.f ? (m + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
     if (wave_active && row_ok) {

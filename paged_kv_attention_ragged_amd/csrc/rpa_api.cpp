@@ -120,7 +120,7 @@ rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out) {
     out->num_tiles = int64_t(S.tiles.size());
     out->num_split_groups = int64_t(S.merges.size());
     out->max_splits = S.max_splits;
-    out->block_m = rpa::kBlockM;
+    out->block_m = S.block_m;
     out->block_n = S.block_n;
     out->tokens_per_tile = S.tokens_per_tile;
     out->partial_rows = S.partial_rows;
@@ -207,16 +207,31 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
     L.bf16 = P.dtype == RPA_BF16;
     L.n_tiles = int64_t(S.tiles.size());
 
-    L.has_narrow = S.narrow_tiles > 0;
+    // One kernel for the wide tiles (tiles[0, wide)), one for the narrow tiles after them.
     // Profiling: an event pair stamped by each dispatch itself (start and end of the kernel).
     const bool prof = g_prof_on;
     ProfEv e0{nullptr, nullptr, 0}, e1{nullptr, nullptr, 1};
-    if (prof) {
-        e0.a = prof_event();
-        e0.b = prof_event();
+    hipError_t e = hipSuccess;
+    if (S.wide_tiles > 0) {
+        if (prof) {
+            e0.a = prof_event();
+            e0.b = prof_event();
+        }
+        L.n_tiles = S.wide_tiles;
+        e = rpa::launch_wide(L, st, e0.a, e0.b);
+        if (e != hipSuccess) return hip_err(e, "wide attention kernel launch");
     }
-    hipError_t e = rpa::launch_attention(L, st, e0.a, e0.b);
-    if (e != hipSuccess) return hip_err(e, "attention kernel launch");
+    if (S.narrow_tiles > 0) {
+        if (prof) {
+            e1.a = prof_event();
+            e1.b = prof_event();
+        }
+        rpa::LaunchAttn N = L;
+        N.a.tiles = L.a.tiles + S.wide_tiles;
+        N.n_tiles = S.narrow_tiles;
+        e = rpa::launch_narrow(N, st, e1.a, e1.b);
+        if (e != hipSuccess) return hip_err(e, "narrow attention kernel launch");
+    }
     if (prof) {
         std::lock_guard<std::mutex> lk(g_prof_mu);
         if (e0.a && e0.b) g_prof_events.push_back(e0);

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rpa_launch.h"
 #include "rpa_schedule.h"
 
@@ -124,9 +126,6 @@ __device__ __forceinline__ float xor32(float x) {
 // Lazy-rescale threshold (log2 units): P never exceeds 2^kLazy = 256.
 constexpr float kLazy = 8.0f;
 
-// XOR swizzle of the 16-byte groups of a transposed-V row, so that both the
-// 8-byte transposing writes and the 16-byte MFMA operand reads spread over banks.
-__device__ __forceinline__ int vt_swz(int d) { return (d + (d >> 3)) & 7; }
 
 
 // Device-coherent fp32 accesses for the split partials.  Agent-scope relaxed
@@ -221,11 +220,14 @@ __device__ __forceinline__ void finish_split(const AttnArgs& A, const Tile& T) {
 }
 
 template <int D>
-struct WideLds {
-    static constexpr int BN = 8192 / D;                 // keys per block
-    static constexpr int KS = D + 8;                    // K row stride in LDS (elements), 16-byte pad
-    static constexpr int stage = BN * KS + D * BN;      // elements of one K + V^T block
-    static constexpr int bytes = 2 * stage * 2;         // double buffered
+struct WideCfg {
+    static constexpr int BN = 8192 / D;             // keys per block
+    static constexpr int NC = 1;                    // 32-row MFMA column blocks per wave
+    static constexpr int RW = 32 * NC;              // query rows per wave
+    static constexpr int KS = D + 8;                // K row stride in LDS (elements), 16-byte pad
+    static constexpr int STAGE = BN * KS + D * BN;  // elements of one K block + one V^T block
+    static constexpr int NSTAGE = 2;                // LDS ring: block j and block j+1
+    static constexpr int bytes = NSTAGE * STAGE * 2;
 };
 
 template <int D>
@@ -237,89 +239,100 @@ struct NarrowLds {
     static constexpr int bytes = stage_bytes > combine_bytes ? stage_bytes : combine_bytes;
 };
 
-// Wide tile: up to 128 rows (4 waves x 32 rows), keys walked block by block by the
-// whole workgroup; see the file comment.
+// XOR swizzle of the 16-byte groups of a transposed-V row: the 8-byte transposing
+// writes (rows 8ch + e) and the 16-byte MFMA operand reads (rows 32db + lane) both
+// spread over the banks, and the read swizzle splits into a per-lane part and a
+// compile-time part.
+__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
+// Wide tile: up to block_m = 128 rows = 4 waves x 32 rows (token-major (token, qo
+// head) pairs of one kv head); keys in blocks of BN through a two-stage LDS ring; two
+// workgroups per CU.  Each wave software-pipelines in units of 32 keys: the basic
+// block that computes the exponentials and P V of one unit also issues Q K^T of the
+// next unit, so the matrix core and the VALU of one wave work on different units at
+// the same time.  Block j+1 is staged (and block j+2's gather issued) half-way
+// through block j, so the next block's first Q K^T finds it in LDS.
 template <int D, bool BF16>
 __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char* smem) {
-    constexpr int BN = WideLds<D>::BN;  // keys per block
-    constexpr int CH = D / 8;           // 16-byte chunks per K/V row
-    constexpr int KS = WideLds<D>::KS;  // K row stride in LDS (elements)
-    constexpr int SB = BN / 32;         // 32-key score blocks
-    constexpr int DK = D / 16;          // k-steps of Q K^T
-    constexpr int DB = D / 32;          // 32-wide d blocks of O
-    constexpr int KC = BN / 16;         // 16-key steps of P V
+    using C = WideCfg<D>;
+    constexpr int BN = C::BN, NC = C::NC, RW = C::RW, KS = C::KS, STAGE = C::STAGE;
+    constexpr int CH = D / 8;    // 16-byte chunks per K/V row
+    constexpr int SB = BN / 32;  // 32-key score blocks
+    constexpr int DK = D / 16;   // k-steps of Q K^T
+    constexpr int DB = D / 32;   // 32-wide d blocks of O
+    constexpr int KC = BN / 16;  // 16-key steps of P V
     static_assert(CH * (BN / 4) == 256, "each thread gathers 4 keys x 16 bytes");
-    // Two stages of [K block | V^T block]: block n is computed from stage n % 2 while
-    // block n+1 is written into the other, so one barrier per block suffices.
-    uint16_t* const lds0 = reinterpret_cast<uint16_t*>(smem);
-    constexpr int STAGE = WideLds<D>::stage;
+    uint16_t* const lds = reinterpret_cast<uint16_t*>(smem);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
     const int G = A.G;
     const int rows_valid = T.q_count * G;
-    const int row = wave * 32 + col;
-    const int tok = row / G, g = row - tok * G;
-    const bool row_ok = row < rows_valid;
-    const int pos = T.pos0 + tok;
-    const int64_t orow = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
 
-    // Q^T operand: 8 consecutive d per k-step, kept in VGPRs for the whole tile.
-    u32x4 qf[DK];
-    {
-        const uint16_t* qp = A.q + orow * D + 8 * half;
+    // This lane's query rows: column block c holds row wave*RW + 32c + col.
+    int pos[NC];
+    int64_t orow[NC];
+    bool row_ok[NC];
+    u32x4 qf[NC][DK];  // Q^T operand, 8 consecutive d per k-step, held for the whole tile
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int row = wave * RW + 32 * c + col;
+        const int tok = row / G, g = row - tok * G;
+        row_ok[c] = row < rows_valid;
+        pos[c] = T.pos0 + tok;
+        orow[c] = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
+        const uint16_t* qp = A.q + orow[c] * D + 8 * half;
 #pragma unroll
         for (int kk = 0; kk < DK; ++kk)
-            qf[kk] = row_ok ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
+            qf[c][kk] = row_ok[c] ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
     }
-    const int wrow0 = wave * 32;
-    const int wrows = min(32, rows_valid - wrow0);
-    const bool wave_active = wrows > 0;
-    const int wpos_min = T.pos0 + wrow0 / G;
-    const int wpos_max = T.pos0 + (wrow0 + max(wrows, 1) - 1) / G;
+    const int wpos_min = T.pos0 + (wave * RW) / G;  // smallest position among this wave's rows
 
-    // Gather mapping: thread -> keys 4kg..4kg+3 of the block, d = 8ch..8ch+7.
+    // ---- gather (global -> registers) and stage (registers -> LDS) of one block ----
+    // Thread -> keys 4kg..4kg+3 of the block (one page), d = 8ch..8ch+7.  The loads
+    // always use a valid address (a key past kv_len or a bad page reads page 0); the
+    // rare invalid keys are zeroed before staging.
     const int ch = tid % CH, kg = tid / CH;
     const int64_t slot_stride = (int64_t)A.Hkv * D;
     const uint16_t* kv_base = A.kv + (int64_t)T.kv_head * D + 8 * ch;
     u32x4 kreg[4], vreg[4];
-
-    // Gather of one block: always from a valid address (a key past kv_len, or a bad
-    // page, reads page `safe` instead), then the rare invalid keys are zeroed in a
-    // wave-uniform branch, so full blocks run without per-key branches.
+    bool g_ok = true;
+    int g_kv0 = 0;
     auto gather = [&](int kv0) {
-        const int key0 = kv0 + 4 * kg;  // 4-aligned: the 4 keys share a page
+        const int key0 = kv0 + 4 * kg;
         int page = 0;
         if (key0 < T.kv_len) page = A.page_idx[T.page_base + (key0 >> 4)];
         const bool page_ok = (unsigned)page < (unsigned)A.num_pages;
         if (!page_ok) *A.err_flag = 1;
-        const int pg = page_ok ? page : 0;
-        const uint16_t* src = kv_base + ((int64_t)pg * 32 + (key0 & 15)) * slot_stride;
+        const uint16_t* src = kv_base + ((int64_t)(page_ok ? page : 0) * 32 + (key0 & 15)) * slot_stride;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             kreg[i] = *(const u32x4*)(src + i * slot_stride);
             vreg[i] = *(const u32x4*)(src + (16 + i) * slot_stride);
         }
-        const bool tail = kv0 + BN > T.kv_len;
-        if (__builtin_amdgcn_ballot_w64(tail || !page_ok)) {
+        g_ok = page_ok;
+        g_kv0 = kv0;
+    };
+    auto fix_invalid = [&]() {
+        const int key0 = g_kv0 + 4 * kg;
+        if (__builtin_amdgcn_ballot_w64(!g_ok || g_kv0 + BN > T.kv_len)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (!page_ok || key0 + i >= T.kv_len) {
+                if (!g_ok || key0 + i >= T.kv_len) {
                     kreg[i] = u32x4{0, 0, 0, 0};
                     vreg[i] = u32x4{0, 0, 0, 0};
                 }
         }
     };
-
-    // Key slot order inside each 16-key chunk of V^T: bits 2 and 3 of the key
-    // swapped, so the 8 keys one lane feeds to a P V step are contiguous.
-    const int kb = 4 * kg;
-    const int vslot = (kb & ~15) | (((kb >> 2) & 1) << 3) | (((kb >> 3) & 1) << 2);
-    auto stage = [&](int buf) {
-        uint16_t* k_lds = lds0 + buf * STAGE;
+    // K goes to LDS as is; V is transposed into V^T (fp16) with the keys of each
+    // 16-key chunk in the order the P V MFMA consumes them (bits 2 and 3 swapped).
+    const int kb4 = 4 * kg;
+    const int vslot = (kb4 & ~15) | (((kb4 >> 2) & 1) << 3) | (((kb4 >> 3) & 1) << 2);
+    auto stage = [&](int st) {
+        uint16_t* k_lds = lds + st * STAGE;
         uint16_t* vt_lds = k_lds + BN * KS;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(k_lds + (kb + i) * KS + 8 * ch) = kreg[i];
+        for (int i = 0; i < 4; ++i) *(u32x4*)(k_lds + (kb4 + i) * KS + 8 * ch) = kreg[i];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int d = 8 * ch + e;
@@ -330,122 +343,174 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         }
     };
 
-    f32x16 oacc[DB];
+    // ---- per-lane LDS read offsets (elements, within a stage) ----
+    const int k_off = col * KS + 8 * half;  // + 32*kb*KS + 16*kk
+    // V^T row 32db + col, 16-byte group (2kc + half) ^ vt_swz(row): the group is
+    // (half ^ s_col) ^ (2kc ^ 4*(db & 1)) with s_col = (col ^ (col >> 3)) & 7.
+    const int s_col = (col ^ (col >> 3)) & 7;
+    int v_off[4];  // indexed by (2kc ^ 4(db&1)) / 2
 #pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-    float m = -INFINITY;  // running max of the scaled scores (log2 units)
-    float lsum = 0.f;     // this lane's share of the running sum
+    for (int k = 0; k < 4; ++k) v_off[k] = BN * KS + col * BN + 8 * ((half ^ s_col) ^ (2 * k));
 
+    // ---- state ----
+    f32x16 oacc[DB][NC];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) oacc[db][c] = f32x16{};
+    float m[NC], lsum[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        m[c] = -INFINITY;  // reference max of the scaled scores (log2 units)
+        lsum[c] = 0.f;     // this lane's share of the row sum
+    }
+
+    // The pipeline works in units of 32 keys (score block sb of LDS block j); scores
+    // of consecutive units alternate between two register buffers.
+    auto qk = [&](int st, int sb, f32x16 (&S)[NC]) {
+        const uint16_t* k_lds = lds + st * STAGE + k_off + 32 * sb * KS;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) S[c] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < DK; ++kk) {
+            const u32x4 kf = *(const u32x4*)(k_lds + 16 * kk);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) S[c] = mfma_qk(kf, qf[c][kk], S[c], BF16);
+        }
+    };
+
+    // One unit: scores of unit (j, SBI) are in S; Q K^T of the next unit goes to Sn.
+    // st_j / st_j1 are the LDS stages of blocks j and j+1.  Unit 0 stages block j+1
+    // (gathered during block j-1) and issues block j+2's gather; a barrier then makes
+    // block j+1 visible before the last unit's Q K^T reads it.  The barrier after the
+    // last unit ends every read of stage st_j before block j+2 overwrites it.
+    auto unit = [&](auto sbi, int j, int st_j, int st_j1, f32x16 (&S)[NC], f32x16 (&Sn)[NC]) {
+        constexpr int SBI = decltype(sbi)::value;
+        const int kv0 = T.kv_begin + j * BN + 32 * SBI;
+        if (SBI == 0) fix_invalid();  // block j+1's gathered keys, staged below
+        // mask (boundary units only)
+        if ((kv0 + 32 > T.kv_len) || (A.causal && kv0 + 31 > wpos_min)) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                    if (key >= T.kv_len || (A.causal && key > pos[c])) S[c][r] = -INFINITY;
+                }
+        }
+        // row max of the raw scores; lazy rescaling (see kLazy)
+        bool any_upd = false;
+        float bx[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float bmax = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, S[c][r]);
+            bmax = fmaxf(bmax, xor32(bmax));
+            bx[c] = bmax * A.c_log2;
+            any_upd |= bx[c] > m[c] + kLazy;
+        }
+        if (__builtin_amdgcn_ballot_w64(any_upd)) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const float m_new = bx[c] > m[c] + kLazy ? bx[c] : m[c];
+                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[c] - m_new);
+                m[c] = m_new;
+                lsum[c] *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) oacc[db][c] *= alpha;
+            }
+        }
+        float nm[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) nm[c] = m[c] == -INFINITY ? 0.f : -m[c];
+
+        // ---- one basic block: Q K^T (next unit) | exponentials | P V | stage ----
+        if (SBI + 1 < SB) qk(st_j, SBI + 1, Sn);
+        else qk(st_j1, 0, Sn);
+        u32x4 pf[NC][2];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const fp16x2 ph = __builtin_amdgcn_cvt_pkrtz(
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(S[c][8 * h + 2 * e], A.c_log2, nm[c])),
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(S[c][8 * h + 2 * e + 1], A.c_log2, nm[c])));
+                    lsum[c] = __builtin_amdgcn_fdot2(ph, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum[c], false);
+                    pf[c][h][e] = __builtin_bit_cast(uint32_t, ph);
+                }
+        const uint16_t* st_base = lds + st_j * STAGE;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int kc = 2 * SBI + h;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int vk = (kc ^ (2 * (db & 1))) & 3;  // (2kc ^ 4(db & 1)) / 2 within 4 chunks
+                const u32x4 vf = *(const u32x4*)(st_base + v_off[vk] + 32 * db * BN + 16 * (kc & ~3));
+#pragma unroll
+                for (int c = 0; c < NC; ++c) oacc[db][c] = mfma_pv(vf, pf[c][h], oacc[db][c]);
+            }
+        }
+        if (SBI == 0) {
+            stage(st_j1);
+            const int kvb = T.kv_begin + j * BN;
+            if (kvb + 2 * BN < T.kv_end) gather(kvb + 2 * BN);
+            __syncthreads();
+        }
+        if (SBI == SB - 1) __syncthreads();
+    };
+
+    // ---- prologue: block 0 staged, block 1 in flight, scores of unit 0 ----
     const int nblk = (T.kv_end - T.kv_begin + BN - 1) / BN;
     gather(T.kv_begin);
+    fix_invalid();
     stage(0);
     if (nblk > 1) gather(T.kv_begin + BN);
     __syncthreads();
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int kv0 = T.kv_begin + blk * BN;
-        const uint16_t* k_lds = lds0 + (blk & 1) * STAGE;
-        const uint16_t* vt_lds = k_lds + BN * KS;
-        // every row of this wave is masked for this block: nothing to compute
-        const bool skip = !wave_active || (A.causal && kv0 > wpos_max);
-        if (!skip) {
-
-        f32x16 s[SB];
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < DK; ++kk)
-#pragma unroll
-            for (int sb = 0; sb < SB; ++sb)
-                s[sb] = mfma_qk(*(const u32x4*)(k_lds + (32 * sb + col) * KS + 8 * half + 16 * kk), qf[kk], s[sb],
-                                BF16);
-
-        const bool need_mask = (kv0 + BN > T.kv_len) || (A.causal && kv0 + BN - 1 > wpos_min);
-        if (need_mask) {
-#pragma unroll
-            for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (key >= T.kv_len || (A.causal && key > pos)) s[sb][r] = -INFINITY;
-                }
+    f32x16 sa[NC], sb_[NC];
+    qk(0, 0, sa);
+    int st0 = 0;  // stage of block j; block j+1 goes to 1 - st0
+    for (int j = 0; j < nblk; ++j) {
+        unit(std::integral_constant<int, 0>{}, j, st0, 1 - st0, sa, sb_);
+        unit(std::integral_constant<int, 1>{}, j, st0, 1 - st0, sb_, sa);
+        if constexpr (SB == 4) {
+            unit(std::integral_constant<int, 2>{}, j, st0, 1 - st0, sa, sb_);
+            unit(std::integral_constant<int, 3>{}, j, st0, 1 - st0, sb_, sa);
         }
-        // Row max of the raw scores (the scale is positive, so it commutes with max).
-        float bmax = -INFINITY;
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, s[sb][r]);
-        bmax = fmaxf(bmax, xor32(bmax));
-        // Lazy rescaling: a row's reference m (log2 units) moves only when the block's
-        // max exceeds it by more than kLazy, so P = 2^(x - m) <= 2^kLazy (exact in
-        // fp16) and the O / l rescale is skipped unless some row of the wave moved.
-        const float bx = bmax * A.c_log2;
-        const bool upd = bx > m + kLazy;  // always true for a row's first visible block
-        if (__builtin_amdgcn_ballot_w64(upd)) {
-            const float m_new = upd ? bx : m;
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-            m = m_new;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        }
-        const float nm = m == -INFINITY ? 0.f : -m;  // a row with no visible key yet: P = 0
-
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-            const int sb = kc >> 1, r0 = (kc & 1) * 8;
-            // P = 2^(scale*log2(e)*s - m), rounded toward zero to fp16; the row sum is
-            // taken from the same rounded values, so the weights and their normaliser
-            // agree exactly.
-            u32x4 pf;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(
-                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r0 + 2 * e], A.c_log2, nm)),
-                    __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r0 + 2 * e + 1], A.c_log2, nm)));
-                lsum = __builtin_amdgcn_fdot2(h, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum, false);
-                pf[e] = __builtin_bit_cast(uint32_t, h);
-            }
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int d = 32 * db + col;
-                const u32x4 vf = *(const u32x4*)(vt_lds + d * BN + 8 * ((2 * kc + half) ^ vt_swz(d)));
-                oacc[db] = mfma_pv(vf, pf, oacc[db]);
-            }
-        }
-        }  // !skip
-        if (blk + 1 < nblk) {
-            stage((blk + 1) & 1);
-            if (blk + 2 < nblk) gather(kv0 + 2 * BN);
-        }
-        __syncthreads();
+        st0 = 1 - st0;
     }
 
-    const float ltot = lsum + xor32(lsum);
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    const float lse_val = ltot > 0.f ? (m + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
-    if (wave_active && row_ok) {
+    // ---- epilogue ----
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const float ltot = lsum[c] + xor32(lsum[c]);
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        const float lse_val = ltot > 0.f ? (m[c] + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+        if (!row_ok[c]) continue;
+        const int row = wave * RW + 32 * c + col;
         if (T.part < 0) {
-            uint16_t* op = A.o + orow * D + 4 * half;
+            uint16_t* op = A.o + orow[c] * D + 4 * half;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int jj = 0; jj < 4; ++jj) {
                     u32x2 w;
-                    w[0] = pack_out<BF16>(oacc[db][4 * j + 0] * inv, oacc[db][4 * j + 1] * inv);
-                    w[1] = pack_out<BF16>(oacc[db][4 * j + 2] * inv, oacc[db][4 * j + 3] * inv);
-                    *(u32x2*)(op + 32 * db + 8 * j) = w;
+                    w[0] = pack_out<BF16>(oacc[db][c][4 * jj + 0] * inv, oacc[db][c][4 * jj + 1] * inv);
+                    w[1] = pack_out<BF16>(oacc[db][c][4 * jj + 2] * inv, oacc[db][c][4 * jj + 3] * inv);
+                    *(u32x2*)(op + 32 * db + 8 * jj) = w;
                 }
-            if (A.lse && half == 0) A.lse[orow] = lse_val;
+            if (A.lse && half == 0) A.lse[orow[c]] = lse_val;
         } else {
             float* pp = A.part_o + ((int64_t)T.part + row) * D + 4 * half;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    f32x4 w = {oacc[db][4 * j] * inv, oacc[db][4 * j + 1] * inv, oacc[db][4 * j + 2] * inv,
-                               oacc[db][4 * j + 3] * inv};
-                    st_dev4(pp + 32 * db + 8 * j, w);
+                for (int jj = 0; jj < 4; ++jj) {
+                    f32x4 w = {oacc[db][c][4 * jj] * inv, oacc[db][c][4 * jj + 1] * inv,
+                               oacc[db][c][4 * jj + 2] * inv, oacc[db][c][4 * jj + 3] * inv};
+                    st_dev4(pp + 32 * db + 8 * jj, w);
                 }
             if (half == 0) st_dev(A.part_lse + T.part + row, lse_val);
         }
@@ -694,43 +759,59 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     if (T.part >= 0) finish_split<D, BF16>(A, T);
 }
 
+// Wide tiles: two workgroups per CU (two waves per SIMD).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_tile_kernel(AttnArgs A) {
+void attn_wide_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];
     if (T.q_count <= 0) return;
-    if (T.kind == kNarrow) narrow_tile<D, BF16>(A, T, smem);
-    else wide_tile<D, BF16>(A, T, smem);
+    wide_tile<D, BF16>(A, T, smem);
+}
+
+// Narrow tiles: two workgroups per CU, so twice the loads in flight per CU.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_narrow_kernel(AttnArgs A) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const Tile T = A.tiles[blockIdx.x];
+    if (T.q_count <= 0) return;
+    narrow_tile<D, BF16>(A, T, smem);
 }
 
 // ---- host-side launchers -----------------------------------------------------------------
 
-template <int D, bool BF16>
-hipError_t launch_attention_t(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-    const size_t lds = L.has_narrow ? size_t(NarrowLds<D>::bytes > WideLds<D>::bytes ? NarrowLds<D>::bytes
-                                                                                     : WideLds<D>::bytes)
-                                    : size_t(WideLds<D>::bytes);
-    static bool attr_set = false;  // raise the dynamic-LDS limit once per instantiation
+template <typename K>
+hipError_t launch_with_lds(K kernel, const LaunchAttn& L, int lds, hipStream_t stream, hipEvent_t ev0,
+                           hipEvent_t ev1) {
+    // Dynamic LDS above 64 KiB must be allowed per kernel; do it once per instantiation.
+    static bool attr_set = false;
     if (!attr_set) {
-        const int max_lds = NarrowLds<D>::bytes > WideLds<D>::bytes ? NarrowLds<D>::bytes : WideLds<D>::bytes;
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_tile_kernel<D, BF16>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipExtLaunchKernelGGL((attn_tile_kernel<D, BF16>), dim3((unsigned)L.n_tiles), dim3(256), (uint32_t)lds, stream,
-                          ev0, ev1, 0, L.a);
+    hipExtLaunchKernelGGL(kernel, dim3((unsigned)L.n_tiles), dim3(256), (uint32_t)lds, stream, ev0, ev1, 0, L.a);
     return hipGetLastError();
 }
 
-hipError_t launch_attention(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (L.n_tiles <= 0) return hipSuccess;
     if (L.head_dim == 128)
-        return L.bf16 ? launch_attention_t<128, true>(L, stream, ev0, ev1)
-                      : launch_attention_t<128, false>(L, stream, ev0, ev1);
-    return L.bf16 ? launch_attention_t<64, true>(L, stream, ev0, ev1)
-                  : launch_attention_t<64, false>(L, stream, ev0, ev1);
+        return L.bf16 ? launch_with_lds(&attn_wide_kernel<128, true>, L, WideCfg<128>::bytes, stream, ev0, ev1)
+                      : launch_with_lds(&attn_wide_kernel<128, false>, L, WideCfg<128>::bytes, stream, ev0, ev1);
+    return L.bf16 ? launch_with_lds(&attn_wide_kernel<64, true>, L, WideCfg<64>::bytes, stream, ev0, ev1)
+                  : launch_with_lds(&attn_wide_kernel<64, false>, L, WideCfg<64>::bytes, stream, ev0, ev1);
+}
+
+hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    if (L.n_tiles <= 0) return hipSuccess;
+    if (L.head_dim == 128)
+        return L.bf16 ? launch_with_lds(&attn_narrow_kernel<128, true>, L, NarrowLds<128>::bytes, stream, ev0, ev1)
+                      : launch_with_lds(&attn_narrow_kernel<128, false>, L, NarrowLds<128>::bytes, stream, ev0, ev1);
+    return L.bf16 ? launch_with_lds(&attn_narrow_kernel<64, true>, L, NarrowLds<64>::bytes, stream, ev0, ev1)
+                  : launch_with_lds(&attn_narrow_kernel<64, false>, L, NarrowLds<64>::bytes, stream, ev0, ev1);
 }
 
 }  // namespace rpa

@@ -25,15 +25,15 @@ struct AttnArgs {
 };
 
 struct LaunchAttn {
-    AttnArgs a;
+    AttnArgs a;       // a.tiles points at this launch's first tile
     int head_dim;
     bool bf16;
-    bool has_narrow;  // the plan has narrow tiles: reserve their LDS
     int64_t n_tiles;
 };
 
 
 // ev0 / ev1: optional events stamped at the start and end of the dispatch (NULL: none).
-hipError_t launch_attention(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 
 }  // namespace rpa

@@ -45,12 +45,13 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
         return fail(err, E_SHAPE, "head_dim %ld not supported (64 or 128)", p.head_dim);
     if (p.page_size != kPageSize) return fail(err, E_SHAPE, "page_size %ld not supported (16)", p.page_size);
     const int32_t G = p.num_qo_heads / p.num_kv_heads;
-    if (G > kBlockM) return fail(err, E_SHAPE, "query group %ld exceeds %ld heads per kv head", G, kBlockM);
+    if (G > kMaxGroup) return fail(err, E_SHAPE, "query group %ld exceeds %ld heads per kv head", G, kMaxGroup);
     if (p.max_kv_splits < 0) return fail(err, E_ARG, "max_kv_splits must be >= 0");
 
     Schedule S;
     S.block_n = block_n_for(p.head_dim);
-    S.tokens_per_tile = kBlockM / G;
+    S.block_m = block_m_for(p.head_dim);
+    S.tokens_per_tile = S.block_m / G;
     const int32_t BN = S.block_n, TQ = S.tokens_per_tile;
 
     if (batch > 0 && (qo_indptr[0] != 0 || kv_page_indptr[0] != 0))
@@ -174,9 +175,13 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     if (part_next > INT32_MAX) return fail(err, E_ARG, "too many partial rows");
     S.partial_rows = part_next;
 
-    // ---- launch order: longest first (LPT), ties in natural order --------------------------
-    std::stable_sort(pieces.begin(), pieces.end(),
-                     [](const Piece& a, const Piece& b) { return a.cost > b.cost; });
+    // ---- launch order: wide tiles, then narrow tiles (one kernel each); longest first
+    // (LPT) within each kind, ties in natural order ------------------------------------------
+    std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& a, const Piece& b) {
+        if (a.t.kind != b.t.kind) return a.t.kind == kWide;
+        return a.cost > b.cost;
+    });
+    S.wide_tiles = int64_t(pieces.size()) - S.narrow_tiles;
     S.tiles.reserve(pieces.size());
     for (auto& pc : pieces) S.tiles.push_back(pc.t);
     *out = std::move(S);

@@ -9,8 +9,12 @@
 namespace rpa {
 
 constexpr int kPageSize = 16;
-constexpr int kBlockM = 128;  // query rows (token x qo head of one kv group) per tile
-constexpr int kWaves = 4;     // wavefronts per workgroup, 32 query rows each
+constexpr int kMaxGroup = 128;  // largest number of qo heads per kv head
+constexpr int kWaves = 4;       // wavefronts per workgroup
+
+// Query rows (token x qo head of one kv group, token-major) per wide tile: each of
+// the 4 waves owns one 32-row MFMA column block.
+constexpr int block_m_for(int head_dim) { return head_dim > 0 ? 128 : 128; }
 
 constexpr int kNarrowRows = 16;  // tiles with at most this many rows take the narrow path
 constexpr int kWaveKeys = 64;     // keys one wave handles per step on the narrow path
@@ -68,7 +72,9 @@ struct Schedule {
     std::vector<Merge> merges;
     int64_t partial_rows = 0;
     int32_t tokens_per_tile = 0;
+    int32_t block_m = 0;
     int32_t block_n = 0;
+    int64_t wide_tiles = 0;     // tiles[0, wide_tiles) are wide, the rest narrow
     int32_t max_splits = 1;
     int64_t narrow_tiles = 0;
     int64_t total_q = 0;

@@ -99,10 +99,14 @@ def check_schedule(b: W.Batch, plan):
     assert info["partial_rows"] == n_part_rows
     # 3. tile kind: narrow (decode-like path) exactly when a tile has at most 16 rows
     assert all((r[F["kind"]] == 1) == (r[F["q_count"]] * G <= 16) for r in t)
-    # 4. longest-first launch order (keys walked, rounded to the path's step)
-    gran = [BN if r[F["kind"]] == 0 else 64 for r in t]
-    cost = [-(-(r[F["kv_end"]] - r[F["kv_begin"]]) // q) * q for r, q in zip(t, gran)]
-    assert all(x >= y for x, y in zip(cost, cost[1:]))
+    # 4. launch order: all wide tiles (one kernel), then all narrow tiles (another),
+    #    each longest-first (keys walked, rounded to the path's step)
+    kinds = [int(r[F["kind"]]) for r in t]
+    assert kinds == sorted(kinds)
+    for kind, gran in ((0, BN), (1, 64)):
+        sub = [r for r in t if r[F["kind"]] == kind]
+        cost = [-(-(r[F["kv_end"]] - r[F["kv_begin"]]) // gran) * gran for r in sub]
+        assert all(x >= y for x, y in zip(cost, cost[1:]))
     # 5. split pieces start at multiples of 256 keys
     assert all(r[F["kv_begin"]] % 256 == 0 for r in t)
     # 6. work counts

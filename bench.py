@@ -5,16 +5,16 @@
 
 Default workload (the headline line): decode, batch 128 x q_len 1 x kv_len
 1024, 8 qo / 1 kv heads, D 128, fp16, 64 contiguous pages per sequence (the
-flashinfer issue #323 repro shape).  A step is one forward call (attention
-kernel + split merge kernel) over the whole batch, with the plan built once
+flashinfer issue #323 repro shape).  A step is one forward call (one launch of
+the narrow-tile kernel, split pieces merged inside it) over the whole batch, with the plan built once
 beforehand (as begin_forward is in the pages) and its build time reported
 separately.  Eight copies of the KV cache are rotated so consecutive steps do
 not hit in the 256 MB last-level cache.
 
 value = KV GB/s = unique KV bytes of valid tokens / step time.
-roofline = the attention kernel's algorithmic bytes per launch (KV + Q + O +
-LSE + page table) / its average duration from HIP events recorded around each
-launch on the launch stream, against 8 TB/s HBM.
+roofline = the decode kernel's (attn_narrow_kernel) algorithmic bytes per
+launch (KV + Q + O + LSE + page table) / its average duration from HIP events
+stamped by each dispatch on the launch stream, against 8 TB/s HBM.
 cpu_baseline = the fp64 oracle on a bounded sample of the same batch.
 prefill = a secondary measurement on the long-prompt part of the mixed
 workload (4 causal prompts x 8192, 64 qo / 8 kv heads, bf16): TFLOP/s and
@@ -35,7 +35,7 @@ METRIC = "attention TFLOP/s (prefill) + KV GB/s (decode), % roofline, 1 MI355X"
 
 
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_ragged_amd", "csrc", "rpa_kernels.hip")
-COUNTERS = os.path.join(ROOT, "profiles", "attn_tile_kernel_decode_b128_kv1024_counters.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "attn_narrow_kernel_decode_b128_kv1024_counters.txt")
 
 
 def log(msg):
@@ -49,7 +49,7 @@ def kernel_source_hash():
 
 
 def recorded_traffic():
-    """HBM bytes per launch of the attention kernel on this workload, from the
+    """HBM bytes per launch of the decode kernel on this workload, from the
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/, or None when that
     summary is missing or was taken on a different kernel source."""
     try:
@@ -176,8 +176,9 @@ def bench_decode(args):
     ms, wall = time_steps(plan, b.q, kvs, o, lse, args.steps, args.warmup)
     kt = kernel_times(plan, b.q, kvs, o, lse, args.steps)
     flops, kv_bytes, alg_bytes = algorithmic(b, info)
-    n_attn, ms_attn = kt["attention"]
-    n_merge, ms_merge = kt["merge"]
+    n_attn, ms_attn = kt["narrow"]  # every tile of a q_len = 1, G = 8 batch is narrow
+    n_wide, _ = kt["wide"]
+    assert n_wide == 0 and n_attn == args.steps
     attn_avg = ms_attn / max(n_attn, 1)
     achieved = alg_bytes / (attn_avg * 1e-3) / 1e9
     res = {
@@ -189,11 +190,10 @@ def bench_decode(args):
                    "page_size": 16, "kv_cache_copies_rotated": len(kvs)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
-                     "kernel": "attn_tile_kernel", "avg_ms": attn_avg,
+                     "kernel": "attn_narrow_kernel", "avg_ms": attn_avg,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "tflops": flops / (ms * 1e-3) / 1e12,
-        "kernels": {"attention_avg_ms": attn_avg, "merge_avg_ms": ms_merge / max(n_merge, 1),
-                    "launches_per_step": (n_attn + n_merge) / args.steps},
+        "kernels": {"narrow_avg_ms": attn_avg, "launches_per_step": (n_attn + n_wide) / args.steps},
         "plan": {"host_ms": plan_ms, "tiles": info["num_tiles"], "split_groups": info["num_split_groups"],
                  "max_splits": info["max_splits"]},
         "wall_s_timed": wall,
@@ -219,13 +219,14 @@ def bench_prefill(args):
     ms, _ = time_steps(plan, b.q, [b.kv_cache], o, lse, steps, 2)
     kt = kernel_times(plan, b.q, [b.kv_cache], o, lse, steps)
     flops, kv_bytes, alg_bytes = algorithmic(b, info)
-    n_attn, ms_attn = kt["attention"]
+    n_attn, ms_attn = kt["wide"]  # causal prompts: every tile is wide
     attn_avg = ms_attn / max(n_attn, 1)
     tf = flops / (attn_avg * 1e-3) / 1e12
     plan.close()
     return {"workload": "mixed_long_prompts_4x8192", "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / MFMA_PEAK_TFLOPS, "avg_ms": attn_avg, "algorithmic_flops_per_launch": flops},
+                         "frac": tf / MFMA_PEAK_TFLOPS, "kernel": "attn_wide_kernel", "avg_ms": attn_avg,
+                         "algorithmic_flops_per_launch": flops},
             "dtype": b.dtype, "tiles": info["num_tiles"]}
 
 

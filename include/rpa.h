@@ -143,8 +143,10 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
  *   kv_cache  device [num_pages][2][page_size][num_kv_heads][head_dim], same dtype
  *   o         device [total_q][num_qo_heads][head_dim], same dtype (written)
  *   lse       device fp32 [total_q][num_qo_heads] (written), or NULL
- * Enqueues one kernel on `stream`; when the plan splits key ranges, the piece
- * of each split group that finishes last merges the group inside that kernel.
+ * Enqueues on `stream` one kernel for the plan's wide tiles (up to 128 query
+ * rows each) and one for its narrow tiles (up to 16 rows: decode-like), each
+ * only if the plan has such tiles; when the plan splits key ranges, the piece
+ * of each split group that finishes last merges the group inside its kernel.
  * No allocation, no host<->device synchronisation.  One run at a time per
  * (plan, workspace): the partial-result region and the split counters are
  * shared by all runs of a plan.
@@ -182,8 +184,8 @@ const char* rpa_version(void);
  * Kernel timing (benchmarks): while enabled, rpa_run has a HIP event pair
  * stamped by each kernel dispatch it enqueues (start and end of the kernel).
  * rpa_prof_stop synchronises those events and returns, per kernel kind
- * (0 = attention, 1 = reserved, always 0), the number of launches and their
- * summed duration in milliseconds.
+ * (0 = wide-tile kernel, 1 = narrow-tile kernel), the number of launches and
+ * their summed duration in milliseconds.
  */
 rpa_status rpa_prof_start(void);
 rpa_status rpa_prof_stop(int64_t counts_out[2], double ms_out[2]);

@@ -242,8 +242,9 @@ def prof_start():
 
 
 def prof_stop():
-    """{'attention': (launches, ms), 'merge': (launches, ms)} since prof_start()."""
+    """{'wide': (launches, ms), 'narrow': (launches, ms)} since prof_start(): the
+    kernel of the wide tiles and the kernel of the narrow (decode-like) tiles."""
     counts = (ctypes.c_int64 * 2)()
     ms = (ctypes.c_double * 2)()
     _check(load().rpa_prof_stop(counts, ms))
-    return {"attention": (counts[0], ms[0]), "merge": (counts[1], ms[1])}
+    return {"wide": (counts[0], ms[0]), "narrow": (counts[1], ms[1])}

@@ -78,7 +78,7 @@ typedef struct {
 typedef struct rpa_plan rpa_plan;
 
 typedef struct {
-    int64_t num_tiles;         /* attention work items (including split pieces)   */
+    int64_t num_tiles;         /* work items: split pieces and empty XCD padding  */
     int64_t num_split_groups;  /* query tiles whose key range is split            */
     int32_t max_splits;        /* largest split count of any query tile           */
     int32_t block_m;           /* query rows (token, head) per tile               */
@@ -111,7 +111,9 @@ rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
 
 /*
  * Copy of the plan's work items for inspection: up to `cap` records of 16
- * int32 each into `out_h` (host), in launch order.  Fields per record:
+ * int32 each into `out_h` (host), in launch order.  Wide records with
+ * [1] == 0 are empty padding that aligns tiles to XCDs (workgroup i of a launch
+ * runs on XCD i % 8).  Fields per record:
  *   [0] first query row, [1] query tokens, [2] position of the first query,
  *   [3] kv_len, [4] kv_page_indptr[b], [5] kv head, [6] first key, [7] end key,
  *   [8] first partial row (-1: writes O directly), [9] sequence, [10] split

@@ -260,7 +260,6 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     constexpr int SB = BN / 32;  // 32-key score blocks
     constexpr int DK = D / 16;   // k-steps of Q K^T
     constexpr int DB = D / 32;   // 32-wide d blocks of O
-    constexpr int KC = BN / 16;  // 16-key steps of P V
     static_assert(CH * (BN / 4) == 256, "each thread gathers 4 keys x 16 bytes");
     uint16_t* const lds = reinterpret_cast<uint16_t*>(smem);
 
@@ -289,19 +288,24 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     const int wpos_min = T.pos0 + (wave * RW) / G;  // smallest position among this wave's rows
 
     // ---- gather (global -> registers) and stage (registers -> LDS) of one block ----
-    // Thread -> keys 4kg..4kg+3 of the block (one page), d = 8ch..8ch+7.  The loads
-    // always use a valid address (a key past kv_len or a bad page reads page 0); the
-    // rare invalid keys are zeroed before staging.
+    // Thread -> keys 4kg..4kg+3 of the block (one page), d = 8ch..8ch+7.  The page
+    // index of the next gather is loaded one gather ahead, so its latency is never
+    // waited on.  The loads always use a valid address (a key past kv_len or a bad
+    // page reads page 0); the rare invalid keys are zeroed when staged.
     const int ch = tid % CH, kg = tid / CH;
     const int64_t slot_stride = (int64_t)A.Hkv * D;
     const uint16_t* kv_base = A.kv + (int64_t)T.kv_head * D + 8 * ch;
     u32x4 kreg[4], vreg[4];
     bool g_ok = true;
     int g_kv0 = 0;
+    int page_next = 0;  // page index of the next gather's keys (unchecked)
+    auto load_page = [&](int kv0) {
+        const int key0 = kv0 + 4 * kg;
+        page_next = key0 < T.kv_len ? A.page_idx[T.page_base + (key0 >> 4)] : 0;
+    };
     auto gather = [&](int kv0) {
         const int key0 = kv0 + 4 * kg;
-        int page = 0;
-        if (key0 < T.kv_len) page = A.page_idx[T.page_base + (key0 >> 4)];
+        const int page = page_next;
         const bool page_ok = (unsigned)page < (unsigned)A.num_pages;
         if (!page_ok) *A.err_flag = 1;
         const uint16_t* src = kv_base + ((int64_t)(page_ok ? page : 0) * 32 + (key0 & 15)) * slot_stride;
@@ -312,23 +316,13 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         }
         g_ok = page_ok;
         g_kv0 = kv0;
-    };
-    auto fix_invalid = [&]() {
-        const int key0 = g_kv0 + 4 * kg;
-        if (__builtin_amdgcn_ballot_w64(!g_ok || g_kv0 + BN > T.kv_len)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!g_ok || key0 + i >= T.kv_len) {
-                    kreg[i] = u32x4{0, 0, 0, 0};
-                    vreg[i] = u32x4{0, 0, 0, 0};
-                }
-        }
+        if (kv0 + BN < T.kv_end) load_page(kv0 + BN);
     };
     // K goes to LDS as is; V is transposed into V^T (fp16) with the keys of each
     // 16-key chunk in the order the P V MFMA consumes them (bits 2 and 3 swapped).
     const int kb4 = 4 * kg;
     const int vslot = (kb4 & ~15) | (((kb4 >> 2) & 1) << 3) | (((kb4 >> 3) & 1) << 2);
-    auto stage = [&](int st) {
+    auto store_stage = [&](int st) {
         uint16_t* k_lds = lds + st * STAGE;
         uint16_t* vt_lds = k_lds + BN * KS;
 #pragma unroll
@@ -340,6 +334,23 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             w[0] = v_pair<BF16>(vreg[0], vreg[1], e);
             w[1] = v_pair<BF16>(vreg[2], vreg[3], e);
             *(u32x2*)(vt_lds + d * BN + 8 * ((vslot >> 3) ^ vt_swz(d)) + (vslot & 7)) = w;
+        }
+    };
+    // Keys past kv_len and keys of a bad page are staged as zeros.  The test is
+    // wave-uniform and each side stages on its own, so the common path moves no
+    // registers.
+    auto stage = [&](int st) {
+        const int key0 = g_kv0 + 4 * kg;
+        if (__builtin_amdgcn_ballot_w64(!g_ok || g_kv0 + BN > T.kv_len)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (!g_ok || key0 + i >= T.kv_len) {
+                    kreg[i] = u32x4{0, 0, 0, 0};
+                    vreg[i] = u32x4{0, 0, 0, 0};
+                }
+            store_stage(st);
+        } else {
+            store_stage(st);
         }
     };
 
@@ -387,7 +398,6 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     auto unit = [&](auto sbi, int j, int st_j, int st_j1, f32x16 (&S)[NC], f32x16 (&Sn)[NC]) {
         constexpr int SBI = decltype(sbi)::value;
         const int kv0 = T.kv_begin + j * BN + 32 * SBI;
-        if (SBI == 0) fix_invalid();  // block j+1's gathered keys, staged below
         // mask (boundary units only)
         if ((kv0 + 32 > T.kv_len) || (A.causal && kv0 + 31 > wpos_min)) {
 #pragma unroll
@@ -464,8 +474,8 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
 
     // ---- prologue: block 0 staged, block 1 in flight, scores of unit 0 ----
     const int nblk = (T.kv_end - T.kv_begin + BN - 1) / BN;
+    load_page(T.kv_begin);
     gather(T.kv_begin);
-    fix_invalid();
     stage(0);
     if (nblk > 1) gather(T.kv_begin + BN);
     __syncthreads();

@@ -10,6 +10,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <map>
 #include <numeric>
 
 namespace rpa {
@@ -29,6 +30,62 @@ struct QTile {
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Piece { Tile t; int64_t cost; };
+
+// Wide tiles re-read the keys of their (sequence, kv head) -- a "stream" -- once per
+// query tile, so they are ordered for the L2 caches: workgroup i of a launch runs on
+// XCD i % kXcds, and each XCD has its own L2.  Streams are laid out one after the
+// other (largest total cost first; within a stream, longest tile first) and the
+// list is cut into kXcds runs of about equal cost; run x fills the launch slots
+// x, x + kXcds, x + 2 kXcds, ...  An XCD thus works through few streams at a time,
+// and concurrent tiles of a stream share its K/V blocks in that XCD's L2.  Runs are
+// padded with empty tiles (q_count 0: the kernel returns at once) so that every
+// tile lands on its run's XCD.  Small launches keep plain longest-first order.
+void order_wide_for_xcds(std::vector<Piece>& wide) {
+    auto lpt = [](const Piece& a, const Piece& b) { return a.cost > b.cost; };
+    if (wide.size() < size_t(4 * kXcds)) {
+        std::stable_sort(wide.begin(), wide.end(), lpt);
+        return;
+    }
+    std::map<std::pair<int32_t, int32_t>, int64_t> stream_cost;
+    int64_t total = 0;
+    for (const auto& pc : wide) {
+        stream_cost[{pc.t.seq, pc.t.kv_head}] += pc.cost;
+        total += pc.cost;
+    }
+    std::stable_sort(wide.begin(), wide.end(), [&](const Piece& a, const Piece& b) {
+        const auto ka = std::make_pair(a.t.seq, a.t.kv_head), kb = std::make_pair(b.t.seq, b.t.kv_head);
+        if (ka != kb) {
+            const int64_t ca = stream_cost[ka], cb = stream_cost[kb];
+            return ca != cb ? ca > cb : ka < kb;
+        }
+        return a.cost > b.cost;
+    });
+    std::vector<std::vector<Piece>> run(kXcds);
+    int64_t acc = 0;
+    for (const auto& pc : wide) {
+        // the run whose share of the total cost holds this tile's midpoint
+        const int64_t mid = acc + pc.cost / 2;
+        const int x = int(std::min<int64_t>(kXcds - 1, mid * kXcds / std::max<int64_t>(total, 1)));
+        run[x].push_back(pc);
+        acc += pc.cost;
+    }
+    size_t len = 0;
+    for (const auto& r : run) len = std::max(len, r.size());
+    Piece empty{};
+    empty.t.kind = kWide;
+    empty.t.part = -1;
+    empty.t.group = -1;
+    empty.t.seq = -1;
+    empty.t.n_splits = 1;
+    std::vector<Piece> out;
+    out.reserve(len * kXcds);
+    for (size_t k = 0; k < len; ++k)
+        for (int x = 0; x < kXcds; ++x) out.push_back(k < run[x].size() ? run[x][k] : empty);
+    while (!out.empty() && out.back().t.q_count == 0) out.pop_back();  // not launched
+    wide.swap(out);
+}
 
 }  // namespace
 
@@ -127,7 +184,6 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     }
 
     // ---- expand into pieces ------------------------------------------------------------
-    struct Piece { Tile t; int64_t cost; };
     std::vector<Piece> pieces;
     pieces.reserve(base.size());
     int64_t part_next = 0;
@@ -175,15 +231,16 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     if (part_next > INT32_MAX) return fail(err, E_ARG, "too many partial rows");
     S.partial_rows = part_next;
 
-    // ---- launch order: wide tiles, then narrow tiles (one kernel each); longest first
-    // (LPT) within each kind, ties in natural order ------------------------------------------
-    std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& a, const Piece& b) {
-        if (a.t.kind != b.t.kind) return a.t.kind == kWide;
-        return a.cost > b.cost;
-    });
-    S.wide_tiles = int64_t(pieces.size()) - S.narrow_tiles;
-    S.tiles.reserve(pieces.size());
-    for (auto& pc : pieces) S.tiles.push_back(pc.t);
+    // ---- launch order: wide tiles (one kernel), then narrow tiles (another) ----------------
+    std::vector<Piece> wide, narrow;
+    for (auto& pc : pieces) (pc.t.kind == kWide ? wide : narrow).push_back(pc);
+    // Narrow tiles read their keys once: longest first (LPT), ties in natural order.
+    std::stable_sort(narrow.begin(), narrow.end(), [](const Piece& a, const Piece& b) { return a.cost > b.cost; });
+    order_wide_for_xcds(wide);
+    S.wide_tiles = int64_t(wide.size());
+    S.tiles.reserve(wide.size() + narrow.size());
+    for (auto& pc : wide) S.tiles.push_back(pc.t);
+    for (auto& pc : narrow) S.tiles.push_back(pc.t);
     *out = std::move(S);
     return OK;
 }

@@ -18,6 +18,7 @@ constexpr int block_m_for(int head_dim) { return head_dim > 0 ? 128 : 128; }
 
 constexpr int kNarrowRows = 16;  // tiles with at most this many rows take the narrow path
 constexpr int kWaveKeys = 64;     // keys one wave handles per step on the narrow path
+constexpr int kXcds = 8;          // MI355X: workgroup i of a launch runs on XCD i % 8
 constexpr int kChunkKeys = 256;   // split pieces start at multiples of this many keys
 
 // Keys per inner block of the wide path: one K block plus one V block fill 16 KiB each.

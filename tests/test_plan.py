@@ -55,6 +55,9 @@ def check_schedule(b: W.Batch, plan):
     #    tile's pieces cover [0, kv_end) exactly once, in order, block-aligned
     seen = {}
     for rec in t:
+        if rec[F["q_count"]] == 0:  # empty padding tile (XCD alignment of wide tiles)
+            assert rec[F["kind"]] == 0 and rec[F["part"]] == -1 and rec[F["kv_end"]] == rec[F["kv_begin"]]
+            continue
         key = (rec[F["seq"]], rec[F["kv_head"]], rec[F["q_row0"]])
         seen.setdefault(key, []).append(rec)
     covered = np.zeros((b.total_q, b.num_kv_heads), np.int32)
@@ -98,15 +101,34 @@ def check_schedule(b: W.Batch, plan):
         assert a1 <= c0
     assert info["partial_rows"] == n_part_rows
     # 3. tile kind: narrow (decode-like path) exactly when a tile has at most 16 rows
-    assert all((r[F["kind"]] == 1) == (r[F["q_count"]] * G <= 16) for r in t)
-    # 4. launch order: all wide tiles (one kernel), then all narrow tiles (another),
-    #    each longest-first (keys walked, rounded to the path's step)
+    assert all((r[F["kind"]] == 1) == (0 < r[F["q_count"]] * G <= 16) for r in t)
+    # 4. launch order: all wide tiles (one kernel), then all narrow tiles (another).
+    #    Narrow tiles go longest first (keys walked, rounded to 64).  Wide tiles go
+    #    longest first in small launches; in larger ones, launch slot i runs on XCD
+    #    i % 8 and each XCD's slots hold each (sequence, kv head) stream as one
+    #    contiguous, longest-first run.
     kinds = [int(r[F["kind"]]) for r in t]
     assert kinds == sorted(kinds)
-    for kind, gran in ((0, BN), (1, 64)):
-        sub = [r for r in t if r[F["kind"]] == kind]
-        cost = [-(-(r[F["kv_end"]] - r[F["kv_begin"]]) // gran) * gran for r in sub]
-        assert all(x >= y for x, y in zip(cost, cost[1:]))
+
+    def cost(r, gran):
+        return -(-(r[F["kv_end"]] - r[F["kv_begin"]]) // gran) * gran
+
+    narrow = [cost(r, 64) for r in t if r[F["kind"]] == 1]
+    assert all(x >= y for x, y in zip(narrow, narrow[1:]))
+    wide = [r for r in t if r[F["kind"]] == 0]
+    if len(wide) < 32:
+        c = [cost(r, BN) for r in wide]
+        assert all(x >= y for x, y in zip(c, c[1:])) and all(r[F["q_count"]] > 0 for r in wide)
+    else:
+        assert wide[-1][F["q_count"]] > 0
+        for x in range(8):
+            lane = [r for r in wide[x::8] if r[F["q_count"]] > 0]
+            streams = [(int(r[F["seq"]]), int(r[F["kv_head"]])) for r in lane]
+            starts = [s for i, s in enumerate(streams) if i == 0 or streams[i - 1] != s]
+            assert len(starts) == len(set(starts)), "a stream is split within one XCD's slots"
+            for a, c in zip(lane, lane[1:]):
+                if (a[F["seq"]], a[F["kv_head"]]) == (c[F["seq"]], c[F["kv_head"]]):
+                    assert cost(a, BN) >= cost(c, BN)
     # 5. split pieces start at multiples of 256 keys
     assert all(r[F["kv_begin"]] % 256 == 0 for r in t)
     # 6. work counts

@@ -21,7 +21,9 @@
  *   position kv_len - q_len + i, and with causal != 0 it sees keys 0..that
  *   position (llama.cpp discussion #15958, "Pad for prefill stage?": real
  *   tokens first, fully masked tails skipped); with causal == 0 it sees all
- *   kv_len keys.  qo head h reads kv head h / (num_qo_heads / num_kv_heads).
+ *   kv_len keys, and q_len may exceed kv_len (one shared prefix attended by
+ *   many requests' queries, the first half of a cascade; vLLM issue #227).
+ *   qo head h reads kv head h / (num_qo_heads / num_kv_heads).
  *
  *   O[row][h][:] = sum_j softmax_j(sm_scale * <Q[row][h], K_j>) * V_j   (input dtype,
  *                  rounded to nearest-even from fp32)
@@ -54,7 +56,8 @@ typedef enum {
     RPA_E_SHAPE = 2,           /* heads / head_dim / page_size not supported      */
     RPA_E_INDPTR = 3,          /* an indptr does not start at 0 or decreases      */
     RPA_E_LAST_PAGE_LEN = 4,   /* kv_last_page_len outside [1, page_size]         */
-    RPA_E_QLEN_GT_KVLEN = 5,   /* a sequence has more queries than cached tokens  */
+    RPA_E_QLEN_GT_KVLEN = 5,   /* causal: q_len > kv_len; non-causal: queries but
+                                  no cached token                                 */
     RPA_E_WORKSPACE = 6,       /* workspace too small or misaligned               */
     RPA_E_UNSUPPORTED = 7,     /* valid request this build does not implement     */
     RPA_E_HIP = 8,             /* a HIP runtime call failed (message has details) */
@@ -175,6 +178,29 @@ void rpa_plan_destroy(rpa_plan* plan);
  */
 rpa_status rpa_validate_page_table(int32_t batch, const int32_t* kv_page_indptr_h,
                                    const int32_t* kv_page_indices_h, int64_t num_pages);
+
+/*
+ * Merge two attention states of the same query rows computed over disjoint key
+ * sets A and B (the split-KV merge applied to whole outputs; it joins the two
+ * halves of a cascade: a prefix shared by many requests, attended once for all of
+ * them with causal == 0, plus each request's private suffix; vLLM issue #227,
+ * "Question about efficient memory sharing"):
+ *   w_x = exp(LSE_x - max(LSE_a, LSE_b)),
+ *   O   = (w_a O_a + w_b O_b) / (w_a + w_b)   (rounded to nearest-even to dtype),
+ *   LSE = max(LSE_a, LSE_b) + ln(w_a + w_b).
+ * A state with LSE = -inf has weight 0 and its O values are ignored (they may be
+ * anything, NaN included); when both do, O = 0 and LSE = -inf.
+ *   o_a, o_b, o   device [rows][num_heads][head_dim], dtype, 16-byte aligned
+ *   lse_a, lse_b  device fp32 [rows][num_heads]
+ *   lse           device fp32 [rows][num_heads] (written), or NULL
+ * o may alias o_a or o_b, and lse may alias lse_a or lse_b (in-place merge).
+ * Enqueues one kernel on `stream`; no allocation, no synchronisation.
+ * Errors: E_ARG (NULL pointer, misaligned O, bad dtype), E_SHAPE (head_dim not
+ * 64 or 128), E_HIP (launch failure).
+ */
+rpa_status rpa_merge_states(int64_t rows, int32_t num_heads, int32_t head_dim, int32_t dtype, const void* o_a,
+                            const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+                            void* stream);
 
 /* Thread-local message describing the last non-OK status ("" if none). */
 const char* rpa_last_error(void);

@@ -19,7 +19,13 @@ What is computed, and where it comes from:
     tails skipped);
   * grouped-query heads (qo head h reads kv head h // (H_qo // H_kv)):
     flashinfer issue #323 (64/8 qo heads over 8/8 kv heads);
-  * softmax attention and its log-sum-exp, in natural log.
+  * softmax attention and its log-sum-exp, in natural log;
+  * ``merge_states``: two attention states of the same query rows over
+    disjoint key sets combined into the state over their union, with weights
+    exp(LSE_x - max LSE) (the split-KV merge behind kv-parallelism in
+    flashinfer issue #323, and the join of a cascade's shared-prefix and
+    private halves in vLLM issue #227, "Question about efficient memory
+    sharing").  Plain numpy in binary64.
 """
 from __future__ import annotations
 
@@ -133,4 +139,28 @@ def run(*, qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, q, kv_c
                             0 if rows_a is None else len(rows_a), int(nthreads))
     if rc != 0:
         raise ValueError("oracle rejected the input: %s" % ERRORS.get(rc, rc))
+    return o, lse
+
+
+def merge_states(o_a, lse_a, o_b, lse_b):
+    """(O, LSE) over the union of two disjoint key sets from the states over each:
+    m = max(LSE_a, LSE_b), w_x = exp(LSE_x - m), O = (w_a O_a + w_b O_b) / (w_a + w_b),
+    LSE = m + ln(w_a + w_b).  A state with LSE = -inf (no visible key) has weight 0
+    and its O is not used (it may hold anything); with no visible key in either,
+    O = 0 and LSE = -inf.  Inputs of any float type,
+    O [..., D], LSE [...]; binary64 out."""
+    o_a, o_b = np.asarray(o_a, np.float64), np.asarray(o_b, np.float64)
+    lse_a, lse_b = np.asarray(lse_a, np.float64), np.asarray(lse_b, np.float64)
+    m = np.maximum(lse_a, lse_b)
+    none = np.isneginf(m)
+    mu = np.where(none, 0.0, m)
+    wa, wb = np.exp(lse_a - mu), np.exp(lse_b - mu)
+    tot = wa + wb
+    with np.errstate(invalid="ignore", divide="ignore"):
+        ta = np.where((wa > 0)[..., None], wa[..., None] * o_a, 0.0)  # a weight-0 state's O is unused
+        tb = np.where((wb > 0)[..., None], wb[..., None] * o_b, 0.0)
+        o = (ta + tb) / tot[..., None]
+        lse = mu + np.log(tot)
+    o[none] = 0.0
+    lse[none] = -np.inf
     return o, lse

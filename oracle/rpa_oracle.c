@@ -28,7 +28,11 @@
  *   sits at position pos = kv_len - q_len + i and, when causal, sees keys
  *   0..pos; otherwise it sees all kv_len keys (llama.cpp discussion #15958,
  *   "Pad for prefill stage?": prompts are real tokens followed by padding,
- *   and the FlashAttention kernel's mask hides the tail).
+ *   and the FlashAttention kernel's mask hides the tail).  A causal sequence
+ *   needs q_len <= kv_len; a non-causal one may have more queries than keys
+ *   (the shared-prefix segment of a cascade: every request's queries against
+ *   one prefix, vLLM issue #227, "Question about efficient memory sharing"),
+ *   but at least one key when it has queries.
  *
  *   Query head h reads kv head h / (num_qo_heads / num_kv_heads) (grouped
  *   query attention with contiguous groups; flashinfer issue #323 uses
@@ -213,7 +217,11 @@ int rpa_oracle_run(int32_t batch, const int32_t* qo_indptr, const int32_t* kv_pa
         int32_t np = kv_page_indptr[b + 1] - kv_page_indptr[b];
         if (np > 0 && (kv_last_page_len[b] < 1 || kv_last_page_len[b] > page_size)) return ORC_E_LAST_PAGE_LEN;
         int32_t kv_len = np == 0 ? 0 : (np - 1) * page_size + kv_last_page_len[b];
-        if (qo_indptr[b + 1] - qo_indptr[b] > kv_len) return ORC_E_QLEN_GT_KVLEN;
+        int32_t q_len = qo_indptr[b + 1] - qo_indptr[b];
+        /* Causal queries are the last q_len of kv_len positions, so q_len <= kv_len;
+         * non-causal queries see all kv_len keys, any number of them, but need at
+         * least one key. */
+        if (causal ? q_len > kv_len : (q_len > 0 && kv_len == 0)) return ORC_E_QLEN_GT_KVLEN;
         for (int32_t p = kv_page_indptr[b]; p < kv_page_indptr[b + 1]; ++p)
             if (kv_page_indices[p] < 0 || kv_page_indices[p] >= num_pages) return ORC_E_PAGE_OOB;
         if (kv_len > max_kv) max_kv = kv_len;

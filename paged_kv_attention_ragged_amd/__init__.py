@@ -81,6 +81,7 @@ def load():
             "rpa_version": (ctypes.c_char_p, []),
             "rpa_prof_start": (st, []),
             "rpa_prof_stop": (st, [P, P]),
+            "rpa_merge_states": (st, [i64, i32, i32, i32, P, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -235,6 +236,32 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
+    """Merge two attention states of the same rows over disjoint key sets:
+    o_* [rows, H, D] (fp16 / bf16 CUDA tensors), lse_* [rows, H] fp32.  Returns
+    (O, LSE); `out` / `lse_out` may be o_a / lse_a for an in-place merge."""
+    import torch
+    rows, H, D = o_a.shape
+    for t in (o_a, o_b):
+        if t.shape != o_a.shape or t.dtype != o_a.dtype or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("o_a and o_b must be contiguous CUDA tensors of one shape and dtype")
+    for t in (lse_a, lse_b):
+        if tuple(t.shape) != (rows, H) or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("lse_a and lse_b must be contiguous fp32 CUDA tensors [rows, H]")
+    if out is None:
+        out = torch.empty_like(o_a)
+    elif out.shape != o_a.shape or out.dtype != o_a.dtype or not out.is_contiguous():
+        raise ValueError("out must match o_a")
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    if stream is None:
+        stream = torch.cuda.current_stream(o_a.device)
+    _check(load().rpa_merge_states(rows, H, D, _dtype_code(o_a.dtype), o_a.data_ptr(), lse_a.data_ptr(),
+                                   o_b.data_ptr(), lse_b.data_ptr(), out.data_ptr(), lse_out.data_ptr(),
+                                   stream.cuda_stream))
+    return out, lse_out
 
 
 def prof_start():

@@ -277,6 +277,33 @@ rpa_status rpa_validate_page_table(int32_t batch, const int32_t* kv_page_indptr_
     return RPA_OK;
 }
 
+rpa_status rpa_merge_states(int64_t rows, int32_t num_heads, int32_t head_dim, int32_t dtype, const void* o_a,
+                            const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+                            void* stream) {
+    if (rows < 0 || num_heads < 1) return set_err(RPA_E_ARG, "rows must be >= 0 and num_heads >= 1");
+    if (head_dim != 64 && head_dim != 128)
+        return set_err(RPA_E_SHAPE, "head_dim " + std::to_string(head_dim) + " not supported (64 or 128)");
+    if (dtype != RPA_F16 && dtype != RPA_BF16) return set_err(RPA_E_ARG, "dtype must be RPA_F16 or RPA_BF16");
+    if (rows == 0) return RPA_OK;
+    if (!o_a || !lse_a || !o_b || !lse_b || !o)
+        return set_err(RPA_E_ARG, "o_a, lse_a, o_b, lse_b and o must be non-NULL");
+    auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+    if (misaligned(o_a) || misaligned(o_b) || misaligned(o))
+        return set_err(RPA_E_ARG, "o_a, o_b and o must be 16-byte aligned");
+    rpa::MergeArgs M{};
+    M.o_a = static_cast<const uint16_t*>(o_a);
+    M.lse_a = lse_a;
+    M.o_b = static_cast<const uint16_t*>(o_b);
+    M.lse_b = lse_b;
+    M.o = static_cast<uint16_t*>(o);
+    M.lse = lse;
+    M.items = rows * num_heads * (head_dim / 8);
+    M.head_dim = head_dim;
+    const hipError_t e = rpa::launch_merge(M, dtype == RPA_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_err(e, "merge kernel launch");
+    return RPA_OK;
+}
+
 rpa_status rpa_prof_start(void) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof_on = true;

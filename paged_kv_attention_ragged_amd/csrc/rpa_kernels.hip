@@ -791,6 +791,52 @@ void attn_narrow_kernel(AttnArgs A) {
 
 // ---- host-side launchers -----------------------------------------------------------------
 
+// Merge of two attention states over disjoint key sets A and B of the same query
+// rows: with weights w = exp(LSE - max(LSE_a, LSE_b)),
+//   O = (w_a O_a + w_b O_b) / (w_a + w_b),  LSE = max + ln(w_a + w_b).
+// It is the split-KV merge applied to whole outputs (kv-parallelism, flashinfer
+// issue #323) and joins the two halves of a cascade: a prefix shared by many
+// requests attended once for all of them, plus each request's private suffix
+// (vLLM issue #227, "Question about efficient memory sharing").  A state with
+// LSE = -inf (no visible key) has weight 0 and its O is not read into the sum
+// (it may hold anything); if both have none, O = 0 and LSE = -inf.  One thread per 8 elements of a (row, head); the head_dim / 8
+// threads of a (row, head) are adjacent lanes of one wave, so every one of them
+// has read LSE_a and LSE_b before the wave's LSE store: O and LSE may be merged
+// in place.
+template <bool BF16>
+__device__ __forceinline__ float elem16(uint32_t w, int hi) {
+    const uint16_t h = uint16_t(hi ? (w >> 16) : (w & 0xffffu));
+    if (BF16) return __builtin_bit_cast(float, uint32_t(h) << 16);
+    return float(__builtin_bit_cast(_Float16, h));
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void merge_states_kernel(MergeArgs M) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= M.items) return;
+    const int C = M.head_dim / 8;
+    const int64_t rh = i / C;
+    const int c = int(i - rh * C);
+    const float la = M.lse_a[rh], lb = M.lse_b[rh];
+    const float mx = fmaxf(la, lb);
+    const float mu = mx == -INFINITY ? 0.f : mx;
+    const float wa = __expf(la - mu), wb = __expf(lb - mu);
+    const float sum = wa + wb;
+    const float inv = sum > 0.f ? 1.f / sum : 0.f;
+    const int64_t off = rh * M.head_dim + 8 * c;
+    const u32x4 a = *(const u32x4*)(M.o_a + off);
+    const u32x4 b = *(const u32x4*)(M.o_b + off);
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        r[e] = pack_out<BF16>(((wa > 0.f ? wa * elem16<BF16>(a[e], 0) : 0.f) +
+                               (wb > 0.f ? wb * elem16<BF16>(b[e], 0) : 0.f)) * inv,
+                              ((wa > 0.f ? wa * elem16<BF16>(a[e], 1) : 0.f) +
+                               (wb > 0.f ? wb * elem16<BF16>(b[e], 1) : 0.f)) * inv);
+    *(u32x4*)(M.o + off) = r;
+    if (M.lse && c == 0) M.lse[rh] = sum > 0.f ? mu + __logf(sum) : -INFINITY;
+}
+
 template <typename K>
 hipError_t launch_with_lds(K kernel, const LaunchAttn& L, int lds, hipStream_t stream, hipEvent_t ev0,
                            hipEvent_t ev1) {
@@ -822,6 +868,16 @@ hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0
                       : launch_with_lds(&attn_narrow_kernel<128, false>, L, NarrowLds<128>::bytes, stream, ev0, ev1);
     return L.bf16 ? launch_with_lds(&attn_narrow_kernel<64, true>, L, NarrowLds<64>::bytes, stream, ev0, ev1)
                   : launch_with_lds(&attn_narrow_kernel<64, false>, L, NarrowLds<64>::bytes, stream, ev0, ev1);
+}
+
+hipError_t launch_merge(const MergeArgs& M, bool bf16, hipStream_t stream) {
+    if (M.items <= 0) return hipSuccess;
+    const int64_t blocks = (M.items + 255) / 256;
+    if (bf16)
+        hipLaunchKernelGGL(merge_states_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, M);
+    else
+        hipLaunchKernelGGL(merge_states_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, M);
+    return hipGetLastError();
 }
 
 }  // namespace rpa

@@ -32,8 +32,21 @@ struct LaunchAttn {
 };
 
 
+// Merge of two attention states (O, LSE) computed over disjoint key sets.
+struct MergeArgs {
+    const uint16_t* o_a;  // [items / (head_dim / 8)][head_dim]: rows x heads x head_dim
+    const float* lse_a;   // one per (row, head)
+    const uint16_t* o_b;
+    const float* lse_b;
+    uint16_t* o;          // may alias o_a or o_b
+    float* lse;           // may alias lse_a or lse_b; NULL: not written
+    int64_t items;        // (row, head, 8-element chunk) triples
+    int32_t head_dim;
+};
+
 // ev0 / ev1: optional events stamped at the start and end of the dispatch (NULL: none).
 hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_merge(const MergeArgs& M, bool bf16, hipStream_t stream);
 
 }  // namespace rpa

@@ -127,8 +127,11 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
         const int64_t kv_len64 = n_pages == 0 ? 0 : int64_t(n_pages - 1) * kPageSize + kv_last_page_len[b];
         if (kv_len64 > INT32_MAX / 2) return fail(err, E_ARG, "sequence %ld too long", b);
         const int32_t kv_len = int32_t(kv_len64);
-        if (q_len > kv_len)
-            return fail(err, E_QLEN_GT_KVLEN, "sequence %ld: q_len %ld > kv_len %ld", b, q_len, kv_len);
+        // Causal queries are the last q_len positions (q_len <= kv_len); non-causal ones
+        // see all keys and may outnumber them (a cascade's shared-prefix segment), but
+        // need at least one key.
+        if (p.causal ? q_len > kv_len : (q_len > 0 && kv_len == 0))
+            return fail(err, E_QLEN_GT_KVLEN, "sequence %ld: q_len %ld with kv_len %ld", b, q_len, kv_len);
         if (q_len == 0) continue;
         S.total_q += q_len;
         S.kv_tokens += kv_len;

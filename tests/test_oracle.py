@@ -55,6 +55,9 @@ def small_cases():
                        head_dim=16, dtype="f16", seed=8, spare_pages=1)
     yield W.make_batch("full_attn", [4, 1, 6], [10, 17, 6], num_qo_heads=4, num_kv_heads=1,
                        head_dim=8, dtype="bf16", seed=9, causal=False)
+    # non-causal with more queries than keys (a cascade's shared-prefix segment)
+    yield W.make_batch("full_attn_q_gt_kv", [21, 2, 5], [5, 17, 1], num_qo_heads=4, num_kv_heads=2,
+                       head_dim=16, dtype="f16", seed=10, causal=False, spare_pages=2, poison=True)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -249,6 +252,35 @@ def test_shared_prefix_equals_duplicated_prefix():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_cascade_halves_merge_to_the_whole():
+    # Keys split into a shared prefix (attended non-causally by every request's
+    # queries at once) and each request's private rest (causal): merging the two
+    # results with weights exp(LSE_x - max LSE) gives the attention over all keys,
+    # an exact identity of the softmax (vLLM issue #227's sharing as a cascade).
+    kw = dict(n_req=4, prefix=40, suffix=7, decode_steps=0, num_qo_heads=8, num_kv_heads=2,
+              head_dim=32, dtype="bf16")
+    b = W.shared_prefix_suffix(**kw)
+    shared, private = W.cascade_view(b, prefix=40)
+    assert shared.batch == 1 and shared.q_lens[0] == b.total_q and shared.kv_lens[0] == 40
+    assert (private.kv_lens == 7).all() and private.causal and not shared.causal
+    o, lse = oracle.run(**b.oracle_kwargs())
+    om, lm = oracle.merge_states(*oracle.run(**shared.oracle_kwargs()), *oracle.run(**private.oracle_kwargs()))
+    assert np.abs(om - o).max() < 1e-12 and np.abs(lm - lse).max() < 1e-12
+    # merging is symmetric, and merging with an empty state (LSE = -inf) is the identity
+    om2, lm2 = oracle.merge_states(*oracle.run(**private.oracle_kwargs()), *oracle.run(**shared.oracle_kwargs()))
+    assert np.abs(om2 - o).max() < 1e-12 and np.abs(lm2 - lse).max() < 1e-12
+    oe, le = oracle.merge_states(o, lse, np.full_like(o, np.nan), np.full_like(lse, -np.inf))
+    assert np.array_equal(oe, o) and np.array_equal(le, lse)
+    oz, lz = oracle.merge_states(o, np.full_like(lse, -np.inf), o, np.full_like(lse, -np.inf))
+    assert (oz == 0).all() and np.isneginf(lz).all()
+    # decode rows after appending tokens split the same way
+    d = W.decode_step(W.shared_prefix_suffix(**dict(kw, decode_steps=3)), 3)
+    shared, private = W.cascade_view(d, prefix=40)
+    o, lse = oracle.run(**d.oracle_kwargs())
+    om, lm = oracle.merge_states(*oracle.run(**shared.oracle_kwargs()), *oracle.run(**private.oracle_kwargs()))
+    assert np.abs(om - o).max() < 1e-12 and np.abs(lm - lse).max() < 1e-12
+
+
 def test_gqa_equals_expanded_mha():
     b = W.make_batch("gqa", [6, 2], [6, 30], num_qo_heads=6, num_kv_heads=2, head_dim=8, dtype="bf16", seed=15)
     G = 3
@@ -313,6 +345,10 @@ def test_rejects_invalid_page_tables():
     assert "E_LAST_PAGE_LEN" in _bad(b, kv_last_page_len=np.array([1, 0, 5, 16], np.int32))
     assert "E_LAST_PAGE_LEN" in _bad(b, kv_last_page_len=np.array([1, 17, 5, 16], np.int32))
     assert "E_QLEN_GT_KVLEN" in _bad(b, kv_last_page_len=np.array([1, 14, 4, 16], np.int32))
+    # non-causal: more queries than keys is allowed, queries without any key are not
+    nc = W.make_batch("nc", [3, 2], [1, 0], num_qo_heads=2, num_kv_heads=1, head_dim=8, dtype="f16",
+                      seed=4, causal=False)
+    assert "E_QLEN_GT_KVLEN" in _bad(nc)
     bad_idx = b.kv_page_indices.copy()
     bad_idx[3] = b.num_pages
     assert "E_PAGE_OOB" in _bad(b, kv_page_indices=bad_idx)

@@ -152,7 +152,10 @@ def qo_row_in_seq(b, s, r0):
     lengths_batch([8192] * 4 + [1] * 256, [8192] * 4 + list(range(512, 8192, 30))[:256], H=64, Hk=8),
     lengths_batch([3, 9], [40, 9], H=6, Hk=2, D=64, causal=False),
     lengths_batch([5, 1], [5, 1], H=12, Hk=1),  # G = 12 does not divide 128
-], ids=["tiny", "decode", "ragged", "suffix", "decode_mixed", "mixed_long", "noncausal", "g12"])
+    lengths_batch([7680], [200], H=32, Hk=8, causal=False),  # cascade: shared prefix, all queries
+    lengths_batch([256, 1, 40], [200, 3, 0 + 17], H=8, Hk=1, causal=False),
+], ids=["tiny", "decode", "ragged", "suffix", "decode_mixed", "mixed_long", "noncausal", "g12",
+        "cascade_shared", "noncausal_q_gt_kv"])
 @pytest.mark.parametrize("max_kv_splits", [0, 1, 3])
 def test_schedule_properties(case, max_kv_splits):
     plan = make_plan(case, max_kv_splits=max_kv_splits)
@@ -219,6 +222,30 @@ def test_plan_rejects_bad_input(bad, code):
         rpa.Plan(kw.pop("qo_indptr"), kw.pop("kv_page_indptr"), kw.pop("kv_last_page_len"), **kw)
     assert e.value.status == code
     assert len(str(e.value)) > len(code) + 5
+
+
+def test_noncausal_may_have_more_queries_than_keys():
+    # non-causal: q_len > kv_len is a valid request (every query sees all keys) ...
+    info = make_plan(lengths_batch([40, 3], [5, 2], causal=False)).info
+    assert info["visible_pairs"] == (40 * 5 + 3 * 2) * 8
+    # ... but a causal one is not, and neither are queries with no key at all
+    with pytest.raises(rpa.RPAError) as e:
+        make_plan(lengths_batch([40, 3], [5, 2], causal=True))
+    assert e.value.status == "RPA_E_QLEN_GT_KVLEN"
+    with pytest.raises(rpa.RPAError) as e:
+        make_plan(lengths_batch([2, 3], [0, 2], causal=False))
+    assert e.value.status == "RPA_E_QLEN_GT_KVLEN"
+
+
+def test_merge_states_rejects_bad_arguments_without_launching():
+    lib = rpa.load()
+    P = 256  # a 16-byte aligned stand-in address; these calls fail validation before any launch
+    assert lib.rpa_merge_states(0, 8, 128, 1, None, None, None, None, None, None, None) == 0  # nothing to do
+    assert rpa.STATUS[lib.rpa_merge_states(4, 8, 96, 1, P, P, P, P, P, P, None)] == "RPA_E_SHAPE"
+    assert rpa.STATUS[lib.rpa_merge_states(4, 8, 128, 5, P, P, P, P, P, P, None)] == "RPA_E_ARG"
+    assert rpa.STATUS[lib.rpa_merge_states(4, 8, 128, 1, None, P, P, P, P, P, None)] == "RPA_E_ARG"
+    assert rpa.STATUS[lib.rpa_merge_states(4, 8, 128, 1, P + 2, P, P, P, P, P, None)] == "RPA_E_ARG"
+    assert rpa.STATUS[lib.rpa_merge_states(-1, 8, 128, 1, P, P, P, P, P, P, None)] == "RPA_E_ARG"
 
 
 def test_validate_page_table():

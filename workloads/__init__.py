@@ -316,6 +316,65 @@ def decode_step(base: Batch, step: int, seed: int = 5004) -> Batch:
     return b
 
 
+def cascade_view(b: Batch, prefix: int, poison: bool = True):
+    """The same token values in the layout of a two-level cascade: one copy of the
+    `prefix` tokens every sequence shares, in pages of their own (the last one
+    partly filled), plus each sequence's remaining tokens in private pages (vLLM
+    issue #227: many requests over one system prompt).  Returns (shared, private):
+      shared  -- one non-causal sequence holding every query row of b (q_len =
+                 b.total_q) over the prefix (kv_len = prefix);
+      private -- b's sequences and queries over their own tokens past the prefix
+                 (kv_len - prefix each), with b's causal flag.
+    Both index one new pool; unused slots are NaN when `poison`.  Every query must
+    sit at or after the prefix, so that it sees all of it.  Layout only: token
+    values are copied, never combined."""
+    ps = b.page_size
+    kvl, ql = b.kv_lens, b.q_lens
+    assert b.batch > 0 and (kvl >= prefix).all() and (kvl - ql >= prefix).all()
+
+    def tokens(seq):  # [kv_len, 2, Hkv, D] through the page table
+        L = int(kvl[seq])
+        pg = b.kv_page_indices[b.kv_page_indptr[seq]:b.kv_page_indptr[seq + 1]]
+        t = np.arange(L)
+        idx = torch.from_numpy(pg[t // ps].astype(np.int64)).to(b.kv_cache.device)
+        sl = torch.from_numpy((t % ps).astype(np.int64)).to(b.kv_cache.device)
+        return b.kv_cache[idx, :, sl]
+
+    pre = tokens(0)[:prefix]
+    n_sh = pages_for(prefix)
+    priv_len = [int(kvl[s]) - prefix for s in range(b.batch)]
+    n_pr = [pages_for(L) for L in priv_len]
+    pool = n_sh + sum(n_pr)
+    kv = torch.empty((pool, 2, ps, b.num_kv_heads, b.head_dim), dtype=b.kv_cache.dtype, device=b.kv_cache.device)
+    kv.fill_(float("nan") if poison else 0.0)
+
+    def put(first_page, vals):  # vals [L, 2, Hkv, D] into consecutive pages from first_page
+        L = vals.shape[0]
+        t = np.arange(L)
+        idx = torch.from_numpy(first_page + t // ps).to(kv.device)
+        sl = torch.from_numpy(t % ps).to(kv.device)
+        kv[idx, :, sl] = vals
+
+    put(0, pre)
+    priv_idx, nxt = [], n_sh
+    for s in range(b.batch):
+        full = tokens(s)
+        assert torch.equal(full[:prefix].view(torch.int16), pre.view(torch.int16)), "prefix differs at %d" % s
+        put(nxt, full[prefix:])
+        priv_idx.append(np.arange(nxt, nxt + n_pr[s], dtype=np.int32))
+        nxt += n_pr[s]
+    shared = Batch(b.name + "_cascade_shared", np.array([0, b.total_q], np.int32),
+                   np.array([0, n_sh], np.int32), np.arange(n_sh, dtype=np.int32),
+                   np.array([last_page_len_for(prefix)], np.int32), b.q, kv,
+                   b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype, False, ps)
+    private = Batch(b.name + "_cascade_private", b.qo_indptr.copy(),
+                    np.concatenate([[0], np.cumsum(n_pr)]).astype(np.int32),
+                    np.concatenate(priv_idx).astype(np.int32) if priv_idx else np.zeros(0, np.int32),
+                    np.array([last_page_len_for(L) if L else 1 for L in priv_len], np.int32), b.q, kv,
+                    b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype, b.causal, ps)
+    return shared, private
+
+
 def mixed_long_lengths(n_prompts: int = 4, prompt_len: int = 8192, n_decode: int = 256,
                        lo: int = 512, hi: int = 8192, seed: int = 1005):
     gen = torch.Generator("cpu").manual_seed(seed)

@@ -161,6 +161,32 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
                    void* stream);
 
 /*
+ * Re-plan in place for new lengths of the same batch (a decode step: every
+ * sequence one token longer), keeping the launch shape: the new schedule must
+ * have the same number of tiles, wide tiles and split groups, and no more partial
+ * rows; otherwise RPA_E_UNSUPPORTED (create and bind a new plan).  Host-only: the
+ * new schedule is written into the plan's pinned staging image (if bound) and
+ * reaches the device with the next rpa_plan_upload.  This is what lets a captured
+ * HIP graph [rpa_plan_upload, rpa_append_kv, rpa_run] be replayed step after step
+ * (flashinfer issue #323: auxiliary data built by begin_forward, reused by
+ * forward).  The caller makes sure the previous upload has completed (e.g. by
+ * synchronising its stream) before calling this, since it rewrites the staging
+ * image that upload reads.
+ * Errors: those of rpa_plan_create, E_UNSUPPORTED.
+ */
+rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int32_t* kv_page_indptr_h,
+                           const int32_t* kv_last_page_len_h);
+
+/*
+ * Enqueue on `stream` the copy of the plan's current schedule into its workspace
+ * (the same copy rpa_plan_bind makes; it also clears the error flag and the split
+ * counters).  One hipMemcpyAsync from pinned host memory, so it can be captured
+ * into a HIP graph.
+ * Errors: E_ARG (unbound plan), E_HIP.
+ */
+rpa_status rpa_plan_upload(const rpa_plan* plan, void* stream);
+
+/*
  * Error flag of a bound plan: synchronises `stream`, then reports whether any
  * run since the last bind met a page index outside [0, num_pages)
  * (*flag_out = 1, and RPA_E_PAGE_OOB is returned) or not (*flag_out = 0).
@@ -178,6 +204,49 @@ void rpa_plan_destroy(rpa_plan* plan);
  */
 rpa_status rpa_validate_page_table(int32_t batch, const int32_t* kv_page_indptr_h,
                                    const int32_t* kv_page_indices_h, int64_t num_pages);
+
+/*
+ * Append new tokens' K and V into their page slots (the page-table addressing of
+ * flashinfer issue #323's repro: token t of sequence b is in page
+ * kv_page_indices[kv_page_indptr[b] + t / 16], slot t % 16).  The page table
+ * describes the sequences AFTER the append; the new tokens of sequence b are its
+ * last append_indptr[b+1] - append_indptr[b] tokens, like queries and qo_indptr.
+ *   append_indptr_d     device int32 [batch+1], [0] == 0, [batch] == n_new
+ *   kv_page_indptr_d    device int32 [batch+1]
+ *   kv_page_indices_d   device int32 [kv_page_indptr[batch]]
+ *   kv_last_page_len_d  device int32 [batch]
+ *   new_kv_d            device [n_new][2][num_kv_heads][head_dim] (K then V), the
+ *                       cache's dtype, 16-byte aligned
+ *   kv_cache_d          device [num_pages][2][16][num_kv_heads][head_dim], written
+ *   err_flag_d          device int32, set to 1 if a token has no valid slot (its
+ *                       position or page is out of range; it is not written); or NULL
+ * The device arrays are read by the kernel, not checked on the host.  Enqueues one
+ * kernel on `stream`; no allocation, no synchronisation (graph-capturable).
+ * Errors: E_ARG, E_SHAPE, E_HIP.
+ */
+rpa_status rpa_append_kv(int32_t batch, int64_t n_new, int32_t num_kv_heads, int32_t head_dim,
+                         const int32_t* append_indptr_d, const int32_t* kv_page_indptr_d,
+                         const int32_t* kv_page_indices_d, const int32_t* kv_last_page_len_d, const void* new_kv_d,
+                         void* kv_cache_d, int64_t num_pages, int32_t* err_flag_d, void* stream);
+
+/*
+ * Trim sequences to shorter lengths (drop padding KV after a padded prefill;
+ * llama.cpp discussion #15958, "Pad for prefill stage?"): a page-table edit, no
+ * data moves.  Sequence b keeps its first new_kv_len[b] <= kv_len tokens, i.e. its
+ * first ceil(new_kv_len[b] / 16) pages, in order; the dropped pages go back to the
+ * caller's allocator and later appends overwrite the kept page's tail slots.
+ * Host arrays only:
+ *   in:  kv_page_indptr_h [batch+1], kv_page_indices_h, kv_last_page_len_h [batch],
+ *        new_kv_len_h [batch]
+ *   out: out_kv_page_indptr_h [batch+1], out_kv_page_indices_h (room for
+ *        kv_page_indptr_h[batch] entries), out_kv_last_page_len_h [batch] (0 for an
+ *        emptied sequence)
+ * Errors: E_ARG (NULL array, new length outside [0, kv_len]), E_INDPTR, E_LAST_PAGE_LEN.
+ */
+rpa_status rpa_trim_page_table(int32_t batch, const int32_t* kv_page_indptr_h, const int32_t* kv_page_indices_h,
+                               const int32_t* kv_last_page_len_h, const int32_t* new_kv_len_h,
+                               int32_t* out_kv_page_indptr_h, int32_t* out_kv_page_indices_h,
+                               int32_t* out_kv_last_page_len_h);
 
 /*
  * Merge two attention states of the same query rows computed over disjoint key

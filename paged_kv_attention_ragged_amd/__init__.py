@@ -82,6 +82,10 @@ def load():
             "rpa_prof_start": (st, []),
             "rpa_prof_stop": (st, [P, P]),
             "rpa_merge_states": (st, [i64, i32, i32, i32, P, P, P, P, P, P, P]),
+            "rpa_plan_update": (st, [P, P, P, P]),
+            "rpa_plan_upload": (st, [P, P]),
+            "rpa_append_kv": (st, [i32, i64, i32, i32, P, P, P, P, P, P, i64, P, P]),
+            "rpa_trim_page_table": (st, [i32, P, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -217,6 +221,23 @@ class Plan:
                               lse.data_ptr() if lse is not None else None, stream.cuda_stream))
         return (out, lse) if return_lse else out
 
+    def update(self, qo_indptr, kv_page_indptr, kv_last_page_len):
+        """Re-plan in place for new lengths with the same launch shape (raises
+        RPAError RPA_E_UNSUPPORTED otherwise); the device copy changes at upload()."""
+        qo, kp, kl = _host_i32(qo_indptr), _host_i32(kv_page_indptr), _host_i32(kv_last_page_len)
+        if len(qo) != self.batch + 1 or len(kp) != self.batch + 1 or len(kl) != self.batch:
+            raise ValueError("update needs the plan's batch size (%d)" % self.batch)
+        p = lambda a: a.ctypes.data if a.size else None
+        _check(load().rpa_plan_update(self._h, p(qo), p(kp), p(kl)))
+        self._qo, self._kp, self._kl = qo, kp, kl
+
+    def upload(self, stream=None):
+        """Enqueue the copy of the current schedule into the workspace (graph-capturable)."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream()
+        _check(load().rpa_plan_upload(self._h, stream.cuda_stream))
+
     def check(self, stream=None) -> bool:
         """Synchronise and report whether a run met an out-of-range page index (raises)."""
         import torch
@@ -236,6 +257,44 @@ class Plan:
             self.close()
         except Exception:
             pass
+
+
+def append_kv(new_kv, kv_cache, append_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len,
+              err_flag=None, stream=None):
+    """Write new tokens' K/V (new_kv [n_new, 2, H_kv, D], the cache's dtype) into
+    kv_cache [num_pages, 2, 16, H_kv, D] at the slots the page table (lengths after
+    the append; int32 CUDA tensors) gives the last append_indptr[b+1] - append_indptr[b]
+    tokens of each sequence.  err_flag: optional int32 CUDA tensor set to 1 for a
+    token with no valid slot."""
+    import torch
+    n_new = new_kv.shape[0]
+    Hk, D = kv_cache.shape[3], kv_cache.shape[4]
+    if (new_kv.dim() != 4 or tuple(new_kv.shape[1:]) != (2, Hk, D) or new_kv.dtype != kv_cache.dtype
+            or not new_kv.is_contiguous() or not kv_cache.is_contiguous()):
+        raise ValueError("new_kv must be a contiguous [n_new, 2, H_kv, D] tensor of the cache's dtype")
+    for t in (append_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len):
+        if not (t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()):
+            raise ValueError("page-table arrays must be contiguous int32 CUDA tensors")
+    if stream is None:
+        stream = torch.cuda.current_stream(kv_cache.device)
+    _check(load().rpa_append_kv(append_indptr.numel() - 1, n_new, Hk, D, append_indptr.data_ptr(),
+                                kv_page_indptr.data_ptr(), kv_page_indices.data_ptr() if kv_page_indices.numel() else None,
+                                kv_last_page_len.data_ptr(), new_kv.data_ptr(), kv_cache.data_ptr(), kv_cache.shape[0],
+                                err_flag.data_ptr() if err_flag is not None else None, stream.cuda_stream))
+
+
+def trim_page_table(kv_page_indptr, kv_page_indices, kv_last_page_len, new_kv_len):
+    """Host page-table edit keeping each sequence's first new_kv_len[b] tokens:
+    returns (kv_page_indptr, kv_page_indices, kv_last_page_len) as int32 numpy arrays."""
+    ip, ix, kl, nl = (_host_i32(a) for a in (kv_page_indptr, kv_page_indices, kv_last_page_len, new_kv_len))
+    batch = len(ip) - 1
+    o_ip = np.zeros(batch + 1, np.int32)
+    o_ix = np.zeros(max(len(ix), 1), np.int32)
+    o_kl = np.zeros(max(batch, 1), np.int32)
+    p = lambda a: a.ctypes.data if a.size else None
+    _check(load().rpa_trim_page_table(batch, p(ip), p(ix), p(kl), p(nl), o_ip.ctypes.data, o_ix.ctypes.data,
+                                      o_kl.ctypes.data))
+    return o_ip, o_ix[:o_ip[-1]].copy(), o_kl[:batch].copy()
 
 
 def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):

@@ -177,6 +177,46 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
     return RPA_OK;
 }
 
+rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int32_t* kv_page_indptr_h,
+                           const int32_t* kv_last_page_len_h) {
+    if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
+    const rpa_params& P = plan->params;
+    rpa::PlanParams pp{P.num_qo_heads, P.num_kv_heads, P.head_dim, P.page_size, P.causal, P.max_kv_splits,
+                       P.num_cus};
+    rpa::Schedule S;
+    std::string err;
+    int rc = 0;
+    try {
+        rc = rpa::build_schedule(pp, plan->batch, qo_indptr_h, kv_page_indptr_h, kv_last_page_len_h, &S, &err);
+    } catch (const std::bad_alloc&) {
+        return set_err(RPA_E_ARG, "out of host memory while planning");
+    }
+    if (rc != 0) return set_err(rpa_status(rc), err);
+    const auto& O = plan->sched;
+    if (S.tiles.size() != O.tiles.size() || S.wide_tiles != O.wide_tiles || S.merges.size() != O.merges.size() ||
+        S.partial_rows > O.partial_rows)
+        return set_err(RPA_E_UNSUPPORTED,
+                       "the new lengths need another launch shape (" + std::to_string(S.tiles.size()) + " tiles, " +
+                           std::to_string(S.merges.size()) + " split groups instead of " +
+                           std::to_string(O.tiles.size()) + ", " + std::to_string(O.merges.size()) +
+                           "): create and bind a new plan");
+    S.partial_rows = O.partial_rows;  // the workspace layout stays as bound
+    plan->sched = std::move(S);
+    if (plan->staging && !plan->sched.tiles.empty())
+        std::memcpy(static_cast<char*>(plan->staging) + plan->off_tiles, plan->sched.tiles.data(),
+                    plan->sched.tiles.size() * sizeof(rpa::Tile));
+    return RPA_OK;
+}
+
+rpa_status rpa_plan_upload(const rpa_plan* plan, void* stream) {
+    if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
+    if (!plan->bound) return set_err(RPA_E_ARG, "plan is not bound to a workspace (rpa_plan_bind)");
+    hipError_t e = hipMemcpyAsync(plan->ws, plan->staging, plan->staging_bytes, hipMemcpyHostToDevice,
+                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(schedule upload)");
+    return RPA_OK;
+}
+
 rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, void* o, float* lse, void* stream) {
     if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
     if (!plan->bound) return set_err(RPA_E_ARG, "plan is not bound to a workspace (rpa_plan_bind)");
@@ -274,6 +314,75 @@ rpa_status rpa_validate_page_table(int32_t batch, const int32_t* kv_page_indptr_
             return set_err(RPA_E_PAGE_OOB, "kv_page_indices[" + std::to_string(i) + "] = " +
                                                std::to_string(kv_page_indices_h[i]) + " outside [0, " +
                                                std::to_string(num_pages) + ")");
+    return RPA_OK;
+}
+
+rpa_status rpa_append_kv(int32_t batch, int64_t n_new, int32_t num_kv_heads, int32_t head_dim,
+                         const int32_t* append_indptr_d, const int32_t* kv_page_indptr_d,
+                         const int32_t* kv_page_indices_d, const int32_t* kv_last_page_len_d, const void* new_kv_d,
+                         void* kv_cache_d, int64_t num_pages, int32_t* err_flag_d, void* stream) {
+    if (batch < 0 || n_new < 0) return set_err(RPA_E_ARG, "batch and n_new must be >= 0");
+    if (num_kv_heads < 1) return set_err(RPA_E_SHAPE, "num_kv_heads must be >= 1");
+    if (head_dim != 64 && head_dim != 128)
+        return set_err(RPA_E_SHAPE, "head_dim " + std::to_string(head_dim) + " not supported (64 or 128)");
+    if (num_pages < 0 || num_pages > INT32_MAX) return set_err(RPA_E_ARG, "num_pages outside [0, 2^31)");
+    if (n_new == 0) return RPA_OK;
+    if (batch == 0) return set_err(RPA_E_ARG, "new tokens need at least one sequence");
+    if (n_new > INT32_MAX) return set_err(RPA_E_ARG, "too many new tokens");
+    if (!append_indptr_d || !kv_page_indptr_d || !kv_page_indices_d || !kv_last_page_len_d || !new_kv_d ||
+        !kv_cache_d)
+        return set_err(RPA_E_ARG, "device arrays must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(new_kv_d) | reinterpret_cast<uintptr_t>(kv_cache_d)) & 15)
+        return set_err(RPA_E_ARG, "new_kv and kv_cache must be 16-byte aligned");
+    rpa::AppendArgs A{};
+    A.append_indptr = append_indptr_d;
+    A.kv_page_indptr = kv_page_indptr_d;
+    A.kv_page_indices = kv_page_indices_d;
+    A.kv_last_page_len = kv_last_page_len_d;
+    A.new_kv = static_cast<const uint16_t*>(new_kv_d);
+    A.kv = static_cast<uint16_t*>(kv_cache_d);
+    A.n_new = n_new;
+    A.batch = batch;
+    A.Hkv = num_kv_heads;
+    A.D = head_dim;
+    A.num_pages = int32_t(num_pages);
+    A.err_flag = err_flag_d;
+    const hipError_t e = rpa::launch_append(A, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_err(e, "append kernel launch");
+    return RPA_OK;
+}
+
+rpa_status rpa_trim_page_table(int32_t batch, const int32_t* kv_page_indptr_h, const int32_t* kv_page_indices_h,
+                               const int32_t* kv_last_page_len_h, const int32_t* new_kv_len_h,
+                               int32_t* out_kv_page_indptr_h, int32_t* out_kv_page_indices_h,
+                               int32_t* out_kv_last_page_len_h) {
+    if (batch < 0) return set_err(RPA_E_ARG, "batch must be >= 0");
+    if (batch > 0 && (!kv_page_indptr_h || !kv_last_page_len_h || !new_kv_len_h || !out_kv_page_indptr_h ||
+                      !out_kv_last_page_len_h))
+        return set_err(RPA_E_ARG, "host arrays must be non-NULL");
+    if (out_kv_page_indptr_h && batch >= 0) out_kv_page_indptr_h[0] = 0;
+    if (batch == 0) return RPA_OK;
+    if (kv_page_indptr_h[0] != 0) return set_err(RPA_E_INDPTR, "kv_page_indptr[0] must be 0");
+    if (kv_page_indptr_h[batch] > 0 && (!kv_page_indices_h || !out_kv_page_indices_h))
+        return set_err(RPA_E_ARG, "kv_page_indices and out_kv_page_indices must be non-NULL");
+    const int P = rpa::kPageSize;
+    int32_t w = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        const int32_t np = kv_page_indptr_h[b + 1] - kv_page_indptr_h[b];
+        if (np < 0) return set_err(RPA_E_INDPTR, "kv_page_indptr decreases at " + std::to_string(b));
+        if (np > 0 && (kv_last_page_len_h[b] < 1 || kv_last_page_len_h[b] > P))
+            return set_err(RPA_E_LAST_PAGE_LEN, "kv_last_page_len[" + std::to_string(b) + "] outside [1, 16]");
+        const int64_t kv_len = np == 0 ? 0 : int64_t(np - 1) * P + kv_last_page_len_h[b];
+        const int32_t nl = new_kv_len_h[b];
+        if (nl < 0 || nl > kv_len)
+            return set_err(RPA_E_ARG, "new_kv_len[" + std::to_string(b) + "] = " + std::to_string(nl) +
+                                          " outside [0, " + std::to_string(kv_len) + "]");
+        const int32_t keep = (nl + P - 1) / P;
+        for (int32_t i = 0; i < keep; ++i) out_kv_page_indices_h[w + i] = kv_page_indices_h[kv_page_indptr_h[b] + i];
+        w += keep;
+        out_kv_page_indptr_h[b + 1] = w;
+        out_kv_last_page_len_h[b] = nl == 0 ? 0 : (nl - 1) % P + 1;
+    }
     return RPA_OK;
 }
 

@@ -837,6 +837,46 @@ __global__ __launch_bounds__(256) void merge_states_kernel(MergeArgs M) {
     if (M.lse && c == 0) M.lse[rh] = sum > 0.f ? mu + __logf(sum) : -INFINITY;
 }
 
+// Append: write new tokens' K and V into the cache slots the page table gives them
+// (the page-table addressing of flashinfer issue #323's repro: token t of a
+// sequence is in page kv_page_indices[kv_page_indptr[b] + t / 16], slot t % 16).
+// The new tokens of sequence b are its last append_indptr[b+1] - append_indptr[b]
+// tokens under the given (already grown) lengths, the same convention as queries
+// and qo_indptr.  One workgroup per new token; its sequence is found by binary
+// search over append_indptr.  A token whose position or page is out of range is
+// not written and raises err_flag.
+__global__ __launch_bounds__(256) void append_kv_kernel(AppendArgs A) {
+    const int64_t tok = blockIdx.x;
+    if (tok >= A.n_new) return;
+    int lo = 0, hi = A.batch - 1;  // last b with append_indptr[b] <= tok
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (A.append_indptr[mid] <= tok) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int64_t a0 = A.append_indptr[b], a1 = A.append_indptr[b + 1];
+    const int np = A.kv_page_indptr[b + 1] - A.kv_page_indptr[b];
+    const int last = A.kv_last_page_len[b];
+    const bool len_ok = np > 0 && last >= 1 && last <= kPageSize && tok >= a0 && tok < a1;
+    const int64_t kv_len = int64_t(np - 1) * kPageSize + last;
+    const int64_t pos = kv_len - (a1 - a0) + (tok - a0);
+    int page = -1;
+    if (len_ok && pos >= 0 && pos < kv_len) page = A.kv_page_indices[A.kv_page_indptr[b] + pos / kPageSize];
+    if ((unsigned)page >= (unsigned)A.num_pages) {
+        if (threadIdx.x == 0 && A.err_flag) *A.err_flag = 1;
+        return;
+    }
+    const int slot = int(pos % kPageSize);
+    const int64_t row = int64_t(A.Hkv) * A.D;  // elements of one K (or V) row
+    const int chunks = int(row / 8);           // 16-byte chunks per row
+    const uint16_t* src = A.new_kv + tok * 2 * row;
+    for (int c = threadIdx.x; c < 2 * chunks; c += 256) {
+        const int kvsel = c / chunks, cc = c - kvsel * chunks;
+        uint16_t* dst = A.kv + ((int64_t(page) * 2 + kvsel) * kPageSize + slot) * row + 8 * cc;
+        *(u32x4*)dst = *(const u32x4*)(src + kvsel * row + 8 * cc);
+    }
+}
+
 template <typename K>
 hipError_t launch_with_lds(K kernel, const LaunchAttn& L, int lds, hipStream_t stream, hipEvent_t ev0,
                            hipEvent_t ev1) {
@@ -868,6 +908,12 @@ hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0
                       : launch_with_lds(&attn_narrow_kernel<128, false>, L, NarrowLds<128>::bytes, stream, ev0, ev1);
     return L.bf16 ? launch_with_lds(&attn_narrow_kernel<64, true>, L, NarrowLds<64>::bytes, stream, ev0, ev1)
                   : launch_with_lds(&attn_narrow_kernel<64, false>, L, NarrowLds<64>::bytes, stream, ev0, ev1);
+}
+
+hipError_t launch_append(const AppendArgs& A, hipStream_t stream) {
+    if (A.n_new <= 0) return hipSuccess;
+    hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)A.n_new), dim3(256), 0, stream, A);
+    return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& M, bool bf16, hipStream_t stream) {

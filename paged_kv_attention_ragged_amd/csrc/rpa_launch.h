@@ -44,9 +44,23 @@ struct MergeArgs {
     int32_t head_dim;
 };
 
+// Append of new tokens' K and V into their page slots.
+struct AppendArgs {
+    const int32_t* append_indptr;     // [batch + 1]: new tokens of sequence b are rows [b], [b+1) of new_kv
+    const int32_t* kv_page_indptr;    // [batch + 1], lengths after the append
+    const int32_t* kv_page_indices;
+    const int32_t* kv_last_page_len;  // [batch]
+    const uint16_t* new_kv;           // [n_new][2][Hkv][D]
+    uint16_t* kv;                     // [num_pages][2][16][Hkv][D]
+    int64_t n_new;
+    int32_t batch, Hkv, D, num_pages;
+    int32_t* err_flag;                // set to 1 for a token with no valid slot; may be NULL
+};
+
 // ev0 / ev1: optional events stamped at the start and end of the dispatch (NULL: none).
 hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_merge(const MergeArgs& M, bool bf16, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& A, hipStream_t stream);
 
 }  // namespace rpa

@@ -6,6 +6,7 @@ import ctypes
 import math
 
 import numpy as np
+import torch
 import pytest
 
 import paged_kv_attention_ragged_amd as rpa
@@ -246,6 +247,64 @@ def test_merge_states_rejects_bad_arguments_without_launching():
     assert rpa.STATUS[lib.rpa_merge_states(4, 8, 128, 1, None, P, P, P, P, P, None)] == "RPA_E_ARG"
     assert rpa.STATUS[lib.rpa_merge_states(4, 8, 128, 1, P + 2, P, P, P, P, P, None)] == "RPA_E_ARG"
     assert rpa.STATUS[lib.rpa_merge_states(-1, 8, 128, 1, P, P, P, P, P, P, None)] == "RPA_E_ARG"
+
+
+def test_plan_update_keeps_the_launch_shape():
+    # a decode step: every sequence one token longer, same tiles (no split change)
+    b0 = lengths_batch([1] * 256, [231] * 256, H=32, Hk=8)
+    b1 = lengths_batch([1] * 256, [232] * 256, H=32, Hk=8)
+    p = make_plan(b0)
+    n0 = p.info["num_tiles"]
+    p.update(b1.qo_indptr, b1.kv_page_indptr, b1.kv_last_page_len)
+    fresh = make_plan(b1)
+    assert p.info["num_tiles"] == n0 and p.info["visible_pairs"] == fresh.info["visible_pairs"]
+    assert np.array_equal(p.tiles(), fresh.tiles())
+    check_schedule(b1, p)
+    # lengths that need another launch shape are refused; the plan is left as it was
+    b2 = lengths_batch([1] * 128, [1024] * 128)
+    b3 = lengths_batch([1] * 128, [1100] * 128)  # 5 split pieces per sequence instead of 4
+    p2 = make_plan(b2)
+    before = p2.tiles().copy()
+    with pytest.raises(rpa.RPAError) as e:
+        p2.update(b3.qo_indptr, b3.kv_page_indptr, b3.kv_last_page_len)
+    assert e.value.status == "RPA_E_UNSUPPORTED"
+    assert np.array_equal(p2.tiles(), before)
+
+
+def test_trim_page_table_keeps_the_real_tokens_of_a_padded_prefill():
+    # llama.cpp discussion #15958: prompts padded to 200, real tokens first; trimming
+    # each sequence back to its real length leaves exactly the ragged batch's tokens
+    rag = W.short_prompt_prefill(n=8)
+    pad = W.short_prompt_prefill(n=8, padded=True)
+    ip, ix, kl = rpa.trim_page_table(pad.kv_page_indptr, pad.kv_page_indices, pad.kv_last_page_len, rag.kv_lens)
+    t = W.Batch("trimmed", np.zeros(rag.batch + 1, np.int32), ip, ix, kl, None, pad.kv_cache,
+                pad.num_qo_heads, pad.num_kv_heads, pad.head_dim, pad.dtype)
+    assert np.array_equal(t.kv_lens, rag.kv_lens)
+    assert np.array_equal(np.diff(ip), [-(-int(L) // 16) for L in rag.kv_lens])
+    for s in range(rag.batch):
+        k1, v1 = W.contiguous_kv(t, s)
+        k2, v2 = W.contiguous_kv(rag, s)
+        assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+        assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+        # the kept pages are the padded sequence's first pages, in order
+        assert np.array_equal(ix[ip[s]:ip[s + 1]], pad.kv_page_indices[pad.kv_page_indptr[s]:][:ip[s + 1] - ip[s]])
+    with pytest.raises(rpa.RPAError) as e:
+        rpa.trim_page_table(pad.kv_page_indptr, pad.kv_page_indices, pad.kv_last_page_len, pad.kv_lens + 1)
+    assert e.value.status == "RPA_E_ARG"
+    ip0, ix0, kl0 = rpa.trim_page_table(pad.kv_page_indptr, pad.kv_page_indices, pad.kv_last_page_len,
+                                        np.zeros(pad.batch, np.int32))
+    assert (ip0 == 0).all() and len(ix0) == 0
+
+
+def test_append_kv_rejects_bad_arguments_without_launching():
+    lib = rpa.load()
+    P = 256  # aligned stand-in address; these calls fail validation before any launch
+    assert lib.rpa_append_kv(4, 0, 8, 128, None, None, None, None, None, None, 10, None, None) == 0
+    assert rpa.STATUS[lib.rpa_append_kv(0, 3, 8, 128, P, P, P, P, P, P, 10, None, None)] == "RPA_E_ARG"
+    assert rpa.STATUS[lib.rpa_append_kv(4, 3, 8, 96, P, P, P, P, P, P, 10, None, None)] == "RPA_E_SHAPE"
+    assert rpa.STATUS[lib.rpa_append_kv(4, 3, 8, 128, P, None, P, P, P, P, 10, None, None)] == "RPA_E_ARG"
+    assert rpa.STATUS[lib.rpa_append_kv(4, 3, 8, 128, P, P, P, P, P + 4, P, 10, None, None)] == "RPA_E_ARG"
+    assert rpa.STATUS[lib.rpa_plan_upload(None, None)] == "RPA_E_ARG"
 
 
 def test_validate_page_table():

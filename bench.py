@@ -19,12 +19,17 @@ cpu_baseline = the fp64 oracle on a bounded sample of the same batch.
 prefill = a secondary measurement on the long-prompt part of the mixed
 workload (4 causal prompts x 8192, 64 qo / 8 kv heads, bf16): TFLOP/s and
 fraction of the 2.5 PFLOP/s dense bf16/fp16 MFMA peak.
+secondary = the pages' other workloads (ragged vs padded short prompts, the
+shared-prefix suffix prefill and decode step directly and as a cascade, the
+mixed long batch's decode rows and the whole batch).
 """
 import argparse
 import json
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -230,6 +235,239 @@ def bench_prefill(args):
             "dtype": b.dtype, "tiles": info["num_tiles"]}
 
 
+def time_fn(fn, steps, warmup):
+    """Mean ms per call of fn() (GPU work on the current stream), by events around `steps` calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bound_plan(b):
+    import torch
+    import paged_kv_attention_ragged_amd as rpa
+    p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
+                 num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal)
+    p.bind(torch.from_numpy(b.kv_page_indices).cuda(), num_pages=b.kv_cache.shape[0])
+    return p
+
+
+def bench_secondary(args):
+    """The other workloads of the pages, one line each: ragged vs padded short
+    prompts, the shared-prefix suffix prefill and a decode step (direct and as a
+    cascade), and the mixed long batch's parts."""
+    import torch
+    import paged_kv_attention_ragged_amd as rpa
+    import workloads as W
+    steps = max(5, args.steps // 10)
+    out = {}
+
+    def direct(b, rotate=1):
+        p = bound_plan(b)
+        q, kv0 = b.q.cuda(), b.kv_cache.cuda()
+        kvs = [kv0] + [kv0.clone() for _ in range(rotate - 1)]
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+        it = iter(range(1 << 30))
+        ms = time_fn(lambda: p.run(q, kvs[next(it) % rotate], out=o, lse=lse, return_lse=True), steps, 3)
+        info = p.info
+        p.close()
+        return ms, info
+
+    def cascade(b, prefix):
+        sh, pr = W.cascade_view(b, prefix=prefix, poison=False)
+        pa, pb = bound_plan(sh), bound_plan(pr)
+        q, kv = b.q.cuda(), sh.kv_cache.cuda()
+        oa, ob = torch.empty_like(q), torch.empty_like(q)
+        la = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+        lb = torch.empty_like(la)
+
+        def step():
+            pa.run(q, kv, out=oa, lse=la, return_lse=True)
+            pb.run(q, kv, out=ob, lse=lb, return_lse=True)
+            rpa.merge_states(oa, la, ob, lb, out=oa, lse_out=la)
+        ms = time_fn(step, steps, 3)
+        pa.close()
+        pb.close()
+        return ms
+
+    # short ragged prompts (lengths U{1..200}) vs the same prompts padded to 200
+    log("short prompts: ragged vs padded")
+    sp = W.short_prompt_prefill()
+    spp = W.short_prompt_prefill(padded=True)
+    ms_r, inf_r = direct(sp)
+    ms_p, inf_p = direct(spp)
+    out["short_prompts"] = {"ragged_ms": ms_r, "padded_ms": ms_p, "time_ratio": ms_r / ms_p,
+                            "flops_ratio": inf_r["visible_pairs"] / inf_p["visible_pairs"],
+                            "ragged_tflops": 4.0 * sp.head_dim * inf_r["visible_pairs"] / ms_r / 1e9}
+    # shared prefix (256 requests x 200 shared + 30 own tokens), then one decode step
+    log("shared prefix: direct vs cascade")
+    b = W.shared_prefix_suffix()
+    pre_direct, inf = direct(b)
+    pre_cascade = cascade(b, 200)
+    d = W.decode_step(b, 1)
+    dec_direct, inf_d = direct(d, rotate=6)
+    dec_cascade = cascade(d, 200)
+    logical = float(inf_d["kv_tokens"]) * d.num_kv_heads * d.head_dim * 4
+    out["shared_prefix"] = {"suffix_prefill_direct_ms": pre_direct, "suffix_prefill_cascade_ms": pre_cascade,
+                            "decode_step_direct_ms": dec_direct, "decode_step_cascade_ms": dec_cascade,
+                            "decode_direct_logical_kv_gbs": logical / dec_direct / 1e6,
+                            "suffix_prefill_tflops_direct": 4.0 * b.head_dim * inf["visible_pairs"] / pre_direct / 1e9}
+    # a long shared prefix (4096 tokens) under the same 256 requests: one decode step
+    log("long shared prefix decode: direct vs cascade")
+    lb = W.decode_step(W.shared_prefix_suffix(prefix=4096, decode_steps=1), 1)
+    ld_direct, inf_l = direct(lb)
+    ld_cascade = cascade(lb, 4096)
+    out["long_prefix_4096"] = {"decode_step_direct_ms": ld_direct, "decode_step_cascade_ms": ld_cascade,
+                               "logical_kv_gb": float(inf_l["kv_tokens"]) * lb.num_kv_heads * lb.head_dim * 4 / 1e9}
+    del lb
+    # the decode loop: eager vs graph-captured steps
+    log("decode loop: eager vs graph")
+    out["decode_loop"] = bench_decode_loop()
+    # mixed long batch: its decode rows alone and the whole batch in one call
+    log("mixed long batch: decode rows, whole batch")
+    for part in ("decode", "all"):
+        mb = W.mixed_long_batch(part=part, device="cuda")
+        ms, info = direct(mb)
+        kvb = float(info["kv_tokens"]) * mb.num_kv_heads * mb.head_dim * 4
+        ent = {"ms": ms, "tflops": 4.0 * mb.head_dim * info["visible_pairs"] / ms / 1e9}
+        if part == "decode":
+            ent["kv_gbs"] = kvb / ms / 1e6
+            ent["hbm_frac"] = ent["kv_gbs"] / HBM_PEAK_GBS
+        out["mixed_long_" + part] = ent
+        del mb
+        torch.cuda.empty_cache()
+    return out
+
+
+def bench_decode_loop(steps=50):
+    """The shared-prefix batch's decode loop (256 requests, one token per step after
+    200 + 30 prompt tokens): per step, append the new token's K/V and attend.
+    Eager: plan + bind + append + run per step.  Graph: the captured [upload,
+    append, run] replayed after an in-place plan update.  Both synchronise every
+    step, as a decode loop must; inputs of all steps are prepared beforehand."""
+    import torch
+    import numpy as np
+    import paged_kv_attention_ragged_amd as rpa
+    import workloads as W
+    base = W.shared_prefix_suffix()
+    n_req, H, Hk, D = base.batch, base.num_qo_heads, base.num_kv_heads, base.head_dim
+    kv0 = base.kv_cache.cuda()
+    ps = base.page_size
+    prepared = []
+    for st in range(1, steps + 1):
+        d = W.decode_step(base, st)
+        rows = []
+        for s in range(n_req):
+            pos = int(d.kv_lens[s]) - 1
+            rows.append(base.kv_cache[d.kv_page_indices[d.kv_page_indptr[s] + pos // ps], :, pos % ps])
+        prepared.append((d, torch.stack(rows).cuda(), d.q.cuda(),
+                         [torch.from_numpy(a.astype(np.int32)).pin_memory()
+                          for a in (d.kv_page_indptr, d.kv_page_indices, d.kv_last_page_len)]))
+    cap = n_req * base.extra["pages_req"]
+    q_buf = torch.empty(n_req, H, D, dtype=kv0.dtype, device="cuda")
+    new_buf = torch.empty(n_req, 2, Hk, D, dtype=kv0.dtype, device="cuda")
+    ip_buf = torch.zeros(n_req + 1, dtype=torch.int32, device="cuda")
+    ix_buf = torch.zeros(cap, dtype=torch.int32, device="cuda")
+    kl_buf = torch.zeros(n_req, dtype=torch.int32, device="cuda")
+    ai_buf = torch.arange(n_req + 1, dtype=torch.int32, device="cuda")
+    o_buf = torch.empty(n_req, H, D, dtype=kv0.dtype, device="cuda")
+    l_buf = torch.empty(n_req, H, dtype=torch.float32, device="cuda")
+
+    def load(i):
+        d, new, q, (ip, ix, kl) = prepared[i]
+        q_buf.copy_(q)
+        new_buf.copy_(new)
+        ip_buf.copy_(ip, non_blocking=True)
+        ix_buf[:ix.numel()].copy_(ix, non_blocking=True)
+        kl_buf.copy_(kl, non_blocking=True)
+        return d
+
+    # eager
+    kv = kv0.clone()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        d = load(i)
+        p = rpa.Plan(d.qo_indptr, d.kv_page_indptr, d.kv_last_page_len, num_qo_heads=H, num_kv_heads=Hk,
+                     head_dim=D, dtype=d.dtype)
+        p.bind(ix_buf, num_pages=kv.shape[0])
+        rpa.append_kv(new_buf, kv, ai_buf, ip_buf, ix_buf, kl_buf)
+        p.run(q_buf, kv, out=o_buf, lse=l_buf, return_lse=True)
+        torch.cuda.synchronize()
+        p.close()
+    eager = (time.perf_counter() - t0) / steps * 1e3
+    # graph
+    kv = kv0.clone()
+    d = load(0)
+    plan = rpa.Plan(d.qo_indptr, d.kv_page_indptr, d.kv_last_page_len, num_qo_heads=H, num_kv_heads=Hk,
+                    head_dim=D, dtype=d.dtype)
+    plan.bind(ix_buf, num_pages=kv.shape[0])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.upload()
+        rpa.append_kv(new_buf, kv, ai_buf, ip_buf, ix_buf, kl_buf)
+        plan.run(q_buf, kv, out=o_buf, lse=l_buf, return_lse=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gpu_ms = 0.0
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if i > 0:
+            d = load(i)
+            plan.update(d.qo_indptr, d.kv_page_indptr, d.kv_last_page_len)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gpu_ms += e0.elapsed_time(e1)
+    graph = (time.perf_counter() - t0) / steps * 1e3
+    plan.close()
+    return {"steps": steps, "eager_step_ms": eager, "graph_step_ms": graph, "graph_replay_gpu_ms": gpu_ms / steps}
+
+
+def bench_sweep(total_tokens=8192, batches=(1, 2, 4, 8, 16, 32, 64, 128, 256), steps=10):
+    """Batch-size sweep at constant total tokens (llama.cpp discussion #15958: batching
+    prompts helps little unless they are very short): B causal prompts of
+    total_tokens / B tokens each (32 qo / 8 kv heads, D 128, bf16), as one ragged
+    call, against the same prompts run one call each.  One JSON line per B."""
+    import torch
+    import workloads as W
+    rows = []
+    for B in batches:
+        L = total_tokens // B
+        b = W.make_batch("sweep_B%d" % B, [L] * B, [L] * B, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                         dtype="bf16", seed=4000 + B, permute=True, device="cuda")
+        q, kv = b.q, b.kv_cache
+        o = torch.empty_like(q)
+        p = bound_plan(b)
+        info = p.info
+        batched = time_fn(lambda: p.run(q, kv, out=o), steps, 2)
+        p.close()
+        one = W.Batch("one", np.array([0, L], np.int32), np.array([0, b.kv_page_indptr[1]], np.int32),
+                      b.kv_page_indices[:b.kv_page_indptr[1]].copy(), b.kv_last_page_len[:1].copy(), q[:L], kv,
+                      b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype)
+        p1 = bound_plan(one)
+        single = time_fn(lambda: p1.run(q[:L], kv, out=o[:L]), steps, 2)
+        p1.close()
+        r = {"sweep": "constant_total_tokens", "total_tokens": total_tokens, "batch": B, "prompt_len": L,
+             "batched_ms": batched, "one_by_one_ms": single * B, "speedup": single * B / batched,
+             "tflops_batched": 4.0 * b.head_dim * info["visible_pairs"] / batched / 1e9}
+        print(json.dumps(r), flush=True)
+        rows.append(r)
+        del b, q, kv, o
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,6 +475,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only the batch-size sweep at constant total tokens (one JSON line per batch size)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -248,6 +489,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import paged_kv_attention_ragged_amd as rpa
     rpa.load()
+    if args.sweep:
+        bench_sweep()
+        return
     if args.calibrate_copy:
         calibrate_copy()
     log("decode_b128_kv1024: %d warmup + %d timed steps" % (args.warmup, args.steps))
@@ -255,6 +499,8 @@ def main():
     if not args.no_prefill:
         log("long prefill 4x8192")
         res["prefill"] = bench_prefill(args)
+    if not args.no_secondary:
+        res["secondary"] = bench_secondary(args)
     if not args.no_cpu_baseline:
         log("oracle baseline on host cores")
         res["cpu_baseline"] = cpu_baseline(b)

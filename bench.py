@@ -172,7 +172,8 @@ def bench_decode(args):
                           for _ in range(7)]
     t0 = time.perf_counter()
     plan = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
-                    num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype)
+                    num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype,
+                    narrow_kernel=args.narrow_kernel)
     plan_ms = (time.perf_counter() - t0) * 1e3
     plan.bind(idx, num_pages=b.num_pages)
     info = plan.info
@@ -195,7 +196,8 @@ def bench_decode(args):
                    "page_size": 16, "kv_cache_copies_rotated": len(kvs)},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
-                     "kernel": "attn_narrow_kernel", "avg_ms": attn_avg,
+                     "kernel": "attn_narrow_kernel" if args.narrow_kernel == "mfma" else "attn_narrow_valu_kernel",
+                     "avg_ms": attn_avg,
                      "algorithmic_bytes_per_launch": alg_bytes},
         "tflops": flops / (ms * 1e-3) / 1e12,
         "kernels": {"narrow_avg_ms": attn_avg, "launches_per_step": (n_attn + n_wide) / args.steps},
@@ -250,11 +252,12 @@ def time_fn(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def bound_plan(b):
+def bound_plan(b, narrow="mfma"):
     import torch
     import paged_kv_attention_ragged_amd as rpa
     p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
-                 num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal)
+                 num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal,
+                 narrow_kernel=narrow)
     p.bind(torch.from_numpy(b.kv_page_indices).cuda(), num_pages=b.kv_cache.shape[0])
     return p
 
@@ -269,8 +272,8 @@ def bench_secondary(args):
     steps = max(5, args.steps // 10)
     out = {}
 
-    def direct(b, rotate=1):
-        p = bound_plan(b)
+    def direct(b, rotate=1, narrow="mfma"):
+        p = bound_plan(b, narrow)
         q, kv0 = b.q.cuda(), b.kv_cache.cuda()
         kvs = [kv0] + [kv0.clone() for _ in range(rotate - 1)]
         o = torch.empty_like(q)
@@ -331,6 +334,14 @@ def bench_secondary(args):
     # the decode loop: eager vs graph-captured steps
     log("decode loop: eager vs graph")
     out["decode_loop"] = bench_decode_loop()
+    # decode tiles on the VALU kernel instead of MFMA (the pages' CUDA-core decode)
+    log("decode on the VALU kernel")
+    db = W.decode_b128_kv1024(device="cuda")
+    v_ms, _ = direct(db, rotate=8, narrow="valu")
+    m_ms, _ = direct(db, rotate=8)
+    out["decode_b128_kv1024_valu_vs_mfma"] = {"valu_ms": v_ms, "mfma_ms": m_ms}
+    del db
+    out["shared_prefix"]["decode_step_valu_ms"] = direct(d, rotate=6, narrow="valu")[0]
     # mixed long batch: its decode rows alone and the whole batch in one call
     log("mixed long batch: decode rows, whole batch")
     for part in ("decode", "all"):
@@ -341,6 +352,7 @@ def bench_secondary(args):
         if part == "decode":
             ent["kv_gbs"] = kvb / ms / 1e6
             ent["hbm_frac"] = ent["kv_gbs"] / HBM_PEAK_GBS
+            ent["valu_ms"] = direct(mb, narrow="valu")[0]
         out["mixed_long_" + part] = ent
         del mb
         torch.cuda.empty_cache()
@@ -476,6 +488,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads")
+    ap.add_argument("--narrow-kernel", choices=("mfma", "valu"), default="mfma",
+                    help="kernel for the headline decode tiles (default: the MFMA one)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the batch-size sweep at constant total tokens (one JSON line per batch size)")
     ap.add_argument("--calibrate-copy", action="store_true",

@@ -76,6 +76,9 @@ typedef struct {
     float sm_scale;         /* <= 0 selects 1/sqrt(head_dim)                      */
     int32_t max_kv_splits;  /* 0: planner decides; 1: never split; n: at most n   */
     int32_t num_cus;        /* compute units the schedule targets; 0 selects 256  */
+    int32_t narrow_kernel;  /* decode-like tiles: 0 MFMA kernel (up to 16 rows per
+                               tile), 1 VALU kernel without MFMA (up to 8 rows;
+                               the design of the pages' CUDA-core decode)        */
 } rpa_params;
 
 typedef struct rpa_plan rpa_plan;
@@ -149,8 +152,9 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
  *   o         device [total_q][num_qo_heads][head_dim], same dtype (written)
  *   lse       device fp32 [total_q][num_qo_heads] (written), or NULL
  * Enqueues on `stream` one kernel for the plan's wide tiles (up to 128 query
- * rows each) and one for its narrow tiles (up to 16 rows: decode-like), each
- * only if the plan has such tiles; when the plan splits key ranges, the piece
+ * rows each) and one for its narrow tiles (up to 16 rows: decode-like; up to 8
+ * on the VALU kernel, params.narrow_kernel = 1), each only if the plan has such
+ * tiles; when the plan splits key ranges, the piece
  * of each split group that finishes last merges the group inside its kernel.
  * No allocation, no host<->device synchronisation.  One run at a time per
  * (plan, workspace): the partial-result region and the split counters are

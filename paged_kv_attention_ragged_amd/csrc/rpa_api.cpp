@@ -84,8 +84,10 @@ rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_
         return set_err(RPA_E_ARG, "dtype must be RPA_F16 (0) or RPA_BF16 (1)");
     if (params->causal != 0 && params->causal != 1) return set_err(RPA_E_ARG, "causal must be 0 or 1");
     if (!std::isfinite(params->sm_scale)) return set_err(RPA_E_ARG, "sm_scale must be finite");
+    if (params->narrow_kernel != 0 && params->narrow_kernel != 1)
+        return set_err(RPA_E_ARG, "narrow_kernel must be 0 (MFMA) or 1 (VALU)");
     rpa::PlanParams pp{params->num_qo_heads, params->num_kv_heads, params->head_dim, params->page_size,
-                       params->causal, params->max_kv_splits, params->num_cus};
+                       params->causal, params->max_kv_splits, params->num_cus, params->narrow_kernel};
     rpa_plan* plan = new (std::nothrow) rpa_plan();
     if (!plan) return set_err(RPA_E_ARG, "out of host memory");
     std::string err;
@@ -182,7 +184,7 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
     if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
     const rpa_params& P = plan->params;
     rpa::PlanParams pp{P.num_qo_heads, P.num_kv_heads, P.head_dim, P.page_size, P.causal, P.max_kv_splits,
-                       P.num_cus};
+                       P.num_cus, P.narrow_kernel};
     rpa::Schedule S;
     std::string err;
     int rc = 0;
@@ -269,7 +271,8 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
         rpa::LaunchAttn N = L;
         N.a.tiles = L.a.tiles + S.wide_tiles;
         N.n_tiles = S.narrow_tiles;
-        e = rpa::launch_narrow(N, st, e1.a, e1.b);
+        e = P.narrow_kernel == 1 ? rpa::launch_narrow_valu(N, S.narrow_max_rows, st, e1.a, e1.b)
+                                 : rpa::launch_narrow(N, st, e1.a, e1.b);
         if (e != hipSuccess) return hip_err(e, "narrow attention kernel launch");
     }
     if (prof) {

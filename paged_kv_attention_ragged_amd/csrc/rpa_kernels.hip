@@ -43,6 +43,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 fp16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma_qk(u32x4 a, u32x4 b, f32x16 c, bool bf16) {
     if (bf16)
@@ -91,6 +92,14 @@ __device__ __forceinline__ uint32_t pack_out(float a, float b) {
 }
 
 // Two fp32 probabilities in [0, 1] -> packed fp16, round to nearest-even.
+// One 16-bit element (low or high half of a packed word) as fp32, exactly.
+template <bool BF16>
+__device__ __forceinline__ float elem16(uint32_t w, int hi) {
+    const uint16_t h = uint16_t(hi ? (w >> 16) : (w & 0xffffu));
+    if (BF16) return __builtin_bit_cast(float, uint32_t(h) << 16);
+    return float(__builtin_bit_cast(_Float16, h));
+}
+
 __device__ __forceinline__ uint32_t pack_p(float a, float b) { return pack_out<false>(a, b); }
 
 // 16-bit element e (0..7) of a 16-byte vector, widened to an fp32 bit pattern
@@ -529,6 +538,49 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
 }
 
 
+// Combine of the 4 waves of a narrow tile (each walked its own keys) and the tile's
+// output: c_o holds each wave's unnormalised O rows ([wave * 16 + row][D + 4] fp32),
+// c_m / c_l its running max (log2 units) and sum per row.  Writes O (and LSE), or
+// the split partials followed by the fused merge.
+template <int D, bool BF16>
+__device__ __forceinline__ void narrow_combine_store(const AttnArgs& A, const Tile& T, const float* c_o,
+                                                     const float* c_m, const float* c_l, int rows_valid) {
+    constexpr int OS = D + 4;
+    constexpr int D4 = D / 4;
+    const int G = A.G;
+    for (int idx = threadIdx.x; idx < 16 * D4; idx += 256) {
+        const int r = idx / D4, c4 = idx - r * D4;
+        if (r >= rows_valid) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, c_m[w * 16 + r]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float L = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float wt = __builtin_amdgcn_exp2f(c_m[w * 16 + r] - Mu);
+            L += wt * c_l[w * 16 + r];
+            acc += wt * *(const f32x4*)(c_o + (w * 16 + r) * OS + 4 * c4);
+        }
+        const float inv = L > 0.f ? 1.f / L : 0.f;
+        const float lse_val = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
+        const int rt = r / G, rg = r - rt * G;
+        const int64_t orow_r = (int64_t)(T.q_row0 + rt) * A.H + T.kv_head * G + rg;
+        if (T.part < 0) {
+            u32x2 w2;
+            w2[0] = pack_out<BF16>(acc[0] * inv, acc[1] * inv);
+            w2[1] = pack_out<BF16>(acc[2] * inv, acc[3] * inv);
+            *(u32x2*)(A.o + orow_r * D + 4 * c4) = w2;
+            if (A.lse && c4 == 0) A.lse[orow_r] = lse_val;
+        } else {
+            st_dev4(A.part_o + ((int64_t)T.part + r) * D + 4 * c4, acc * inv);
+            if (c4 == 0) st_dev(A.part_lse + T.part + r, lse_val);
+        }
+    }
+    if (T.part >= 0) finish_split<D, BF16>(A, T);
+}
+
 // Narrow tile (decode-like): at most 16 rows (q_count * G <= 16), all in one
 // 16-column MFMA block.  The 4 waves split the key range: wave w takes the 64-key
 // steps w, w+4, w+8, ... of [kv_begin, kv_end), each with its own running max,
@@ -735,38 +787,224 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
         c_l[wave * 16 + col] = lsum;
     }
     __syncthreads();
-    constexpr int D4 = D / 4;
-    for (int idx = tid; idx < 16 * D4; idx += 256) {
-        const int r = idx / D4, c4 = idx - r * D4;
-        if (r >= rows_valid) continue;
-        float M = -INFINITY;
+    narrow_combine_store<D, BF16>(A, T, c_o, c_m, c_l, rows_valid);
+}
+
+// Narrow tile on the VALU, without MFMA: the decode design of the pages' GPUs,
+// where decode runs on the CUDA cores and prefill on the tensor cores (flashinfer
+// issue #323, "How are prefill and decode kernels different?"), kept for
+// comparison with the MFMA narrow kernel.  At most RM <= 8 rows; the 4 waves split
+// the key range in 32-key steps (wave w takes steps w, w+4, ...).  Lane layout:
+// lane = LPR * g + j, LPR = D / 8 lanes per K/V row (j: d = 8j .. 8j+7) and
+// KPI = 64 / LPR keys per load instruction (g: which key).
+//   * Q is pinned in VGPRs: each lane holds its 8 d of every row;
+//   * scores: per key, 4 dot2 per row, then a reduce-scatter over the key's LPR
+//     lanes (halving exchanges), after which each lane holds one row's score;
+//   * P and the per-row rescale factors go through LDS ([key][row]) and are read
+//     back as broadcasts;
+//   * O: each lane accumulates its 8 d of every row over its keys, fp32 FMAs; the
+//     KPI key groups are summed once at the end.
+template <int D, bool BF16, int RM>
+__device__ __forceinline__ void valu_tile(const AttnArgs& A, const Tile& T, char* smem) {
+    constexpr int LPR = D / 8;
+    constexpr int KPI = 64 / LPR;
+    constexpr int KW = kValuKeys;
+    constexpr int NI = KW / KPI;
+    constexpr int KB = KW / 16;  // pages per step
+    static_assert(RM <= LPR && KW % KPI == 0, "lane layout");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane / LPR, j = lane % LPR;
+    const int G = A.G;
+    const int rows_valid = T.q_count * G;
+    int my_row = 0;  // the row whose score this lane holds after the reduce-scatter
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, c_m[w * 16 + r]);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        float L = 0.f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int dl = LPR / 2, half = RM / 2; dl >= 1 && half >= 1; dl /= 2, half /= 2)
+        if (j & dl) my_row += half;
+    const int my_pos = T.pos0 + my_row / G;
+    const int pos_min = T.pos0;
+
+    u32x4 qv[RM];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float wt = __builtin_amdgcn_exp2f(c_m[w * 16 + r] - Mu);
-            L += wt * c_l[w * 16 + r];
-            acc += wt * *(const f32x4*)(c_o + (w * 16 + r) * OS + 4 * c4);
+    for (int r = 0; r < RM; ++r) {
+        const int tok = r / G, gh = r - tok * G;
+        const int64_t orow = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + gh;
+        qv[r] = r < rows_valid ? *(const u32x4*)(A.q + orow * D + 8 * j) : u32x4{0, 0, 0, 0};
+    }
+    float oacc[RM][8];
+#pragma unroll
+    for (int r = 0; r < RM; ++r)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) oacc[r][e] = 0.f;
+    float m = -INFINITY, lsum = 0.f;
+    float* p_lds = reinterpret_cast<float*>(smem) + wave * (KW * RM + RM);  // [KW][RM], then alpha[RM]
+    float* a_lds = p_lds + KW * RM;
+    const int64_t ss = (int64_t)A.Hkv * D;
+    const uint16_t* kvh = A.kv + (int64_t)T.kv_head * D + 8 * j;
+
+    constexpr int STRIDE = kWaves * KW;
+    for (int kbase = T.kv_begin + wave * KW; kbase < T.kv_end; kbase += STRIDE) {
+        int pages[KB];
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            int pg = -1;
+            if (kbase + 16 * b < T.kv_len) {
+                pg = A.page_idx[T.page_base + (kbase >> 4) + b];
+                if ((unsigned)pg >= (unsigned)A.num_pages) {
+                    *A.err_flag = 1;
+                    pg = -1;
+                }
+            }
+            pages[b] = pg;
         }
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        const float lse_val = L > 0.f ? (M + __log2f(L)) * 0.69314718055994530942f : -INFINITY;
-        const int rt = r / G, rg = r - rt * G;
-        const int64_t orow_r = (int64_t)(T.q_row0 + rt) * A.H + T.kv_head * G + rg;
-        if (T.part < 0) {
-            u32x2 w2;
-            w2[0] = pack_out<BF16>(acc[0] * inv, acc[1] * inv);
-            w2[1] = pack_out<BF16>(acc[2] * inv, acc[3] * inv);
-            *(u32x2*)(A.o + orow_r * D + 4 * c4) = w2;
-            if (A.lse && c4 == 0) A.lse[orow_r] = lse_val;
-        } else {
-            st_dev4(A.part_o + ((int64_t)T.part + r) * D + 4 * c4, acc * inv);
-            if (c4 == 0) st_dev(A.part_lse + T.part + r, lse_val);
+        u32x4 kr[NI], vr[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int kl = KPI * i + g;  // key within the step
+            const int pg = pages[kl >> 4];
+            const bool ok = pg >= 0 && kbase + kl < T.kv_len;
+            const uint16_t* src = kvh + ((int64_t)pg * 32 + (kl & 15)) * ss;
+            kr[i] = ok ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
+            vr[i] = ok ? *(const u32x4*)(src + 16 * ss) : u32x4{0, 0, 0, 0};
+        }
+        // ---- scores ----
+        float sv[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float part[RM];
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // element copies first: __builtin_bit_cast of a vector-element
+                    // expression is compiled as a read of element 0
+                    const uint32_t qe = qv[r][e], ke = kr[i][e];
+                    if (BF16)
+                        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qe),
+                                                              __builtin_bit_cast(bf16x2, ke), acc, false);
+                    else
+                        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2, qe), __builtin_bit_cast(fp16x2, ke),
+                                                     acc, false);
+                }
+                part[r] = acc;
+            }
+            int len = RM;
+#pragma unroll
+            for (int dl = LPR / 2; dl >= 1; dl /= 2) {
+                if (len > 1) {
+                    const int half = len / 2;
+                    const bool bit = (j & dl) != 0;
+#pragma unroll
+                    for (int t = 0; t < half; ++t) {
+                        const float send = bit ? part[t] : part[half + t];
+                        const float keep = bit ? part[half + t] : part[t];
+                        part[t] = keep + __shfl_xor(send, dl);
+                    }
+                    len = half;
+                } else {
+                    part[0] += __shfl_xor(part[0], dl);
+                }
+            }
+            sv[i] = part[0];
+        }
+        // ---- online softmax of this lane's row over the step's keys ----
+        const bool need_mask = (kbase + KW > T.kv_len) || (A.causal && kbase + KW - 1 > pos_min);
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            float x = sv[i] * A.c_log2;
+            if (need_mask) {
+                const int key = kbase + KPI * i + g;
+                if (key >= T.kv_len || (A.causal && key > my_pos)) x = -INFINITY;
+            }
+            sv[i] = x;
+            bmax = fmaxf(bmax, x);
+        }
+#pragma unroll
+        for (int dl = LPR; dl < 64; dl *= 2) bmax = fmaxf(bmax, __shfl_xor(bmax, dl));
+        const float m_new = fmaxf(m, bmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        m = m_new;
+        lsum *= alpha;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float pv = __builtin_amdgcn_exp2f(sv[i] - m_use);
+            lsum += pv;
+            p_lds[(KPI * i + g) * RM + my_row] = pv;
+        }
+        if (g == 0) a_lds[my_row] = alpha;
+        // A wave's LDS accesses complete in issue order, so the reads below see the
+        // writes above; the previous step's reads were issued before these writes.
+        float ar[RM];
+#pragma unroll
+        for (int r = 0; r < RM; ++r) ar[r] = a_lds[r];
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oacc[r][e] *= ar[r];
+        // ---- O += P V ----
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const float* pk = p_lds + (KPI * i + g) * RM;
+            float pr[RM];
+#pragma unroll
+            for (int r = 0; r < RM; ++r) pr[r] = pk[r];
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[2 * e] = elem16<BF16>(vr[i][e], 0);
+                v[2 * e + 1] = elem16<BF16>(vr[i][e], 1);
+            }
+#pragma unroll
+            for (int r = 0; r < RM; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) oacc[r][e] = __builtin_fmaf(pr[r], v[e], oacc[r][e]);
         }
     }
-    if (T.part >= 0) finish_split<D, BF16>(A, T);
+
+    // ---- sum the key groups, then combine the 4 waves ----
+#pragma unroll
+    for (int dl = LPR; dl < 64; dl *= 2) {
+        lsum += __shfl_xor(lsum, dl);
+#pragma unroll
+        for (int r = 0; r < RM; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) oacc[r][e] += __shfl_xor(oacc[r][e], dl);
+    }
+    __syncthreads();  // every wave is done with its P staging area
+    constexpr int OS = D + 4;
+    float* c_o = reinterpret_cast<float*>(smem);
+    float* c_m = c_o + kWaves * 16 * OS;
+    float* c_l = c_m + kWaves * 16;
+    if (g == 0) {
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            *(f32x4*)(c_o + (wave * 16 + r) * OS + 8 * j) = f32x4{oacc[r][0], oacc[r][1], oacc[r][2], oacc[r][3]};
+            *(f32x4*)(c_o + (wave * 16 + r) * OS + 8 * j + 4) = f32x4{oacc[r][4], oacc[r][5], oacc[r][6], oacc[r][7]};
+        }
+        c_m[wave * 16 + my_row] = m;
+        c_l[wave * 16 + my_row] = lsum;
+    }
+    __syncthreads();
+    narrow_combine_store<D, BF16>(A, T, c_o, c_m, c_l, rows_valid);
+}
+
+template <int D>
+struct ValuLds {
+    static constexpr int stage_bytes = kWaves * (kValuKeys * kValuRows + kValuRows) * 4;
+    static constexpr int combine_bytes = kWaves * 16 * (D + 4) * 4 + 2 * kWaves * 16 * 4;
+    static constexpr int bytes = stage_bytes > combine_bytes ? stage_bytes : combine_bytes;
+};
+
+// Narrow tiles on the VALU: at most RM rows each.
+template <int D, bool BF16, int RM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_narrow_valu_kernel(AttnArgs A) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const Tile T = A.tiles[blockIdx.x];
+    if (T.q_count <= 0) return;
+    valu_tile<D, BF16, RM>(A, T, smem);
 }
 
 // Wide tiles: two workgroups per CU (two waves per SIMD).
@@ -803,12 +1041,6 @@ void attn_narrow_kernel(AttnArgs A) {
 // threads of a (row, head) are adjacent lanes of one wave, so every one of them
 // has read LSE_a and LSE_b before the wave's LSE store: O and LSE may be merged
 // in place.
-template <bool BF16>
-__device__ __forceinline__ float elem16(uint32_t w, int hi) {
-    const uint16_t h = uint16_t(hi ? (w >> 16) : (w & 0xffffu));
-    if (BF16) return __builtin_bit_cast(float, uint32_t(h) << 16);
-    return float(__builtin_bit_cast(_Float16, h));
-}
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void merge_states_kernel(MergeArgs M) {
@@ -908,6 +1140,25 @@ hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0
                       : launch_with_lds(&attn_narrow_kernel<128, false>, L, NarrowLds<128>::bytes, stream, ev0, ev1);
     return L.bf16 ? launch_with_lds(&attn_narrow_kernel<64, true>, L, NarrowLds<64>::bytes, stream, ev0, ev1)
                   : launch_with_lds(&attn_narrow_kernel<64, false>, L, NarrowLds<64>::bytes, stream, ev0, ev1);
+}
+
+template <int D, bool BF16>
+hipError_t launch_valu_d(const LaunchAttn& L, int rows, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    if (rows <= 2)
+        return launch_with_lds(&attn_narrow_valu_kernel<D, BF16, 2>, L, ValuLds<D>::bytes, stream, ev0, ev1);
+    if (rows <= 4)
+        return launch_with_lds(&attn_narrow_valu_kernel<D, BF16, 4>, L, ValuLds<D>::bytes, stream, ev0, ev1);
+    return launch_with_lds(&attn_narrow_valu_kernel<D, BF16, 8>, L, ValuLds<D>::bytes, stream, ev0, ev1);
+}
+
+hipError_t launch_narrow_valu(const LaunchAttn& L, int max_rows, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    if (L.n_tiles <= 0) return hipSuccess;
+    if (max_rows > kValuRows) return hipErrorInvalidValue;
+    if (L.head_dim == 128)
+        return L.bf16 ? launch_valu_d<128, true>(L, max_rows, stream, ev0, ev1)
+                      : launch_valu_d<128, false>(L, max_rows, stream, ev0, ev1);
+    return L.bf16 ? launch_valu_d<64, true>(L, max_rows, stream, ev0, ev1)
+                  : launch_valu_d<64, false>(L, max_rows, stream, ev0, ev1);
 }
 
 hipError_t launch_append(const AppendArgs& A, hipStream_t stream) {

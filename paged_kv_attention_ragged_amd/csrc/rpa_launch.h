@@ -60,6 +60,8 @@ struct AppendArgs {
 // ev0 / ev1: optional events stamped at the start and end of the dispatch (NULL: none).
 hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+// Narrow tiles on the VALU kernel; max_rows (<= kValuRows) picks its row capacity.
+hipError_t launch_narrow_valu(const LaunchAttn& L, int max_rows, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_merge(const MergeArgs& M, bool bf16, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& A, hipStream_t stream);
 

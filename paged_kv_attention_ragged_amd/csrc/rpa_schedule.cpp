@@ -150,7 +150,7 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
                 t.page_base = kv_page_indptr[b];
                 // keys past the last query's position are masked for every row: skip them
                 t.kv_end = p.causal ? std::min(kv_len, t.pos0 + t.q_count) : kv_len;
-                t.kind = t.q_count * G <= kNarrowRows ? kNarrow : kWide;
+                t.kind = t.q_count * G <= (p.narrow_valu ? kValuRows : kNarrowRows) ? kNarrow : kWide;
                 base.push_back(t);
             }
     }
@@ -224,9 +224,12 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
             t.n_splits = ns;
             t.kind = q.kind;
             t.group = ns > 1 ? int32_t(S.merges.size()) - 1 : -1;
-            if (t.kind == kNarrow) ++S.narrow_tiles;
+            if (t.kind == kNarrow) {
+                ++S.narrow_tiles;
+                S.narrow_max_rows = std::max(S.narrow_max_rows, t.q_count * G);
+            }
             // cost ~ keys walked (wide tiles: rounded up to whole blocks) plus a fixed overhead
-            const int64_t gran = t.kind == kWide ? BN : kWaveKeys;
+            const int64_t gran = t.kind == kWide ? BN : (p.narrow_valu ? kValuKeys : kWaveKeys);
             pieces.push_back({t, ceil_div(t.kv_end - t.kv_begin, gran) * gran + 64});
         }
         if (ns > 1) part_next += int64_t(ns) * rows;

@@ -18,6 +18,8 @@ constexpr int block_m_for(int head_dim) { return head_dim > 0 ? 128 : 128; }
 
 constexpr int kNarrowRows = 16;  // tiles with at most this many rows take the narrow path
 constexpr int kWaveKeys = 64;     // keys one wave handles per step on the narrow path
+constexpr int kValuRows = 8;      // narrow threshold when narrow tiles run on the VALU kernel
+constexpr int kValuKeys = 32;     // keys one wave handles per step on the VALU narrow path
 constexpr int kXcds = 8;          // MI355X: workgroup i of a launch runs on XCD i % 8
 constexpr int kChunkKeys = 256;   // split pieces start at multiples of this many keys
 
@@ -66,6 +68,7 @@ struct PlanParams {
     int32_t num_qo_heads, num_kv_heads, head_dim, page_size, causal;
     int32_t max_kv_splits;  // 0 = decide, 1 = never, n = cap
     int32_t num_cus;
+    int32_t narrow_valu;    // 1: narrow tiles (<= kValuRows rows) run on the VALU kernel
 };
 
 struct Schedule {
@@ -78,6 +81,7 @@ struct Schedule {
     int64_t wide_tiles = 0;     // tiles[0, wide_tiles) are wide, the rest narrow
     int32_t max_splits = 1;
     int64_t narrow_tiles = 0;
+    int32_t narrow_max_rows = 0;  // largest row count among narrow tiles
     int64_t total_q = 0;
     int64_t visible_pairs = 0;  // per qo head, summed over heads
     int64_t kv_tokens = 0;

@@ -307,6 +307,21 @@ def test_append_kv_rejects_bad_arguments_without_launching():
     assert rpa.STATUS[lib.rpa_plan_upload(None, None)] == "RPA_E_ARG"
 
 
+def test_valu_narrow_kernel_takes_tiles_of_at_most_8_rows():
+    b = lengths_batch([1, 2, 1, 3], [40, 50, 1000, 300], H=8, Hk=2)  # G = 4: rows 4, 8, 4, 12
+    p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=8, num_kv_heads=2,
+                 head_dim=128, dtype="bf16", narrow_kernel="valu")
+    t = p.tiles()
+    rows = t[:, F["q_count"]] * 4
+    assert ((t[:, F["kind"]] == 1) == ((rows > 0) & (rows <= 8))).all()
+    assert (t[t[:, F["kind"]] == 1][:, F["kv_begin"]] % 32 == 0).all()
+    m = make_plan(b).tiles()  # the MFMA narrow kernel takes up to 16 rows
+    assert ((m[:, F["kind"]] == 1) == ((m[:, F["q_count"]] * 4 > 0) & (m[:, F["q_count"]] * 4 <= 16))).all()
+    with pytest.raises(KeyError):
+        rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=8, num_kv_heads=2,
+                 head_dim=128, narrow_kernel="tensor")
+
+
 def test_validate_page_table():
     b = W.tiny_ragged_prefill(spare_pages=2)
     rpa.validate_page_table(b.kv_page_indptr, b.kv_page_indices, b.num_pages)

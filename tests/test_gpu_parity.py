@@ -76,6 +76,22 @@ def test_narrow_tiles(shape):
         assert_close(o, l, ro, rl, what="narrow %s splits=%d cus=%d" % (shape, splits, cus))
 
 
+def test_64k_token_sequences_sampled():
+    """Long sequences: a decode row and a 256-token prefill chunk over 65536 cached
+    tokens each (64 qo / 8 kv heads, bf16), and a 20000-token causal prompt; both
+    kernels, splits and the 32-bit index arithmetic at this size."""
+    say("generate 64k batch on cuda")
+    b = W.make_batch("long64k", [1, 256, 20000], [65536, 65536, 20000], num_qo_heads=64, num_kv_heads=8,
+                     head_dim=128, dtype="bf16", seed=51, device="cuda")
+    dev = (b.q, b.kv_cache, torch.from_numpy(b.kv_page_indices).cuda())
+    rows = [0, 1, 2, 100, 255, 256] + list(range(257, 257 + 20000, 997)) + [257 + 19999]
+    ro, rl = ref(b, rows=rows)
+    for cus in (0, 65536):  # as planned, and with the long key ranges split
+        o, l, info = run(b, dev=dev, num_cus=cus)
+        assert cus == 0 or info["num_split_groups"] > 0
+        assert_close(o, l, ro, rl, rows=rows, what="64k sampled cus=%d" % cus)
+
+
 def test_long_single_sequence_splits():
     b = W.make_batch("long1", [5], [4000], num_qo_heads=8, num_kv_heads=1, head_dim=128, dtype="bf16", seed=32)
     ro, rl = ref(b)

@@ -11,6 +11,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 import oracle
@@ -51,6 +52,9 @@ MUTATIONS = {
     "f16_subnormal": ("v = ldexp((double)f, -24);", "v = ldexp((double)f, -25);"),
     # sign bit ignored for binary16
     "f16_sign": ("return sign ? -v : v;\n}\n\n/* bfloat16", "return v;\n}\n\n/* bfloat16"),
+    # non-causal sequences with more queries than keys rejected like causal ones
+    "noncausal_q_gt_kv_rejected": ("if (causal ? q_len > kv_len : (q_len > 0 && kv_len == 0))",
+                                   "if (q_len > kv_len)"),
 }
 
 
@@ -99,3 +103,36 @@ def test_every_planted_mistake_fails_a_pin(mutation, tmp_path):
         return  # crashed: caught
     line = [l for l in p.stdout.splitlines() if l.startswith("FAILED_PINS")][-1]
     assert int(line.split()[1]) > 0, "no pin caught the planted mistake %r" % mutation
+
+
+# Planted mistakes in oracle.merge_states (numpy): the cascade pin must catch each.
+def _merge_unweighted(o_a, lse_a, o_b, lse_b):
+    o, lse = _true_merge(o_a, lse_a, o_b, lse_b)
+    return (np.asarray(o_a, np.float64) + np.asarray(o_b, np.float64)) / 2, lse
+
+
+def _merge_swapped(o_a, lse_a, o_b, lse_b):
+    return _true_merge(o_b, lse_a, o_a, lse_b)
+
+
+def _merge_lse_is_max(o_a, lse_a, o_b, lse_b):
+    o, _ = _true_merge(o_a, lse_a, o_b, lse_b)
+    return o, np.maximum(lse_a, lse_b)
+
+
+def _merge_log2(o_a, lse_a, o_b, lse_b):
+    m = np.maximum(lse_a, lse_b)
+    wa, wb = np.exp2(lse_a - m), np.exp2(lse_b - m)
+    return (wa[..., None] * o_a + wb[..., None] * o_b) / (wa + wb)[..., None], m + np.log2(wa + wb)
+
+
+_true_merge = oracle.merge_states
+MERGE_MUTANTS = {"unweighted": _merge_unweighted, "swapped_outputs": _merge_swapped,
+                 "lse_is_max": _merge_lse_is_max, "base2_weights": _merge_log2}
+
+
+@pytest.mark.parametrize("mutant", sorted(MERGE_MUTANTS))
+def test_every_planted_merge_mistake_fails_the_cascade_pin(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "merge_states", MERGE_MUTANTS[mutant])
+    with pytest.raises(AssertionError):
+        pins.test_cascade_halves_merge_to_the_whole()

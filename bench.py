@@ -496,8 +496,8 @@ def main():
                     help="first run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (see DESIGN.md for how it "
-              "would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the path shards by "
+              "sequence or kv head without communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"

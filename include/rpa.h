@@ -59,7 +59,7 @@ typedef enum {
     RPA_E_QLEN_GT_KVLEN = 5,   /* causal: q_len > kv_len; non-causal: queries but
                                   no cached token                                 */
     RPA_E_WORKSPACE = 6,       /* workspace too small or misaligned               */
-    RPA_E_UNSUPPORTED = 7,     /* valid request this build does not implement     */
+    RPA_E_UNSUPPORTED = 7,     /* valid request the library does not implement    */
     RPA_E_HIP = 8,             /* a HIP runtime call failed (message has details) */
     RPA_E_PAGE_OOB = 9         /* a page index outside [0, num_pages)             */
 } rpa_status;

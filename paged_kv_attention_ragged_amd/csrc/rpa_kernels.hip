@@ -1,30 +1,30 @@
 // rpa_kernels.hip -- gfx950 (CDNA4) kernels for ragged attention over a paged
-// KV cache: the attention tile kernel and the split-KV merge kernel.
+// KV cache.  One 256-thread workgroup (4 wave64) per Tile; rows of a tile are
+// (token, qo head) pairs of one kv head's query group, token-major, so the G
+// heads sharing a kv head read each K/V block once (grouped-query attention,
+// flashinfer issue #323).
 //
-// Attention tile kernel, one 256-thread workgroup (4 wave64) per Tile:
-//   * rows of the tile are (token, qo head) pairs of one kv head's query group,
-//     token-major; wave w owns rows 32w .. 32w+31, so the G heads sharing a kv
-//     head are stacked into the MFMA dimension and read each K/V block once
-//     (grouped-query attention, flashinfer issue #323);
-//   * keys are walked in blocks of BN = 8192/D: each thread gathers 4 keys x 16
-//     bytes of K and of V through the page table (one page per wave for D=128),
-//     K goes to LDS as is, V is transposed (and, for bf16 inputs, converted to
-//     fp16) on its way to LDS; the next block's gather is in flight while the
-//     current block is computed;
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: each lane then holds one
-//     query row and 16 of its scores, so the running max needs one cross-half
-//     exchange and the running sum none until the end;
-//   * mask only on boundary blocks (past kv_len, or crossing the causal diagonal
-//     of the wave's rows); blocks past every row's position are never loaded
-//     (llama.cpp discussion #15958: fully masked tails are skipped);
-//   * online softmax in the exp2 domain, O^T += V^T P^T on
-//     v_mfma_f32_32x32x16_f16 with P rounded to fp16 (10 fraction bits);
-//   * epilogue: O / l rounded to nearest-even into the input dtype and
-//     LSE = ln(l) + max, or fp32 partial rows when the key range is split.
-// Split KV: a long key range is cut into pieces that run as separate work items;
-// the last piece to finish merges the pieces' (O_s, LSE_s) by weights
+//   attn_wide_kernel    tiles of up to 128 rows (prefill): S^T = K Q^T and
+//                       O^T += V^T P^T on v_mfma_f32_32x32x16, keys in blocks of
+//                       8192/D through a two-stage LDS ring, a software pipeline
+//                       over 32-key units (see wide_tile);
+//   attn_narrow_kernel  tiles of up to 16 rows (decode-like): the 4 waves split
+//                       the keys, v_mfma_f32_16x16x32, K straight into MFMA
+//                       registers, V read back transposed (see narrow_tile);
+//   attn_narrow_valu_kernel  the same tiles (up to 8 rows) without MFMA, on dot2
+//                       and fp32 FMAs, for comparison (see valu_tile);
+//   merge_states_kernel join of two attention states (cascade halves);
+//   append_kv_kernel    new tokens' K/V into their page slots.
+//
+// Common to the attention kernels: online softmax in the exp2 domain with P
+// rounded to fp16 for the P V product (bf16 V converted to fp16); masks only on
+// boundary blocks, and blocks past every row's causal position never loaded
+// (llama.cpp discussion #15958: fully masked tails are skipped); epilogue O / l
+// rounded to nearest-even into the input dtype and LSE = ln(l) + max.  Split KV:
+// a long key range is cut into pieces that run as separate work items; each
+// writes fp32 partial rows and the last piece to finish merges them by weights
 // exp(LSE_s - max LSE) inside the same launch (flashinfer issue #323 speaks of
-// kv-parallelism / split-k in the prefill kernel).
+// kv-parallelism / split-k).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>

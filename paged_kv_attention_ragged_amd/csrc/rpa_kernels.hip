@@ -183,7 +183,7 @@ __device__ __forceinline__ void finish_split(const AttnArgs& A, const Tile& T) {
     const int part0 = T.part - T.split * R;
     constexpr int D4 = D / 4;
     constexpr int NB = 8;  // pieces whose partials are loaded together (one memory round trip)
-    for (int idx = threadIdx.x; idx < R * D4; idx += 256) {
+    for (int idx = threadIdx.x; idx < R * D4; idx += blockDim.x) {
         const int r = idx / D4, c4 = idx - r * D4;
         float mx = -INFINITY, wsum = 0.f;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -302,6 +302,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     // waited on.  The loads always use a valid address (a key past kv_len or a bad
     // page reads page 0); the rare invalid keys are zeroed when staged.
     const int ch = tid % CH, kg = tid / CH;
+    const bool stager = kWideWaves == 4 || tid < 256;  // the threads that gather and stage
     const int64_t slot_stride = (int64_t)A.Hkv * D;
     const uint16_t* kv_base = A.kv + (int64_t)T.kv_head * D + 8 * ch;
     u32x4 kreg[4], vreg[4];
@@ -309,10 +310,12 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     int g_kv0 = 0;
     int page_next = 0;  // page index of the next gather's keys (unchecked)
     auto load_page = [&](int kv0) {
+        if (!stager) return;
         const int key0 = kv0 + 4 * kg;
         page_next = key0 < T.kv_len ? A.page_idx[T.page_base + (key0 >> 4)] : 0;
     };
     auto gather = [&](int kv0) {
+        if (!stager) return;
         const int key0 = kv0 + 4 * kg;
         const int page = page_next;
         const bool page_ok = (unsigned)page < (unsigned)A.num_pages;
@@ -349,6 +352,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     // wave-uniform and each side stages on its own, so the common path moves no
     // registers.
     auto stage = [&](int st) {
+        if (!stager) return;
         const int key0 = g_kv0 + 4 * kg;
         if (__builtin_amdgcn_ballot_w64(!g_ok || g_kv0 + BN > T.kv_len)) {
 #pragma unroll
@@ -1012,7 +1016,7 @@ void attn_narrow_valu_kernel(AttnArgs A) {
 
 // Wide tiles: two workgroups per CU (two waves per SIMD).
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_wide_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];
@@ -1112,46 +1116,49 @@ __global__ __launch_bounds__(256) void append_kv_kernel(AppendArgs A) {
     }
 }
 
-template <typename K>
-hipError_t launch_with_lds(K kernel, const LaunchAttn& L, int lds, hipStream_t stream, hipEvent_t ev0,
+// Launch one workgroup of `threads` per tile with `lds` bytes of dynamic LDS.  Dynamic
+// LDS above 64 KiB must be allowed per kernel: done once per kernel (the template
+// argument), before its first launch.
+template <void (*Kernel)(AttnArgs)>
+hipError_t launch_with_lds(const LaunchAttn& L, int lds, int threads, hipStream_t stream, hipEvent_t ev0,
                            hipEvent_t ev1) {
-    // Dynamic LDS above 64 KiB must be allowed per kernel; do it once per instantiation.
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipExtLaunchKernelGGL(kernel, dim3((unsigned)L.n_tiles), dim3(256), (uint32_t)lds, stream, ev0, ev1, 0, L.a);
+    hipExtLaunchKernelGGL(Kernel, dim3((unsigned)L.n_tiles), dim3(threads), (uint32_t)lds, stream, ev0, ev1, 0,
+                          L.a);
     return hipGetLastError();
 }
 
 hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (L.n_tiles <= 0) return hipSuccess;
     if (L.head_dim == 128)
-        return L.bf16 ? launch_with_lds(&attn_wide_kernel<128, true>, L, WideCfg<128>::bytes, stream, ev0, ev1)
-                      : launch_with_lds(&attn_wide_kernel<128, false>, L, WideCfg<128>::bytes, stream, ev0, ev1);
-    return L.bf16 ? launch_with_lds(&attn_wide_kernel<64, true>, L, WideCfg<64>::bytes, stream, ev0, ev1)
-                  : launch_with_lds(&attn_wide_kernel<64, false>, L, WideCfg<64>::bytes, stream, ev0, ev1);
+        return L.bf16 ? launch_with_lds<&attn_wide_kernel<128, true>>(L, WideCfg<128>::bytes, kWideWaves * 64, stream, ev0, ev1)
+                      : launch_with_lds<&attn_wide_kernel<128, false>>(L, WideCfg<128>::bytes, kWideWaves * 64, stream, ev0, ev1);
+    return L.bf16 ? launch_with_lds<&attn_wide_kernel<64, true>>(L, WideCfg<64>::bytes, kWideWaves * 64, stream, ev0, ev1)
+                  : launch_with_lds<&attn_wide_kernel<64, false>>(L, WideCfg<64>::bytes, kWideWaves * 64, stream, ev0, ev1);
 }
 
 hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (L.n_tiles <= 0) return hipSuccess;
     if (L.head_dim == 128)
-        return L.bf16 ? launch_with_lds(&attn_narrow_kernel<128, true>, L, NarrowLds<128>::bytes, stream, ev0, ev1)
-                      : launch_with_lds(&attn_narrow_kernel<128, false>, L, NarrowLds<128>::bytes, stream, ev0, ev1);
-    return L.bf16 ? launch_with_lds(&attn_narrow_kernel<64, true>, L, NarrowLds<64>::bytes, stream, ev0, ev1)
-                  : launch_with_lds(&attn_narrow_kernel<64, false>, L, NarrowLds<64>::bytes, stream, ev0, ev1);
+        return L.bf16 ? launch_with_lds<&attn_narrow_kernel<128, true>>(L, NarrowLds<128>::bytes, kWaves * 64, stream, ev0, ev1)
+                      : launch_with_lds<&attn_narrow_kernel<128, false>>(L, NarrowLds<128>::bytes, kWaves * 64, stream, ev0, ev1);
+    return L.bf16 ? launch_with_lds<&attn_narrow_kernel<64, true>>(L, NarrowLds<64>::bytes, kWaves * 64, stream, ev0, ev1)
+                  : launch_with_lds<&attn_narrow_kernel<64, false>>(L, NarrowLds<64>::bytes, kWaves * 64, stream, ev0, ev1);
 }
 
 template <int D, bool BF16>
 hipError_t launch_valu_d(const LaunchAttn& L, int rows, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (rows <= 2)
-        return launch_with_lds(&attn_narrow_valu_kernel<D, BF16, 2>, L, ValuLds<D>::bytes, stream, ev0, ev1);
+        return launch_with_lds<&attn_narrow_valu_kernel<D, BF16, 2>>(L, ValuLds<D>::bytes, kWaves * 64, stream, ev0, ev1);
     if (rows <= 4)
-        return launch_with_lds(&attn_narrow_valu_kernel<D, BF16, 4>, L, ValuLds<D>::bytes, stream, ev0, ev1);
-    return launch_with_lds(&attn_narrow_valu_kernel<D, BF16, 8>, L, ValuLds<D>::bytes, stream, ev0, ev1);
+        return launch_with_lds<&attn_narrow_valu_kernel<D, BF16, 4>>(L, ValuLds<D>::bytes, kWaves * 64, stream, ev0, ev1);
+    return launch_with_lds<&attn_narrow_valu_kernel<D, BF16, 8>>(L, ValuLds<D>::bytes, kWaves * 64, stream, ev0, ev1);
 }
 
 hipError_t launch_narrow_valu(const LaunchAttn& L, int max_rows, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {

@@ -14,7 +14,8 @@ constexpr int kWaves = 4;       // wavefronts per workgroup
 
 // Query rows (token x qo head of one kv group, token-major) per wide tile: each of
 // the 4 waves owns one 32-row MFMA column block.
-constexpr int block_m_for(int head_dim) { return head_dim > 0 ? 128 : 128; }
+constexpr int kWideWaves = 4;  // wavefronts per wide-tile workgroup, 32 query rows each
+constexpr int block_m_for(int head_dim) { return head_dim > 0 ? 32 * kWideWaves : 32 * kWideWaves; }
 
 constexpr int kNarrowRows = 16;  // tiles with at most this many rows take the narrow path
 constexpr int kWaveKeys = 64;     // keys one wave handles per step on the narrow path

@@ -151,7 +151,7 @@ def cpu_baseline(b, target_s=10.0):
         n = min(b.batch, max(n, int(n * target_s / max(dt, 1e-3))))
         sub, dt = sample(n)
     reps = 1
-    while dt * reps < 0.3 * target_s and reps < 64:  # the whole batch is quick: repeat it
+    while dt * reps < target_s and reps < 200:  # the whole batch is quick: repeat it
         _, t = sample(n)
         dt = (dt * reps + t) / (reps + 1)
         reps += 1

@@ -555,7 +555,7 @@ __device__ __forceinline__ void narrow_combine_store(const AttnArgs& A, const Ti
     constexpr int OS = D + 4;
     constexpr int D4 = D / 4;
     const int G = A.G;
-    for (int idx = threadIdx.x; idx < 16 * D4; idx += 256) {
+    for (int idx = threadIdx.x; idx < 16 * D4; idx += blockDim.x) {
         const int r = idx / D4, c4 = idx - r * D4;
         if (r >= rows_valid) continue;
         float M = -INFINITY;
@@ -1006,7 +1006,7 @@ struct ValuLds {
 
 // Narrow tiles on the VALU: at most RM rows each.
 template <int D, bool BF16, int RM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_narrow_valu_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];
@@ -1026,7 +1026,7 @@ void attn_wide_kernel(AttnArgs A) {
 
 // Narrow tiles: two workgroups per CU, so twice the loads in flight per CU.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_narrow_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];

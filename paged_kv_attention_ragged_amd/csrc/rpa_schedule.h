@@ -10,7 +10,7 @@ namespace rpa {
 
 constexpr int kPageSize = 16;
 constexpr int kMaxGroup = 128;  // largest number of qo heads per kv head
-constexpr int kWaves = 4;       // wavefronts per workgroup
+constexpr int kWaves = 4;       // wavefronts per narrow-tile workgroup
 
 // Query rows (token x qo head of one kv group, token-major) per wide tile: each of
 // the 4 waves owns one 32-row MFMA column block.

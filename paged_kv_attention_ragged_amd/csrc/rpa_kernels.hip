@@ -5,9 +5,9 @@
 // flashinfer issue #323).
 //
 //   attn_wide_kernel    tiles of up to 128 rows (prefill): S^T = K Q^T and
-//                       O^T += V^T P^T on v_mfma_f32_32x32x16, keys in blocks of
-//                       8192/D through a two-stage LDS ring, a software pipeline
-//                       over 32-key units (see wide_tile);
+//                       O^T += V^T P^T on v_mfma_f32_32x32x16, 32-key units
+//                       loaded straight from the cache into an LDS ring, a
+//                       software pipeline over the units (see wide_tile);
 //   attn_narrow_kernel  tiles of up to 16 rows (decode-like): the 4 waves split
 //                       the keys, v_mfma_f32_16x16x32, K straight into MFMA
 //                       registers, V read back transposed (see narrow_tile);
@@ -18,7 +18,7 @@
 //
 // Common to the attention kernels: online softmax in the exp2 domain with P
 // rounded to fp16 for the P V product (bf16 V converted to fp16); masks only on
-// boundary blocks, and blocks past every row's causal position never loaded
+// boundary units, and blocks past every row's causal position never loaded
 // (llama.cpp discussion #15958: fully masked tails are skipped); epilogue O / l
 // rounded to nearest-even into the input dtype and LSE = ln(l) + max.  Split KV:
 // a long key range is cut into pieces that run as separate work items; each
@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "rpa_launch.h"
 #include "rpa_schedule.h"
@@ -80,6 +81,28 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at
+// LDS address m0 + 16 l (global_load_lds_dwordx4, SGPR base + 32-bit lane offset).
+// Written out as assembly so that the compiler's wait-count pass does not track it:
+// that pass cannot tell which later LDS reads may overlap the write and would wait
+// for every load in flight before them.  The caller waits with s_waitcnt vmcnt
+// before anyone reads the bytes.
+// The statement sets M0 itself; the compiler does not honour M0 in a clobber list,
+// which is safe only because no compiler-generated code in the kernels that use it
+// keeps a value in M0 (their assembly has no other M0 access).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t lane_off, uint32_t lds_m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(sbase), "s"(lds_m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// 32-bit LDS address of a pointer into the workgroup's shared memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // Two fp32 -> packed 16-bit, round to nearest-even.
 template <bool BF16>
 __device__ __forceinline__ uint32_t pack_out(float a, float b) {
@@ -109,17 +132,12 @@ __device__ __forceinline__ float bf16_elem(u32x4 v, int e) {
     return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
 }
 
-// Element e of keys i and j as one packed fp16 pair (low = key i).
-template <bool BF16>
-__device__ __forceinline__ uint32_t v_pair(u32x4 vi, u32x4 vj, int e) {
-    if (BF16) {
-        // bf16 -> fp16: exact for |x| in [2^-14, 65504]; round-toward-zero below
-        // (error < 2^-24) and saturation to 65504 above.
-        fp16x2 h = __builtin_amdgcn_cvt_pkrtz(bf16_elem(vi, e), bf16_elem(vj, e));
-        return __builtin_bit_cast(uint32_t, h);
-    }
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    return __builtin_amdgcn_perm(vj[e >> 1], vi[e >> 1], sel);
+// One packed bf16 pair as a packed fp16 pair: exact for |x| in [2^-14, 65504];
+// round-toward-zero below (error < 2^-24) and saturation to 65504 above.
+__device__ __forceinline__ uint32_t v_pair_fp16(uint32_t w) {
+    const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, w << 16),
+                                                __builtin_bit_cast(float, w & 0xffff0000u));
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // Value of lane l ^ 32: v_permlane32_swap exchanges the two 32-lane halves of a
@@ -228,15 +246,25 @@ __device__ __forceinline__ void finish_split(const AttnArgs& A, const Tile& T) {
     if (threadIdx.x == 0) __hip_atomic_store(A.counters + T.group, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Unit slots in the wide tile's LDS ring: 4 lets a unit's loads overlap two units of
+// compute at two workgroups per CU; 3 fits three workgroups per CU (three waves per
+// SIMD) with one unit of overlap.
+constexpr int kWideSlots = 3;
+constexpr int kWideWavesPerEU = kWideSlots == 3 ? 3 : 2;
+
 template <int D>
 struct WideCfg {
-    static constexpr int BN = 8192 / D;             // keys per block
-    static constexpr int NC = 1;                    // 32-row MFMA column blocks per wave
-    static constexpr int RW = 32 * NC;              // query rows per wave
-    static constexpr int KS = D + 8;                // K row stride in LDS (elements), 16-byte pad
-    static constexpr int STAGE = BN * KS + D * BN;  // elements of one K block + one V^T block
-    static constexpr int NSTAGE = 2;                // LDS ring: block j and block j+1
-    static constexpr int bytes = NSTAGE * STAGE * 2;
+    static constexpr int UK = 32;                            // keys per unit
+    static constexpr int R = 1024 / (2 * D);                 // K (or V) rows per 1 KiB load group
+    static constexpr int GS = 1024 + (D == 128 ? 64 : 128);  // LDS bytes per group (padded)
+    static constexpr int NG = UK / R;                        // groups per matrix per unit
+    static constexpr int IPW = NG / kWideWaves;              // loads per wave per matrix per unit
+    static constexpr int MAT = NG * GS;                      // LDS bytes of one unit's K (or V)
+    static constexpr int SLOT = 2 * MAT;                     // one unit: K then V
+    static constexpr int NS = kWideSlots;                    // ring slots
+    static constexpr int bytes = NS * SLOT;
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    static_assert(IPW * kWideWaves == NG, "the waves share a unit's groups evenly");
 };
 
 template <int D>
@@ -248,294 +276,304 @@ struct NarrowLds {
     static constexpr int bytes = stage_bytes > combine_bytes ? stage_bytes : combine_bytes;
 };
 
-// XOR swizzle of the 16-byte groups of a transposed-V row: the 8-byte transposing
-// writes (rows 8ch + e) and the 16-byte MFMA operand reads (rows 32db + lane) both
-// spread over the banks, and the read swizzle splits into a per-lane part and a
-// compile-time part.
-__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
-
 // Wide tile: up to block_m = 128 rows = 4 waves x 32 rows (token-major (token, qo
-// head) pairs of one kv head); keys in blocks of BN through a two-stage LDS ring; two
-// workgroups per CU.  Each wave software-pipelines in units of 32 keys: the basic
-// block that computes the exponentials and P V of one unit also issues Q K^T of the
-// next unit, so the matrix core and the VALU of one wave work on different units at
-// the same time.  Block j+1 is staged (and block j+2's gather issued) half-way
-// through block j, so the next block's first Q K^T finds it in LDS.
+// head) pairs of one kv head); keys in units of 32.  A unit's K and V go from the
+// cache straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at
+// base + 16 * lane), through a ring of NS = kWideSlots unit slots: unit u + NS - 1
+// is requested while unit u is computed, and each wave waits for its own share of
+// unit u + 2 before the barrier that ends unit u.  LDS layout of one matrix of a unit: groups of R = 1024 /
+// (2D) rows, one load instruction each, stored chunk-major (16-byte chunk c of row r
+// at 16 (R c + r)) with GS - 1024 bytes of padding after each group, so that the
+// K^T operand reads (16-byte chunks of 16 rows) and the transposing V reads (8-byte
+// pieces of 4 rows) fall on distinct banks.  V is read with ds_read_b64_tr_b16,
+// which hands each lane 4 keys of one d: the V^T operand, with no transposing store.
+// Each wave software-pipelines: the basic block that computes the exponentials and
+// P V of unit u also issues Q K^T of unit u + 1.  P V runs on fp16: bf16 V is
+// converted in LDS, one unit ahead, by the wave that loaded it.
 template <int D, bool BF16>
 __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char* smem) {
     using C = WideCfg<D>;
-    constexpr int BN = C::BN, NC = C::NC, RW = C::RW, KS = C::KS, STAGE = C::STAGE;
-    constexpr int CH = D / 8;    // 16-byte chunks per K/V row
-    constexpr int SB = BN / 32;  // 32-key score blocks
-    constexpr int DK = D / 16;   // k-steps of Q K^T
-    constexpr int DB = D / 32;   // 32-wide d blocks of O
-    static_assert(CH * (BN / 4) == 256, "each thread gathers 4 keys x 16 bytes");
-    uint16_t* const lds = reinterpret_cast<uint16_t*>(smem);
+    constexpr int R = C::R, GS = C::GS, MAT = C::MAT, SLOT = C::SLOT, IPW = C::IPW;
+    constexpr int DK = D / 16;  // k-steps of Q K^T
+    constexpr int DB = D / 32;  // 32-wide d blocks of O
+    static_assert(kWideWaves == 4, "4 waves of 32 rows");
+    // the page table through the constant address space: wave-uniform indices become
+    // scalar loads, which leave the vector-memory counter to the K/V loads alone
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = lane >> 5, col = lane & 31;
     const int G = A.G;
     const int rows_valid = T.q_count * G;
 
-    // This lane's query rows: column block c holds row wave*RW + 32c + col.
-    int pos[NC];
-    int64_t orow[NC];
-    bool row_ok[NC];
-    u32x4 qf[NC][DK];  // Q^T operand, 8 consecutive d per k-step, held for the whole tile
+    // This lane's query row: wave * 32 + col.
+    const int row = wave * 32 + col;
+    const int tok = row / G, g = row - tok * G;
+    const bool row_ok = row < rows_valid;
+    const int pos = T.pos0 + tok;
+    const int64_t orow = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
+    u32x4 qf[DK];  // Q^T operand, 8 consecutive d per k-step, held for the whole tile
+    {
+        const uint16_t* qp = A.q + orow * D + 8 * half;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int row = wave * RW + 32 * c + col;
-        const int tok = row / G, g = row - tok * G;
-        row_ok[c] = row < rows_valid;
-        pos[c] = T.pos0 + tok;
-        orow[c] = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
-        const uint16_t* qp = A.q + orow[c] * D + 8 * half;
-#pragma unroll
-        for (int kk = 0; kk < DK; ++kk)
-            qf[c][kk] = row_ok[c] ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
+        for (int kk = 0; kk < DK; ++kk) qf[kk] = row_ok ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
     }
-    const int wpos_min = T.pos0 + (wave * RW) / G;  // smallest position among this wave's rows
+    const int wpos_min = T.pos0 + (wave * 32) / G;  // smallest position among this wave's rows
 
-    // ---- gather (global -> registers) and stage (registers -> LDS) of one block ----
-    // Thread -> keys 4kg..4kg+3 of the block (one page), d = 8ch..8ch+7.  The page
-    // index of the next gather is loaded one gather ahead, so its latency is never
-    // waited on.  The loads always use a valid address (a key past kv_len or a bad
-    // page reads page 0); the rare invalid keys are zeroed when staged.
-    const int ch = tid % CH, kg = tid / CH;
-    const bool stager = kWideWaves == 4 || tid < 256;  // the threads that gather and stage
-    const int64_t slot_stride = (int64_t)A.Hkv * D;
-    const uint16_t* kv_base = A.kv + (int64_t)T.kv_head * D + 8 * ch;
-    u32x4 kreg[4], vreg[4];
-    bool g_ok = true;
-    int g_kv0 = 0;
-    int page_next = 0;  // page index of the next gather's keys (unchecked)
-    auto load_page = [&](int kv0) {
-        if (!stager) return;
-        const int key0 = kv0 + 4 * kg;
-        page_next = key0 < T.kv_len ? A.page_idx[T.page_base + (key0 >> 4)] : 0;
-    };
-    auto gather = [&](int kv0) {
-        if (!stager) return;
-        const int key0 = kv0 + 4 * kg;
-        const int page = page_next;
-        const bool page_ok = (unsigned)page < (unsigned)A.num_pages;
-        if (!page_ok) *A.err_flag = 1;
-        const uint16_t* src = kv_base + ((int64_t)(page_ok ? page : 0) * 32 + (key0 & 15)) * slot_stride;
+    // ---- loads of one unit into one ring slot ----
+    // Wave w loads groups m = w + 4j (j < IPW) of K and of V: rows R m .. R m + R - 1
+    // of the unit, all in one page.  Lane l: row R m + l % R, chunk l / R.
+    const int64_t ss = (int64_t)A.Hkv * D;  // elements between token slots
+    const char* kvh = reinterpret_cast<const char*>(A.kv + (int64_t)T.kv_head * D);
+    const uint32_t src_lane = (uint32_t)(((lane % R) * ss + 8 * (lane / R)) * 2);  // bytes
+    const int nunits = (T.kv_end - T.kv_begin + C::UK - 1) / C::UK;
+    // Page of each of this wave's groups for one unit, read ahead (scalar loads, not
+    // waited for here).  A group past kv_len reads page 0: its keys are masked and
+    // their V zeroed.
+    auto pages_of = [&](int t, int (&pg)[IPW]) {
+        const int kv0 = T.kv_begin + C::UK * t;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            kreg[i] = *(const u32x4*)(src + i * slot_stride);
-            vreg[i] = *(const u32x4*)(src + (16 + i) * slot_stride);
-        }
-        g_ok = page_ok;
-        g_kv0 = kv0;
-        if (kv0 + BN < T.kv_end) load_page(kv0 + BN);
-    };
-    // K goes to LDS as is; V is transposed into V^T (fp16) with the keys of each
-    // 16-key chunk in the order the P V MFMA consumes them (bits 2 and 3 swapped).
-    const int kb4 = 4 * kg;
-    const int vslot = (kb4 & ~15) | (((kb4 >> 2) & 1) << 3) | (((kb4 >> 3) & 1) << 2);
-    auto store_stage = [&](int st) {
-        uint16_t* k_lds = lds + st * STAGE;
-        uint16_t* vt_lds = k_lds + BN * KS;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(k_lds + (kb4 + i) * KS + 8 * ch) = kreg[i];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = 8 * ch + e;
-            u32x2 w;
-            w[0] = v_pair<BF16>(vreg[0], vreg[1], e);
-            w[1] = v_pair<BF16>(vreg[2], vreg[3], e);
-            *(u32x2*)(vt_lds + d * BN + 8 * ((vslot >> 3) ^ vt_swz(d)) + (vslot & 7)) = w;
+        for (int j = 0; j < IPW; ++j) {
+            const int key0 = kv0 + R * (wave + 4 * j);
+            pg[j] = key0 < T.kv_len ? ((const_i32*)A.page_idx)[T.page_base + (key0 >> 4)] : 0;
         }
     };
-    // Keys past kv_len and keys of a bad page are staged as zeros.  The test is
-    // wave-uniform and each side stages on its own, so the common path moves no
-    // registers.
-    auto stage = [&](int st) {
-        if (!stager) return;
-        const int key0 = g_kv0 + 4 * kg;
-        if (__builtin_amdgcn_ballot_w64(!g_ok || g_kv0 + BN > T.kv_len)) {
+    // Request one unit into one slot; returns the bad-page bits (bit j: an index outside
+    // [0, num_pages), which raises the error flag and reads page 0, its keys zeroed).
+    const uint32_t lds0 = lds_addr(smem);
+    auto load_unit = [&](int slot, const int (&pg)[IPW]) {
+        int bad = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (!g_ok || key0 + i >= T.kv_len) {
-                    kreg[i] = u32x4{0, 0, 0, 0};
-                    vreg[i] = u32x4{0, 0, 0, 0};
-                }
-            store_stage(st);
-        } else {
-            store_stage(st);
+        for (int j = 0; j < IPW; ++j) {
+            int p = pg[j];
+            if ((unsigned)p >= (unsigned)A.num_pages) {
+                *A.err_flag = 1;
+                p = 0;
+                bad |= 1 << j;
+            }
+            const int m = wave + 4 * j;
+            const char* src = kvh + ((int64_t)p * 32 + ((R * m) & 15)) * ss * 2;
+            const uint32_t dst = lds0 + slot * SLOT + m * GS;
+            load_lds16(src, src_lane, dst);
+            load_lds16(src + 16 * ss * 2, src_lane, dst + MAT);
+        }
+        return bad;
+    };
+    // After this wave's loads of unit t have landed: zero V of keys past kv_len, and K
+    // and V of bad pages (each lane the 16 bytes it loaded).
+    auto fix_unit = [&](int t, int slot, int bad) {
+        const int kv0 = T.kv_begin + C::UK * t;
+        if (bad == 0 && kv0 + C::UK <= T.kv_len) return;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < IPW; ++j) {
+            const int m = wave + 4 * j;
+            char* p = smem + slot * SLOT + m * GS + 16 * lane;
+            const bool b = (bad >> j) & 1;
+            if (b) *(u32x4*)p = u32x4{0, 0, 0, 0};
+            if (b || kv0 + R * m + lane % R >= T.kv_len) *(u32x4*)(p + MAT) = u32x4{0, 0, 0, 0};
         }
     };
 
-    // ---- per-lane LDS read offsets (elements, within a stage) ----
-    const int k_off = col * KS + 8 * half;  // + 32*kb*KS + 16*kk
-    // V^T row 32db + col, 16-byte group (2kc + half) ^ vt_swz(row): the group is
-    // (half ^ s_col) ^ (2kc ^ 4*(db & 1)) with s_col = (col ^ (col >> 3)) & 7.
-    const int s_col = (col ^ (col >> 3)) & 7;
-    int v_off[4];  // indexed by (2kc ^ 4(db&1)) / 2
+    // bf16 V to fp16, in place: each lane the 16 bytes it loaded (P V runs on fp16, as
+    // P keeps 11 bits there against bf16's 8).  Read and write are split so that other
+    // work covers the read's latency.
+    auto v_fp16_read = [&](int slot, u32x4 (&w)[IPW]) {
+        if constexpr (BF16) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) v_off[k] = BN * KS + col * BN + 8 * ((half ^ s_col) ^ (2 * k));
+            for (int j = 0; j < IPW; ++j)
+                w[j] = *(const u32x4*)(smem + slot * SLOT + MAT + (wave + 4 * j) * GS + 16 * lane);
+        }
+    };
+    auto v_fp16_write = [&](int slot, const u32x4 (&w)[IPW]) {
+        if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < IPW; ++j) {
+                u32x4 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = v_pair_fp16(w[j][e]);
+                *(u32x4*)(smem + slot * SLOT + MAT + (wave + 4 * j) * GS + 16 * lane) = h;
+            }
+        }
+    };
+
+    // ---- per-lane LDS read offsets (bytes, within a slot) ----
+    // K^T operand of k-step kk: row col, chunk 2kk + half.
+    const int k_lane = (col / R) * GS + 16 * (R * half + col % R);
+    // V^T operand (tr16): key 16h + 8r + e8 (e8 = 4 half + (i >> 2), i = lane % 16),
+    // d = 32db + 16 ((lane >> 4) & 1) + 4 (i & 3).
+    const int vi = lane & 15, e8 = 4 * half + (vi >> 2);
+    const int v_lane = MAT + (e8 / R) * GS + 16 * (R * (2 * ((lane >> 4) & 1) + ((vi & 3) >> 1)) + e8 % R) +
+                       8 * (vi & 1);
 
     // ---- state ----
-    f32x16 oacc[DB][NC];
+    f32x16 oacc[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) oacc[db][c] = f32x16{};
-    float m[NC], lsum[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        m[c] = -INFINITY;  // reference max of the scaled scores (log2 units)
-        lsum[c] = 0.f;     // this lane's share of the row sum
-    }
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    float m_run = -INFINITY;  // reference max of the scaled scores (log2 units)
+    float lsum = 0.f;         // this lane's share of the row sum
 
-    // The pipeline works in units of 32 keys (score block sb of LDS block j); scores
-    // of consecutive units alternate between two register buffers.
-    auto qk = [&](int st, int sb, f32x16 (&S)[NC]) {
-        const uint16_t* k_lds = lds + st * STAGE + k_off + 32 * sb * KS;
+    auto qk = [&](int slot, f32x16& S) {
+        const char* kp = smem + slot * SLOT + k_lane;
+        S = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) S[c] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < DK; ++kk) {
-            const u32x4 kf = *(const u32x4*)(k_lds + 16 * kk);
-#pragma unroll
-            for (int c = 0; c < NC; ++c) S[c] = mfma_qk(kf, qf[c][kk], S[c], BF16);
-        }
+        for (int kk = 0; kk < DK; ++kk) S = mfma_qk(*(const u32x4*)(kp + 32 * R * kk), qf[kk], S, BF16);
     };
 
-    // One unit: scores of unit (j, SBI) are in S; Q K^T of the next unit goes to Sn.
-    // st_j / st_j1 are the LDS stages of blocks j and j+1.  Unit 0 stages block j+1
-    // (gathered during block j-1) and issues block j+2's gather; a barrier then makes
-    // block j+1 visible before the last unit's Q K^T reads it.  The barrier after the
-    // last unit ends every read of stage st_j before block j+2 overwrites it.
-    auto unit = [&](auto sbi, int j, int st_j, int st_j1, f32x16 (&S)[NC], f32x16 (&Sn)[NC]) {
-        constexpr int SBI = decltype(sbi)::value;
-        const int kv0 = T.kv_begin + j * BN + 32 * SBI;
+    int pg_next[IPW];   // pages of the next unit to request
+    int bad_slots = 0;  // bad-page bits of the units in the ring, IPW per slot
+    auto sync_unit = [&](int t, int slot, bool newer_in_flight) {
+        // wait for this wave's loads of unit t (one younger unit's may stay in flight)
+        if (newer_in_flight) {
+            if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        fix_unit(t, slot, (bad_slots >> (slot * IPW)) & ((1 << IPW) - 1));
+    };
+    auto barrier = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    auto ring = [](int x) { return x >= C::NS ? x - C::NS : x; };  // x mod NS, x < 2 NS
+    constexpr int NS = C::NS;
+
+    // One unit u in slot u % NS: scores of u are in S; Q K^T of u + 1 goes to Sn.
+    auto unit = [&](int u, int slot_u, f32x16& S, f32x16& Sn) {
+        const int SL = slot_u;  // u % NS
+        const int kv0 = T.kv_begin + C::UK * u;
+        // V of unit u + 1 (landed and made visible by the last barrier) goes to fp16
+        // before the next barrier; past the last unit this converts a slot no one reads
+        // again
+        u32x4 vcv[IPW];
+        v_fp16_read(ring(SL + 1), vcv);
         // mask (boundary units only)
-        if ((kv0 + 32 > T.kv_len) || (A.causal && kv0 + 31 > wpos_min)) {
+        if ((kv0 + C::UK > T.kv_len) || (A.causal && kv0 + C::UK - 1 > wpos_min)) {
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kv0 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    if (key >= T.kv_len || (A.causal && key > pos[c])) S[c][r] = -INFINITY;
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + 8 * (r >> 2) + 4 * half + (r & 3);
+                if (key >= T.kv_len || (A.causal && key > pos)) S[r] = -INFINITY;
+            }
         }
         // row max of the raw scores; lazy rescaling (see kLazy)
-        bool any_upd = false;
-        float bx[NC];
+        float bmax = -INFINITY;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            float bmax = -INFINITY;
+        for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, S[r]);
+        bmax = fmaxf(bmax, xor32(bmax));
+        const float bx = bmax * A.c_log2;
+        if (__builtin_amdgcn_ballot_w64(bx > m_run + kLazy)) {
+            const float m_new = bx > m_run + kLazy ? bx : m_run;
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            lsum *= alpha;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, S[c][r]);
-            bmax = fmaxf(bmax, xor32(bmax));
-            bx[c] = bmax * A.c_log2;
-            any_upd |= bx[c] > m[c] + kLazy;
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
         }
-        if (__builtin_amdgcn_ballot_w64(any_upd)) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const float m_new = bx[c] > m[c] + kLazy ? bx[c] : m[c];
-                const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[c] - m_new);
-                m[c] = m_new;
-                lsum[c] *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) oacc[db][c] *= alpha;
-            }
-        }
-        float nm[NC];
-#pragma unroll
-        for (int c = 0; c < NC; ++c) nm[c] = m[c] == -INFINITY ? 0.f : -m[c];
+        const float nm = m_run == -INFINITY ? 0.f : -m_run;
 
-        // ---- one basic block: Q K^T (next unit) | exponentials | P V | stage ----
-        if (SBI + 1 < SB) qk(st_j, SBI + 1, Sn);
-        else qk(st_j1, 0, Sn);
-        u32x4 pf[NC][2];
+        // request unit u + NS - 1 into the slot unit u - 1 has left
+        const bool more_req = u + NS - 1 < nunits;
+        if (more_req) {
+            const int sr = ring(SL + NS - 1);
+            const int bad = load_unit(sr, pg_next);
+            bad_slots = (bad_slots & ~(((1 << IPW) - 1) << (sr * IPW))) | (bad << (sr * IPW));
+        }
+        v_fp16_write(ring(SL + 1), vcv);
+
+        // ---- one basic block: Q K^T (next unit) | exponentials | P V ----
+        qk(ring(SL + 1), Sn);
+        u32x4 pf[2];
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int e = 0; e < 4; ++e) {
+                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * h + 2 * e], A.c_log2, nm));
+                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * h + 2 * e + 1], A.c_log2, nm));
+                const fp16x2 ph = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+                lsum = __builtin_amdgcn_fdot2(ph, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum, false);
+                pf[h][e] = __builtin_bit_cast(uint32_t, ph);
+            }
+        const char* vp = smem + SL * SLOT + v_lane;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const fp16x2 ph = __builtin_amdgcn_cvt_pkrtz(
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(S[c][8 * h + 2 * e], A.c_log2, nm[c])),
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(S[c][8 * h + 2 * e + 1], A.c_log2, nm[c])));
-                    lsum[c] = __builtin_amdgcn_fdot2(ph, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum[c], false);
-                    pf[c][h][e] = __builtin_bit_cast(uint32_t, ph);
-                }
-        const uint16_t* st_base = lds + st_j * STAGE;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int kc = 2 * SBI + h;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int vk = (kc ^ (2 * (db & 1))) & 3;  // (2kc ^ 4(db & 1)) / 2 within 4 chunks
-                const u32x4 vf = *(const u32x4*)(st_base + v_off[vk] + 32 * db * BN + 16 * (kc & ~3));
-#pragma unroll
-                for (int c = 0; c < NC; ++c) oacc[db][c] = mfma_pv(vf, pf[c][h], oacc[db][c]);
+                const u32x2 lo = ds_read_tr16((const uint16_t*)(vp + ((16 * h) / R) * GS + 64 * R * db));
+                const u32x2 hi = ds_read_tr16((const uint16_t*)(vp + ((16 * h + 8) / R) * GS + 64 * R * db));
+                const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
+                oacc[db] = mfma_pv(va, pf[h], oacc[db]);
             }
-        }
         // scheduling hint for this basic block: the compiler's MFMA / LDS-read
-        // interleave for single-wave small GEMMs (measured: 2.8% faster here)
+        // interleave for single-wave small GEMMs
         __builtin_amdgcn_iglp_opt(1);
-        if (SBI == 0) {
-            stage(st_j1);
-            const int kvb = T.kv_begin + j * BN;
-            if (kvb + 2 * BN < T.kv_end) gather(kvb + 2 * BN);
-            __syncthreads();
+
+        // pages of unit u + NS (their latency overlaps the wait below)
+        if (u + NS < nunits) pages_of(u + NS, pg_next);
+        // unit u + 2 must be in LDS (and slot SL free) before unit u + 1 starts
+        if (u + 2 < nunits) {
+            sync_unit(u + 2, ring(SL + 2), NS == 4 && more_req);
+            barrier();
         }
-        if (SBI == SB - 1) __syncthreads();
     };
 
-    // ---- prologue: block 0 staged, block 1 in flight, scores of unit 0 ----
-    const int nblk = (T.kv_end - T.kv_begin + BN - 1) / BN;
-    load_page(T.kv_begin);
-    gather(T.kv_begin);
-    stage(0);
-    if (nblk > 1) gather(T.kv_begin + BN);
-    __syncthreads();
-    f32x16 sa[NC], sb_[NC];
-    qk(0, 0, sa);
-    int st0 = 0;  // stage of block j; block j+1 goes to 1 - st0
-    for (int j = 0; j < nblk; ++j) {
-        unit(std::integral_constant<int, 0>{}, j, st0, 1 - st0, sa, sb_);
-        unit(std::integral_constant<int, 1>{}, j, st0, 1 - st0, sb_, sa);
-        if constexpr (SB == 4) {
-            unit(std::integral_constant<int, 2>{}, j, st0, 1 - st0, sa, sb_);
-            unit(std::integral_constant<int, 3>{}, j, st0, 1 - st0, sb_, sa);
+    if (nunits > 0) {
+        // ---- prologue: units 0 .. NS-2 requested, 0 and 1 landed, scores of unit 0 ----
+        {
+            int pg[IPW];
+#pragma unroll
+            for (int t = 0; t < NS - 1; ++t)
+                if (t < nunits) {
+                    pages_of(t, pg);
+                    bad_slots |= load_unit(t, pg) << (t * IPW);
+                }
+            if (NS - 1 < nunits) pages_of(NS - 1, pg_next);
+            sync_unit(0, 0, NS == 4 && nunits > 1);
+            if (nunits > 1) sync_unit(1, 1, NS == 4 && nunits > 2);
+            u32x4 vcv[IPW];
+            v_fp16_read(0, vcv);
+            v_fp16_write(0, vcv);
+            barrier();
         }
-        st0 = 1 - st0;
+        f32x16 sa, sb;
+        qk(0, sa);
+        // (not unrolled: unrolled copies keep more registers live than the two waves
+        // per SIMD allow)
+        for (int u = 0, sl = 0; u < nunits; ++u, sl = ring(sl + 1)) {
+            unit(u, sl, sa, sb);
+            sa = sb;
+        }
     }
 
     // ---- epilogue ----
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const float ltot = lsum[c] + xor32(lsum[c]);
-        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-        const float lse_val = ltot > 0.f ? (m[c] + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
-        if (!row_ok[c]) continue;
-        const int row = wave * RW + 32 * c + col;
+    const float ltot = lsum + xor32(lsum);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const float lse_val = ltot > 0.f ? (m_run + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
+    if (row_ok) {
         if (T.part < 0) {
-            uint16_t* op = A.o + orow[c] * D + 4 * half;
+            uint16_t* op = A.o + orow * D + 4 * half;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     u32x2 w;
-                    w[0] = pack_out<BF16>(oacc[db][c][4 * jj + 0] * inv, oacc[db][c][4 * jj + 1] * inv);
-                    w[1] = pack_out<BF16>(oacc[db][c][4 * jj + 2] * inv, oacc[db][c][4 * jj + 3] * inv);
+                    w[0] = pack_out<BF16>(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
+                    w[1] = pack_out<BF16>(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
                     *(u32x2*)(op + 32 * db + 8 * jj) = w;
                 }
-            if (A.lse && half == 0) A.lse[orow[c]] = lse_val;
+            if (A.lse && half == 0) A.lse[orow] = lse_val;
         } else {
             float* pp = A.part_o + ((int64_t)T.part + row) * D + 4 * half;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
-                    f32x4 w = {oacc[db][c][4 * jj] * inv, oacc[db][c][4 * jj + 1] * inv,
-                               oacc[db][c][4 * jj + 2] * inv, oacc[db][c][4 * jj + 3] * inv};
+                    f32x4 w = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
+                               oacc[db][4 * jj + 3] * inv};
                     st_dev4(pp + 32 * db + 8 * jj, w);
                 }
             if (half == 0) st_dev(A.part_lse + T.part + row, lse_val);
@@ -1016,7 +1054,7 @@ void attn_narrow_valu_kernel(AttnArgs A) {
 
 // Wide tiles: two workgroups per CU (two waves per SIMD).
 template <int D, bool BF16>
-__global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(kWideWavesPerEU)))
 void attn_wide_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];

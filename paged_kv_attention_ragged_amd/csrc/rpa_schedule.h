@@ -24,8 +24,8 @@ constexpr int kValuKeys = 32;     // keys one wave handles per step on the VALU 
 constexpr int kXcds = 8;          // MI355X: workgroup i of a launch runs on XCD i % 8
 constexpr int kChunkKeys = 256;   // split pieces start at multiples of this many keys
 
-// Keys per inner block of the wide path: one K block plus one V block fill 16 KiB each.
-constexpr int block_n_for(int head_dim) { return 8192 / head_dim; }
+// Keys per inner block (unit) of the wide path, whatever the head_dim.
+constexpr int block_n_for(int) { return 32; }
 
 enum TileKind : int32_t {
     kWide = 0,    // up to 128 rows; 4 waves split the rows, walk keys together

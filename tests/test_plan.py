@@ -50,7 +50,7 @@ def check_schedule(b: W.Batch, plan):
     G = b.num_qo_heads // b.num_kv_heads
     TQ = info["tokens_per_tile"]
     BN = info["block_n"]
-    assert TQ == 128 // G and BN == 8192 // b.head_dim
+    assert TQ == 128 // G and BN == 32
     q_lens, kv_lens = b.q_lens, b.kv_lens
     # 1. every (sequence, kv head, token) appears in exactly one query tile, and each query
     #    tile's pieces cover [0, kv_end) exactly once, in order, block-aligned

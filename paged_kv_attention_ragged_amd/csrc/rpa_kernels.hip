@@ -325,8 +325,13 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     // Wave w loads groups m = w + 4j (j < IPW) of K and of V: rows R m .. R m + R - 1
     // of the unit, all in one page.  Lane l: row R m + l % R, chunk l / R.
     const int64_t ss = (int64_t)A.Hkv * D;  // elements between token slots
-    const char* kvh = reinterpret_cast<const char*>(A.kv + (int64_t)T.kv_head * D);
-    const uint32_t src_lane = (uint32_t)(((lane % R) * ss + 8 * (lane / R)) * 2);  // bytes
+    // The rows a wave's group takes within its page, (R m) % 16, do not depend on j
+    // (4R j is a multiple of 16): they go into the wave's base pointer and the lane
+    // offsets, so a load's address is base + page * page_bytes.
+    const char* kvw = reinterpret_cast<const char*>(A.kv + (int64_t)T.kv_head * D + ((R * wave) & 15) * ss);
+    const uint32_t page_bytes = (uint32_t)(32 * ss * 2);
+    const uint32_t k_src_lane = (uint32_t)(((lane % R) * ss + 8 * (lane / R)) * 2);  // bytes
+    const uint32_t v_src_lane = k_src_lane + (uint32_t)(16 * ss * 2);
     const int nunits = (T.kv_end - T.kv_begin + C::UK - 1) / C::UK;
     // Page of each of this wave's groups for one unit, read ahead (scalar loads, not
     // waited for here).  A group past kv_len reads page 0: its keys are masked and
@@ -339,40 +344,44 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             pg[j] = key0 < T.kv_len ? ((const_i32*)A.page_idx)[T.page_base + (key0 >> 4)] : 0;
         }
     };
-    // Request one unit into one slot; returns the bad-page bits (bit j: an index outside
-    // [0, num_pages), which raises the error flag and reads page 0, its keys zeroed).
-    const uint32_t lds0 = lds_addr(smem);
+    // Request one unit into one slot.  A page index outside [0, num_pages) raises the
+    // error flag and reads page 0; bad_any then sends every later unit through the
+    // slow check in fix_unit, which zeroes that page's keys.
+    const uint32_t lds_w = lds_addr(smem) + wave * GS;
+    int bad_any = 0;
     auto load_unit = [&](int slot, const int (&pg)[IPW]) {
-        int bad = 0;
 #pragma unroll
         for (int j = 0; j < IPW; ++j) {
             int p = pg[j];
             if ((unsigned)p >= (unsigned)A.num_pages) {
                 *A.err_flag = 1;
                 p = 0;
-                bad |= 1 << j;
+                bad_any = 1;
             }
-            const int m = wave + 4 * j;
-            const char* src = kvh + ((int64_t)p * 32 + ((R * m) & 15)) * ss * 2;
-            const uint32_t dst = lds0 + slot * SLOT + m * GS;
-            load_lds16(src, src_lane, dst);
-            load_lds16(src + 16 * ss * 2, src_lane, dst + MAT);
+            const char* src = kvw + (uint64_t)(uint32_t)p * page_bytes;
+            const uint32_t dst = lds_w + slot * SLOT + 4 * j * GS;
+            load_lds16(src, k_src_lane, dst);
+            load_lds16(src, v_src_lane, dst + MAT);
         }
-        return bad;
     };
     // After this wave's loads of unit t have landed: zero V of keys past kv_len, and K
     // and V of bad pages (each lane the 16 bytes it loaded).
-    auto fix_unit = [&](int t, int slot, int bad) {
+    auto fix_unit = [&](int t, int slot) {
         const int kv0 = T.kv_begin + C::UK * t;
-        if (bad == 0 && kv0 + C::UK <= T.kv_len) return;
+        if (!bad_any && kv0 + C::UK <= T.kv_len) return;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
         for (int j = 0; j < IPW; ++j) {
             const int m = wave + 4 * j;
-            char* p = smem + slot * SLOT + m * GS + 16 * lane;
-            const bool b = (bad >> j) & 1;
-            if (b) *(u32x4*)p = u32x4{0, 0, 0, 0};
-            if (b || kv0 + R * m + lane % R >= T.kv_len) *(u32x4*)(p + MAT) = u32x4{0, 0, 0, 0};
+            const int key0 = kv0 + R * m;
+            bool b = false;
+            if (bad_any && key0 < T.kv_len) {
+                const int p = ((const_i32*)A.page_idx)[T.page_base + (key0 >> 4)];
+                b = (unsigned)p >= (unsigned)A.num_pages;
+            }
+            char* q = smem + slot * SLOT + m * GS + 16 * lane;
+            if (b) *(u32x4*)q = u32x4{0, 0, 0, 0};
+            if (b || key0 + lane % R >= T.kv_len) *(u32x4*)(q + MAT) = u32x4{0, 0, 0, 0};
         }
     };
 
@@ -422,7 +431,6 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     };
 
     int pg_next[IPW];   // pages of the next unit to request
-    int bad_slots = 0;  // bad-page bits of the units in the ring, IPW per slot
     auto sync_unit = [&](int t, int slot, bool newer_in_flight) {
         // wait for this wave's loads of unit t (one younger unit's may stay in flight)
         if (newer_in_flight) {
@@ -431,7 +439,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        fix_unit(t, slot, (bad_slots >> (slot * IPW)) & ((1 << IPW) - 1));
+        fix_unit(t, slot);
     };
     auto barrier = [&]() {
         __builtin_amdgcn_sched_barrier(0);
@@ -479,9 +487,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         // request unit u + NS - 1 into the slot unit u - 1 has left
         const bool more_req = u + NS - 1 < nunits;
         if (more_req) {
-            const int sr = ring(SL + NS - 1);
-            const int bad = load_unit(sr, pg_next);
-            bad_slots = (bad_slots & ~(((1 << IPW) - 1) << (sr * IPW))) | (bad << (sr * IPW));
+            load_unit(ring(SL + NS - 1), pg_next);
         }
         v_fp16_write(ring(SL + 1), vcv);
 
@@ -529,7 +535,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             for (int t = 0; t < NS - 1; ++t)
                 if (t < nunits) {
                     pages_of(t, pg);
-                    bad_slots |= load_unit(t, pg) << (t * IPW);
+                    load_unit(t, pg);
                 }
             if (NS - 1 < nunits) pages_of(NS - 1, pg_next);
             sync_unit(0, 0, NS == 4 && nunits > 1);

@@ -269,3 +269,36 @@ def test_out_of_range_page_index_is_flagged_not_read():
         plan.check()
     assert e.value.status == "RPA_E_PAGE_OOB"
     plan.close()
+
+
+@pytest.mark.parametrize("head_dim,dtype", [(64, "f16"), (128, "bf16")])
+@pytest.mark.parametrize("splits", [1, 0])
+def test_out_of_range_page_reads_as_zero(head_dim, dtype, splits):
+    """The keys of a page whose index lies outside [0, num_pages) count as zero K and
+    V (and the flag is raised): the output equals the oracle's over a cache in which
+    that index names an all-zero page.  Sequence 0 takes the wide path (3 tokens x 8
+    heads), sequence 1 the narrow one (1 token); a middle page of each is bad."""
+    import paged_kv_attention_ragged_amd as rpa
+    b = W.make_batch("oobz", [3, 1], [100, 70], num_qo_heads=8, num_kv_heads=1, head_dim=head_dim,
+                     dtype=dtype, seed=39)
+    n_pages = b.kv_cache.shape[0]
+    bad_idx = b.kv_page_indices.copy()
+    for s in range(2):
+        bad_idx[int(b.kv_page_indptr[s]) + 2 - s] = n_pages  # one past the last page
+    # oracle: the same indices over a cache with one more page, all zeros
+    zero_page = torch.zeros((1,) + tuple(b.kv_cache.shape[1:]), dtype=b.kv_cache.dtype)
+    kw = b.oracle_kwargs()
+    kw.update(kv_page_indices=bad_idx, kv_cache=torch.cat([b.kv_cache, zero_page]))
+    say("oob zero: D=%d %s splits=%d" % (head_dim, dtype, splits))
+    ro, rl = oracle.run(**kw)
+    q, kv, _ = on_device(b)
+    plan = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=8, num_kv_heads=1,
+                    head_dim=head_dim, dtype=dtype, max_kv_splits=splits)
+    plan.bind(torch.from_numpy(bad_idx.astype(np.int32)).cuda(), num_pages=n_pages)
+    o, lse = plan.run(q, kv, return_lse=True)
+    torch.cuda.synchronize()
+    with pytest.raises(rpa.RPAError) as e:
+        plan.check()
+    assert e.value.status == "RPA_E_PAGE_OOB"
+    plan.close()
+    assert_close(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, what="bad page as zeros")

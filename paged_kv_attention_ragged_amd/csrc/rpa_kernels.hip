@@ -633,8 +633,8 @@ __device__ __forceinline__ void narrow_combine_store(const AttnArgs& A, const Ti
 }
 
 // Narrow tile (decode-like): at most 16 rows (q_count * G <= 16), all in one
-// 16-column MFMA block.  The 4 waves split the key range: wave w takes the 64-key
-// steps w, w+4, w+8, ... of [kv_begin, kv_end), each with its own running max,
+// 16-column MFMA block.  The 4 waves split the key range: wave w takes the
+// kWaveKeys-key steps w, w+4, w+8, ... of [kv_begin, kv_end), each with its own running max,
 // sum and O, and the waves are combined through LDS at the end.
 //   * K goes from the cache straight into the A operand of
 //     v_mfma_f32_16x16x32 (lane l: key 16b + l%16, 8 consecutive d), so only V
@@ -1068,9 +1068,11 @@ void attn_wide_kernel(AttnArgs A) {
     wide_tile<D, BF16>(A, T, smem);
 }
 
-// Narrow tiles: two workgroups per CU, so twice the loads in flight per CU.
+// Narrow tiles: three workgroups per CU (32-key wave steps keep the kernel within
+// the 168 registers and 53 KiB of LDS that allows), so more tiles' loads are in
+// flight per CU.
 template <int D, bool BF16>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_narrow_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];

@@ -18,7 +18,7 @@ constexpr int kWideWaves = 4;  // wavefronts per wide-tile workgroup, 32 query r
 constexpr int block_m_for(int head_dim) { return head_dim > 0 ? 32 * kWideWaves : 32 * kWideWaves; }
 
 constexpr int kNarrowRows = 16;  // tiles with at most this many rows take the narrow path
-constexpr int kWaveKeys = 64;     // keys one wave handles per step on the narrow path
+constexpr int kWaveKeys = 32;     // keys one wave handles per step on the narrow path
 constexpr int kValuRows = 8;      // narrow threshold when narrow tiles run on the VALU kernel
 constexpr int kValuKeys = 32;     // keys one wave handles per step on the VALU narrow path
 constexpr int kXcds = 8;          // MI355X: workgroup i of a launch runs on XCD i % 8

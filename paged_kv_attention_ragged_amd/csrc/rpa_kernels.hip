@@ -431,15 +431,27 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     };
 
     int pg_next[IPW];   // pages of the next unit to request
-    auto sync_unit = [&](int t, int slot, bool newer_in_flight) {
-        // wait for this wave's loads of unit t (one younger unit's may stay in flight)
-        if (newer_in_flight) {
-            if constexpr (IPW == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    auto sync_unit = [&](int t, int slot, int younger) {
+        // wait for this wave's loads of unit t; those of the `younger` units requested
+        // after it (2 IPW loads each) may stay in flight
+        switch (younger * 2 * IPW) {
+            case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+            case 2: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+            case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+            case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+            case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+            case 10: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+            case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+            case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+            case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+            default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
         }
         fix_unit(t, slot);
+    };
+    // units requested after unit t, up to unit last_req (the newest requested so far)
+    auto younger_than = [&](int t, int last_req) {
+        const int newest = last_req < nunits - 1 ? last_req : nunits - 1;
+        return newest > t ? newest - t : 0;
     };
     auto barrier = [&]() {
         __builtin_amdgcn_sched_barrier(0);
@@ -522,7 +534,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         if (u + NS < nunits) pages_of(u + NS, pg_next);
         // unit u + 2 must be in LDS (and slot SL free) before unit u + 1 starts
         if (u + 2 < nunits) {
-            sync_unit(u + 2, ring(SL + 2), NS == 4 && more_req);
+            sync_unit(u + 2, ring(SL + 2), younger_than(u + 2, u + NS - 1));
             barrier();
         }
     };
@@ -538,8 +550,8 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
                     load_unit(t, pg);
                 }
             if (NS - 1 < nunits) pages_of(NS - 1, pg_next);
-            sync_unit(0, 0, NS == 4 && nunits > 1);
-            if (nunits > 1) sync_unit(1, 1, NS == 4 && nunits > 2);
+            sync_unit(0, 0, younger_than(1, NS - 2));
+            if (nunits > 1) sync_unit(1, 1, younger_than(1, NS - 2));
             u32x4 vcv[IPW];
             v_fp16_read(0, vcv);
             v_fp16_write(0, vcv);

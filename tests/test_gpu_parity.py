@@ -62,7 +62,7 @@ def test_ragged_shapes(shape):
                          ids=lambda s: "h%d_kv%d_d%d_%s" % s)
 def test_narrow_tiles(shape):
     """Tiles of at most 16 rows take the decode path: multi-token causal rows (q_len * G
-    <= 16), several 64-key steps per wave, key ranges that end mid-step and mid-page."""
+    <= 16), several key steps per wave, key ranges that end mid-step and mid-page."""
     H, Hk, D, dt = shape
     G = H // Hk
     tq = max(1, 16 // G)
@@ -74,6 +74,21 @@ def test_narrow_tiles(shape):
     for splits, cus in ((1, 0), (0, 0), (0, 4096)):
         o, l, info = run(b, max_kv_splits=splits, num_cus=cus)
         assert_close(o, l, ro, rl, what="narrow %s splits=%d cus=%d" % (shape, splits, cus))
+
+
+@pytest.mark.parametrize("head_dim,dtype,causal", [(128, "bf16", True), (128, "f16", False), (64, "bf16", True),
+                                                    (64, "f16", False)])
+def test_wide_tiles_at_unit_boundaries(head_dim, dtype, causal):
+    """Wide tiles (3..40 tokens x 8 heads) whose key ranges end just before, on and
+    just after a 32-key unit and a 16-key page, for 1 to 5 units per tile, over a
+    cache whose unowned slots hold NaN (the slots past kv_len must read as zero V)."""
+    lens = [3, 17, 31, 32, 33, 40, 63, 64, 65, 97, 128, 130, 160]
+    b = W.make_batch("unitb", lens, lens, num_qo_heads=8, num_kv_heads=1, head_dim=head_dim, dtype=dtype,
+                     seed=41, spare_pages=4, poison=True, causal=causal)
+    ro, rl = ref(b)
+    for splits in (1, 0):
+        o, l, _ = run(b, max_kv_splits=splits)
+        assert_close(o, l, ro, rl, what="unit boundaries D%d %s splits=%d" % (head_dim, dtype, splits))
 
 
 def test_64k_token_sequences_sampled():

@@ -271,6 +271,10 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
         rpa::LaunchAttn N = L;
         N.a.tiles = L.a.tiles + S.wide_tiles;
         N.n_tiles = S.narrow_tiles;
+        // Split key ranges put each tile's last step on the latency-critical path of the
+        // merge, where the extra LDS round trip of row-wise K loads costs more than their
+        // better coalescing gains; unsplit (many-tile) decode is throughput-bound.
+        N.k_rows = !S.narrow_split;
         e = P.narrow_kernel == 1 ? rpa::launch_narrow_valu(N, S.narrow_max_rows, st, e1.a, e1.b)
                                  : rpa::launch_narrow(N, st, e1.a, e1.b);
         if (e != hipSuccess) return hip_err(e, "narrow attention kernel launch");

@@ -271,6 +271,7 @@ template <int D>
 struct NarrowLds {
     static constexpr int KW = kWaveKeys;  // keys per wave step
     static constexpr int VS = D + 16;     // V row stride (elements), 32-byte pad
+    static constexpr int KS = D + 8;      // K row stride (elements), 16-byte pad (shares V's area)
     static constexpr int stage_bytes = kWaves * KW * VS * 2;
     static constexpr int combine_bytes = kWaves * 16 * (D + 4) * 4 + 2 * kWaves * 16 * 4;
     static constexpr int bytes = stage_bytes > combine_bytes ? stage_bytes : combine_bytes;
@@ -648,9 +649,10 @@ __device__ __forceinline__ void narrow_combine_store(const AttnArgs& A, const Ti
 // 16-column MFMA block.  The 4 waves split the key range: wave w takes the
 // kWaveKeys-key steps w, w+4, w+8, ... of [kv_begin, kv_end), each with its own running max,
 // sum and O, and the waves are combined through LDS at the end.
-//   * K goes from the cache straight into the A operand of
-//     v_mfma_f32_16x16x32 (lane l: key 16b + l%16, 8 consecutive d), so only V
-//     passes through LDS;
+//   * K is loaded in whole rows (each load instruction reads KPJ complete rows)
+//     and passed through the wave's LDS area into the A operand of
+//     v_mfma_f32_16x16x32 (lane l: key 16b + l%16, 8 consecutive d): loads that
+//     touched 16 half rows each made shared-prefix decode 14% slower;
 //   * V is staged in its natural [key][d] layout (fp16; bf16 is converted on the
 //     way) and read back transposed with ds_read_b64_tr_b16: within each 16-lane
 //     group, lane j receives element j%4 of the 8-byte rows addressed by lanes
@@ -658,10 +660,11 @@ __device__ __forceinline__ void narrow_combine_store(const AttnArgs& A, const Ti
 //     one d per lane -- the V^T operand layout;
 //   * S^T = K Q^T gives each lane one row (column l%16) and 4 consecutive keys per
 //     16-key block; the running max needs two cross-lane exchanges per step.
-template <int D, bool BF16>
+template <int D, bool BF16, bool KROWS>
 __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, char* smem) {
     constexpr int KW = NarrowLds<D>::KW;  // keys per wave step
     constexpr int VS = NarrowLds<D>::VS;  // V staging row stride (elements)
+    constexpr int KS = NarrowLds<D>::KS;  // K staging row stride (elements)
     constexpr int DK = D / 32;            // 32-d k-steps of Q K^T
     constexpr int DB = D / 16;            // 16-d blocks of O^T
     constexpr int CH = D / 8;             // 16-byte chunks per row
@@ -697,10 +700,11 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
 
     const int64_t ss = (int64_t)A.Hkv * D;  // elements between token slots
     const uint16_t* kvh = A.kv + (int64_t)T.kv_head * D;
-    const int vkey = lane / CH, vch = lane % CH;  // V gather: key j*KPJ + vkey, chunk vch
+    const int vkey = lane / CH, vch = lane % CH;  // K/V gather: key j*KPJ + vkey, chunk vch
 
-    // Gathers for one step at key `kb0`: page ids, then K into MFMA-layout registers and
-    // V into natural-layout registers.  Keys at or past kv_len read as zero.
+    // Gathers for one step at key `kb0`: page ids, then K and V into natural-layout
+    // registers (each load instruction reads KPJ whole rows).  Keys at or past kv_len
+    // read as zero.
     int pages[KB];
     auto load_pages = [&](int kb0) {
 #pragma unroll
@@ -716,15 +720,28 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
             pages[b] = pg;
         }
     };
-    u32x4 kf[KB][DK];
+    u32x4 kr[VJ];      // K rows (KROWS)
+    u32x4 kf[KB][DK];  // K in MFMA operand layout
     u32x4 vf[VJ];
     auto load_k = [&](int kb0) {
+        if constexpr (KROWS) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            const bool ok = pages[b] >= 0 && kb0 + 16 * b + col < T.kv_len;
-            const uint16_t* src = kvh + ((int64_t)pages[b] * 32 + col) * ss + 8 * grp;
+            for (int j = 0; j < VJ; ++j) {
+                const int key = j * KPJ + vkey;
+                const int pg = pages[(j * KPJ) >> 4];
+                const bool ok = pg >= 0 && kb0 + key < T.kv_len;
+                kr[j] = ok ? *(const u32x4*)(kvh + ((int64_t)pg * 32 + (key & 15)) * ss + 8 * vch)
+                           : u32x4{0, 0, 0, 0};
+            }
+        } else {
 #pragma unroll
-            for (int kk = 0; kk < DK; ++kk) kf[b][kk] = ok ? *(const u32x4*)(src + 32 * kk) : u32x4{0, 0, 0, 0};
+            for (int b = 0; b < KB; ++b) {
+                const bool ok = pages[b] >= 0 && kb0 + 16 * b + col < T.kv_len;
+                const uint16_t* src = kvh + ((int64_t)pages[b] * 32 + col) * ss + 8 * grp;
+#pragma unroll
+                for (int kk = 0; kk < DK; ++kk)
+                    kf[b][kk] = ok ? *(const u32x4*)(src + 32 * kk) : u32x4{0, 0, 0, 0};
+            }
         }
     };
     auto load_v = [&](int kb0) {
@@ -750,6 +767,18 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     for (; kbase < T.kv_end; kbase += STRIDE) {
         const int knext = kbase + STRIDE;
         const bool more = knext < T.kv_end;
+
+        // ---- (KROWS) K through the wave's LDS area: rows in, MFMA operands out (lane:
+        // key 16b + col, d = 32kk + 8grp .. +8); V reuses the area after Q K^T ----
+        if constexpr (KROWS) {
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) *(u32x4*)(v_lds + (j * KPJ + vkey) * KS + 8 * vch) = kr[j];
+#pragma unroll
+            for (int b = 0; b < KB; ++b)
+#pragma unroll
+                for (int kk = 0; kk < DK; ++kk)
+                    kf[b][kk] = *(const u32x4*)(v_lds + (16 * b + col) * KS + 8 * grp + 32 * kk);
+        }
 
         // ---- S^T = K Q^T ----
         f32x4 s[KB];
@@ -1083,13 +1112,13 @@ void attn_wide_kernel(AttnArgs A) {
 // Narrow tiles: three workgroups per CU (32-key wave steps keep the kernel within
 // the 168 registers and 53 KiB of LDS that allows), so more tiles' loads are in
 // flight per CU.
-template <int D, bool BF16>
+template <int D, bool BF16, bool KROWS>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_narrow_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];
     if (T.q_count <= 0) return;
-    narrow_tile<D, BF16>(A, T, smem);
+    narrow_tile<D, BF16, KROWS>(A, T, smem);
 }
 
 // ---- host-side launchers -----------------------------------------------------------------
@@ -1201,13 +1230,17 @@ hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, 
                   : launch_with_lds<&attn_wide_kernel<64, false>>(L, WideCfg<64>::bytes, kWideWaves * 64, stream, ev0, ev1);
 }
 
+template <int D, bool BF16>
+hipError_t launch_narrow_d(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    return L.k_rows ? launch_with_lds<&attn_narrow_kernel<D, BF16, true>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1)
+                    : launch_with_lds<&attn_narrow_kernel<D, BF16, false>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1);
+}
+
 hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     if (L.n_tiles <= 0) return hipSuccess;
     if (L.head_dim == 128)
-        return L.bf16 ? launch_with_lds<&attn_narrow_kernel<128, true>>(L, NarrowLds<128>::bytes, kWaves * 64, stream, ev0, ev1)
-                      : launch_with_lds<&attn_narrow_kernel<128, false>>(L, NarrowLds<128>::bytes, kWaves * 64, stream, ev0, ev1);
-    return L.bf16 ? launch_with_lds<&attn_narrow_kernel<64, true>>(L, NarrowLds<64>::bytes, kWaves * 64, stream, ev0, ev1)
-                  : launch_with_lds<&attn_narrow_kernel<64, false>>(L, NarrowLds<64>::bytes, kWaves * 64, stream, ev0, ev1);
+        return L.bf16 ? launch_narrow_d<128, true>(L, stream, ev0, ev1) : launch_narrow_d<128, false>(L, stream, ev0, ev1);
+    return L.bf16 ? launch_narrow_d<64, true>(L, stream, ev0, ev1) : launch_narrow_d<64, false>(L, stream, ev0, ev1);
 }
 
 template <int D, bool BF16>

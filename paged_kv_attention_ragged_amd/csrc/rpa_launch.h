@@ -29,6 +29,8 @@ struct LaunchAttn {
     int head_dim;
     bool bf16;
     int64_t n_tiles;
+    bool k_rows;      // narrow kernel: K loaded in whole rows through LDS (else straight into
+                      // MFMA operand layout)
 };
 
 

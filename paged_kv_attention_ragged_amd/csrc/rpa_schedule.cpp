@@ -227,6 +227,7 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
             if (t.kind == kNarrow) {
                 ++S.narrow_tiles;
                 S.narrow_max_rows = std::max(S.narrow_max_rows, t.q_count * G);
+                if (ns > 1) S.narrow_split = true;
             }
             // cost ~ keys walked (wide tiles: rounded up to whole blocks) plus a fixed overhead
             const int64_t gran = t.kind == kWide ? BN : (p.narrow_valu ? kValuKeys : kWaveKeys);

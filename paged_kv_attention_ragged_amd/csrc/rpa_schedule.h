@@ -83,6 +83,7 @@ struct Schedule {
     int32_t max_splits = 1;
     int64_t narrow_tiles = 0;
     int32_t narrow_max_rows = 0;  // largest row count among narrow tiles
+    bool narrow_split = false;    // some narrow tile's key range is split into pieces
     int64_t total_q = 0;
     int64_t visible_pairs = 0;  // per qo head, summed over heads
     int64_t kv_tokens = 0;

@@ -9,8 +9,9 @@
 //                       loaded straight from the cache into an LDS ring, a
 //                       software pipeline over the units (see wide_tile);
 //   attn_narrow_kernel  tiles of up to 16 rows (decode-like): the 4 waves split
-//                       the keys, v_mfma_f32_16x16x32, K straight into MFMA
-//                       registers, V read back transposed (see narrow_tile);
+//                       the keys, v_mfma_f32_16x16x32, K into MFMA registers
+//                       directly or in whole rows through LDS, V read back
+//                       transposed (see narrow_tile);
 //   attn_narrow_valu_kernel  the same tiles (up to 8 rows) without MFMA, on dot2
 //                       and fp32 FMAs, for comparison (see valu_tile);
 //   merge_states_kernel join of two attention states (cascade halves);

@@ -252,12 +252,12 @@ def time_fn(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def bound_plan(b, narrow="mfma"):
+def bound_plan(b, narrow="mfma", kv_shared=False):
     import torch
     import paged_kv_attention_ragged_amd as rpa
     p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
                  num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal,
-                 narrow_kernel=narrow)
+                 narrow_kernel=narrow, kv_shared=kv_shared)
     p.bind(torch.from_numpy(b.kv_page_indices).cuda(), num_pages=b.kv_cache.shape[0])
     return p
 
@@ -272,8 +272,8 @@ def bench_secondary(args):
     steps = max(5, args.steps // 10)
     out = {}
 
-    def direct(b, rotate=1, narrow="mfma"):
-        p = bound_plan(b, narrow)
+    def direct(b, rotate=1, narrow="mfma", kv_shared=False):
+        p = bound_plan(b, narrow, kv_shared)
         q, kv0 = b.q.cuda(), b.kv_cache.cuda()
         kvs = [kv0] + [kv0.clone() for _ in range(rotate - 1)]
         o = torch.empty_like(q)
@@ -316,7 +316,7 @@ def bench_secondary(args):
     pre_direct, inf = direct(b)
     pre_cascade = cascade(b, 200)
     d = W.decode_step(b, 1)
-    dec_direct, inf_d = direct(d, rotate=6)
+    dec_direct, inf_d = direct(d, rotate=6, kv_shared=True)  # 12 pages shared by all requests
     dec_cascade = cascade(d, 200)
     logical = float(inf_d["kv_tokens"]) * d.num_kv_heads * d.head_dim * 4
     out["shared_prefix"] = {"suffix_prefill_direct_ms": pre_direct, "suffix_prefill_cascade_ms": pre_cascade,
@@ -326,7 +326,7 @@ def bench_secondary(args):
     # a long shared prefix (4096 tokens) under the same 256 requests: one decode step
     log("long shared prefix decode: direct vs cascade")
     lb = W.decode_step(W.shared_prefix_suffix(prefix=4096, decode_steps=1), 1)
-    ld_direct, inf_l = direct(lb)
+    ld_direct, inf_l = direct(lb, kv_shared=True)
     ld_cascade = cascade(lb, 4096)
     out["long_prefix_4096"] = {"decode_step_direct_ms": ld_direct, "decode_step_cascade_ms": ld_cascade,
                                "logical_kv_gb": float(inf_l["kv_tokens"]) * lb.num_kv_heads * lb.head_dim * 4 / 1e9}
@@ -341,7 +341,8 @@ def bench_secondary(args):
     m_ms, _ = direct(db, rotate=8)
     out["decode_b128_kv1024_valu_vs_mfma"] = {"valu_ms": v_ms, "mfma_ms": m_ms}
     del db
-    out["shared_prefix"]["decode_step_valu_ms"] = direct(d, rotate=6, narrow="valu")[0]
+    out["shared_prefix"]["decode_step_valu_ms"] = direct(d, rotate=6, narrow="valu", kv_shared=True)[0]
+    out["shared_prefix"]["decode_step_streamed_kv_ms"] = direct(d, rotate=6)[0]  # without the hint
     # mixed long batch: its decode rows alone and the whole batch in one call
     log("mixed long batch: decode rows, whole batch")
     for part in ("decode", "all"):
@@ -409,7 +410,7 @@ def bench_decode_loop(steps=50):
     for i in range(steps):
         d = load(i)
         p = rpa.Plan(d.qo_indptr, d.kv_page_indptr, d.kv_last_page_len, num_qo_heads=H, num_kv_heads=Hk,
-                     head_dim=D, dtype=d.dtype)
+                     head_dim=D, dtype=d.dtype, kv_shared=True)
         p.bind(ix_buf, num_pages=kv.shape[0])
         rpa.append_kv(new_buf, kv, ai_buf, ip_buf, ix_buf, kl_buf)
         p.run(q_buf, kv, out=o_buf, lse=l_buf, return_lse=True)
@@ -420,7 +421,7 @@ def bench_decode_loop(steps=50):
     kv = kv0.clone()
     d = load(0)
     plan = rpa.Plan(d.qo_indptr, d.kv_page_indptr, d.kv_last_page_len, num_qo_heads=H, num_kv_heads=Hk,
-                    head_dim=D, dtype=d.dtype)
+                    head_dim=D, dtype=d.dtype, kv_shared=True)
     plan.bind(ix_buf, num_pages=kv.shape[0])
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()

@@ -79,6 +79,14 @@ typedef struct {
     int32_t narrow_kernel;  /* decode-like tiles: 0 MFMA kernel (up to 16 rows per
                                tile), 1 VALU kernel without MFMA (up to 8 rows;
                                the design of the pages' CUDA-core decode)        */
+    int32_t kv_shared;      /* 0: each cache page is read by one sequence (no
+                               shared prefix): decode-like tiles load K/V as
+                               non-temporal streams that do not displace the
+                               caches; 1: pages may be shared by several
+                               sequences (a common prefix, vLLM issue #227):
+                               K/V loads stay cacheable so sequences reading the
+                               same page together hit in L2.  A caching hint
+                               only: results are bitwise the same either way. */
 } rpa_params;
 
 typedef struct rpa_plan rpa_plan;

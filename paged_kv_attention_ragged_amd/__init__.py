@@ -44,7 +44,7 @@ class _Params(ctypes.Structure):
     _fields_ = [("num_qo_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("causal", ctypes.c_int32), ("sm_scale", ctypes.c_float), ("max_kv_splits", ctypes.c_int32),
-                ("num_cus", ctypes.c_int32), ("narrow_kernel", ctypes.c_int32)]
+                ("num_cus", ctypes.c_int32), ("narrow_kernel", ctypes.c_int32), ("kv_shared", ctypes.c_int32)]
 
 
 class _Info(ctypes.Structure):
@@ -142,7 +142,7 @@ class Plan:
     def __init__(self, qo_indptr, kv_page_indptr, kv_last_page_len, *, num_qo_heads: int, num_kv_heads: int,
                  head_dim: int, page_size: int = 16, dtype="f16", causal: bool = True,
                  sm_scale: Optional[float] = None, max_kv_splits: int = 0, num_cus: int = 0,
-                 narrow_kernel: str = "mfma"):
+                 narrow_kernel: str = "mfma", kv_shared: bool = False):
         lib = load()
         self._qo = _host_i32(qo_indptr)
         self._kp = _host_i32(kv_page_indptr)
@@ -150,7 +150,8 @@ class Plan:
         self.batch = len(self._qo) - 1
         self.params = _Params(num_qo_heads, num_kv_heads, head_dim, page_size, _dtype_code(dtype),
                               1 if causal else 0, 0.0 if sm_scale is None else float(sm_scale),
-                              max_kv_splits, num_cus, {"mfma": 0, "valu": 1}[narrow_kernel])
+                              max_kv_splits, num_cus, {"mfma": 0, "valu": 1}[narrow_kernel],
+                              1 if kv_shared else 0)
         h = ctypes.c_void_p()
         p = lambda a: a.ctypes.data if a.size else None
         _check(lib.rpa_plan_create(ctypes.byref(self.params), self.batch, p(self._qo), p(self._kp), p(self._kl),

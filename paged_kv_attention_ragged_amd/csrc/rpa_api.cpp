@@ -86,6 +86,7 @@ rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_
     if (!std::isfinite(params->sm_scale)) return set_err(RPA_E_ARG, "sm_scale must be finite");
     if (params->narrow_kernel != 0 && params->narrow_kernel != 1)
         return set_err(RPA_E_ARG, "narrow_kernel must be 0 (MFMA) or 1 (VALU)");
+    if (params->kv_shared != 0 && params->kv_shared != 1) return set_err(RPA_E_ARG, "kv_shared must be 0 or 1");
     rpa::PlanParams pp{params->num_qo_heads, params->num_kv_heads, params->head_dim, params->page_size,
                        params->causal, params->max_kv_splits, params->num_cus, params->narrow_kernel};
     rpa_plan* plan = new (std::nothrow) rpa_plan();
@@ -275,6 +276,9 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
         // merge, where the extra LDS round trip of row-wise K loads costs more than their
         // better coalescing gains; unsplit (many-tile) decode is throughput-bound.
         N.k_rows = !S.narrow_split;
+        // Pages read by one sequence only are streamed past L2 (non-temporal), which
+        // keeps the schedule, page indices and Q resident; shared pages stay cached.
+        N.kv_stream = P.kv_shared == 0;
         e = P.narrow_kernel == 1 ? rpa::launch_narrow_valu(N, S.narrow_max_rows, st, e1.a, e1.b)
                                  : rpa::launch_narrow(N, st, e1.a, e1.b);
         if (e != hipSuccess) return hip_err(e, "narrow attention kernel launch");

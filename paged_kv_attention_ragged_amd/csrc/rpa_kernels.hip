@@ -11,7 +11,8 @@
 //   attn_narrow_kernel  tiles of up to 16 rows (decode-like): the 4 waves split
 //                       the keys, v_mfma_f32_16x16x32, K into MFMA registers
 //                       directly or in whole rows through LDS, V read back
-//                       transposed (see narrow_tile);
+//                       transposed (see narrow_tile); K/V loads non-temporal
+//                       unless the caller says pages are shared by sequences;
 //   attn_narrow_valu_kernel  the same tiles (up to 8 rows) without MFMA, on dot2
 //                       and fp32 FMAs, for comparison (see valu_tile);
 //   merge_states_kernel join of two attention states (cascade halves);
@@ -102,6 +103,15 @@ __device__ __forceinline__ void load_lds16(const void* sbase, uint32_t lane_off,
 // 32-bit LDS address of a pointer into the workgroup's shared memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// 16 bytes of K or V from the cache.  NT: a non-temporal (streaming) load, for
+// pages that no other tile of the launch reads -- it does not displace the L2
+// lines of the schedule, page indices and Q that every workgroup reads first.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_kv(const uint16_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return *reinterpret_cast<const u32x4*>(p);
 }
 
 // Two fp32 -> packed 16-bit, round to nearest-even.
@@ -661,7 +671,7 @@ __device__ __forceinline__ void narrow_combine_store(const AttnArgs& A, const Ti
 //     one d per lane -- the V^T operand layout;
 //   * S^T = K Q^T gives each lane one row (column l%16) and 4 consecutive keys per
 //     16-key block; the running max needs two cross-lane exchanges per step.
-template <int D, bool BF16, bool KROWS>
+template <int D, bool BF16, bool KROWS, bool NT>
 __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, char* smem) {
     constexpr int KW = NarrowLds<D>::KW;  // keys per wave step
     constexpr int VS = NarrowLds<D>::VS;  // V staging row stride (elements)
@@ -731,7 +741,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
                 const int key = j * KPJ + vkey;
                 const int pg = pages[(j * KPJ) >> 4];
                 const bool ok = pg >= 0 && kb0 + key < T.kv_len;
-                kr[j] = ok ? *(const u32x4*)(kvh + ((int64_t)pg * 32 + (key & 15)) * ss + 8 * vch)
+                kr[j] = ok ? ld_kv<NT>(kvh + ((int64_t)pg * 32 + (key & 15)) * ss + 8 * vch)
                            : u32x4{0, 0, 0, 0};
             }
         } else {
@@ -741,7 +751,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
                 const uint16_t* src = kvh + ((int64_t)pages[b] * 32 + col) * ss + 8 * grp;
 #pragma unroll
                 for (int kk = 0; kk < DK; ++kk)
-                    kf[b][kk] = ok ? *(const u32x4*)(src + 32 * kk) : u32x4{0, 0, 0, 0};
+                    kf[b][kk] = ok ? ld_kv<NT>(src + 32 * kk) : u32x4{0, 0, 0, 0};
             }
         }
     };
@@ -751,7 +761,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
             const int key = j * KPJ + vkey;  // key within the step; its page is pages[key / 16]
             const int pg = pages[(j * KPJ) >> 4];
             const bool ok = pg >= 0 && kb0 + key < T.kv_len;
-            vf[j] = ok ? *(const u32x4*)(kvh + ((int64_t)pg * 32 + 16 + (key & 15)) * ss + 8 * vch)
+            vf[j] = ok ? ld_kv<NT>(kvh + ((int64_t)pg * 32 + 16 + (key & 15)) * ss + 8 * vch)
                        : u32x4{0, 0, 0, 0};
         }
     };
@@ -1113,13 +1123,13 @@ void attn_wide_kernel(AttnArgs A) {
 // Narrow tiles: three workgroups per CU (32-key wave steps keep the kernel within
 // the 168 registers and 53 KiB of LDS that allows), so more tiles' loads are in
 // flight per CU.
-template <int D, bool BF16, bool KROWS>
+template <int D, bool BF16, bool KROWS, bool NT>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_narrow_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];
     if (T.q_count <= 0) return;
-    narrow_tile<D, BF16, KROWS>(A, T, smem);
+    narrow_tile<D, BF16, KROWS, NT>(A, T, smem);
 }
 
 // ---- host-side launchers -----------------------------------------------------------------
@@ -1231,10 +1241,16 @@ hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, 
                   : launch_with_lds<&attn_wide_kernel<64, false>>(L, WideCfg<64>::bytes, kWideWaves * 64, stream, ev0, ev1);
 }
 
+template <int D, bool BF16, bool NT>
+hipError_t launch_narrow_nt(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    return L.k_rows ? launch_with_lds<&attn_narrow_kernel<D, BF16, true, NT>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1)
+                    : launch_with_lds<&attn_narrow_kernel<D, BF16, false, NT>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1);
+}
+
 template <int D, bool BF16>
 hipError_t launch_narrow_d(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-    return L.k_rows ? launch_with_lds<&attn_narrow_kernel<D, BF16, true>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1)
-                    : launch_with_lds<&attn_narrow_kernel<D, BF16, false>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1);
+    return L.kv_stream ? launch_narrow_nt<D, BF16, true>(L, stream, ev0, ev1)
+                       : launch_narrow_nt<D, BF16, false>(L, stream, ev0, ev1);
 }
 
 hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {

@@ -31,6 +31,7 @@ struct LaunchAttn {
     int64_t n_tiles;
     bool k_rows;      // narrow kernel: K loaded in whole rows through LDS (else straight into
                       // MFMA operand layout)
+    bool kv_stream;   // narrow kernel: K/V loads non-temporal (pages not shared by sequences)
 };
 
 

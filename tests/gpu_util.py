@@ -35,14 +35,15 @@ def on_device(b: W.Batch, device="cuda"):
 
 
 def run(b: W.Batch, max_kv_splits=0, num_cus=0, return_lse=True, sm_scale=None, dev=None, label="",
-        narrow_kernel="mfma"):
+        narrow_kernel="mfma", kv_shared=False):
     """(O float64 [T,H,D], LSE float64 [T,H] or None, plan info) from the HIP path."""
-    say("run %s %s splits=%d cus=%d T=%d narrow=%s" % (b.name, label, max_kv_splits, num_cus, b.total_q,
-                                                      narrow_kernel))
+    say("run %s %s splits=%d cus=%d T=%d narrow=%s kv_shared=%d" % (b.name, label, max_kv_splits, num_cus,
+                                                                    b.total_q, narrow_kernel, kv_shared))
     q, kv, idx = dev if dev is not None else on_device(b)
     plan = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
                     num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal,
-                    sm_scale=sm_scale, max_kv_splits=max_kv_splits, num_cus=num_cus, narrow_kernel=narrow_kernel)
+                    sm_scale=sm_scale, max_kv_splits=max_kv_splits, num_cus=num_cus, narrow_kernel=narrow_kernel,
+                    kv_shared=kv_shared)
     plan.bind(idx, num_pages=kv.shape[0])
     res = plan.run(q, kv, return_lse=return_lse)
     o, lse = res if return_lse else (res, None)

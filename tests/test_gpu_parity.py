@@ -190,6 +190,24 @@ def test_shared_prefix_suffix_prefill_and_decode_steps():
         if step in (1, 2, 17, 50):
             rro, rrl = ref(d)
             assert_close(o, l, rro, rrl, what="decode step %d" % step)
+            # cacheable K/V loads (the hint for shared pages) give the same bits
+            os_, ls_, _ = run(d, dev=dev, label="step %d kv_shared" % step, kv_shared=True)
+            assert np.array_equal(o, os_) and np.array_equal(l, ls_), "kv_shared changed step %d" % step
+
+
+@pytest.mark.parametrize("max_kv_splits", [0, 1])
+def test_kv_shared_hint_is_bitwise_neutral(max_kv_splits):
+    """The kv_shared caching hint switches narrow-tile K/V loads between
+    non-temporal and cacheable; it must not change a bit of O or LSE, on the split
+    (row-wise K through LDS off) and the unsplit (row-wise K through LDS) paths."""
+    b = W.decode_b128_kv1024(batch=32, kv_len=777)
+    dev = on_device(b)
+    o0, l0, i0 = run(b, max_kv_splits=max_kv_splits, dev=dev, label="stream")
+    o1, l1, i1 = run(b, max_kv_splits=max_kv_splits, dev=dev, label="cached", kv_shared=True)
+    assert (i0["num_split_groups"] > 0) == (max_kv_splits == 0)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+    ro, rl = ref(b)
+    assert_close(o0, l0, ro, rl, what="decode 32 x 777")
 
 
 def mixed_long_sample_rows(b):

@@ -225,6 +225,16 @@ def test_plan_rejects_bad_input(bad, code):
     assert len(str(e.value)) > len(code) + 5
 
 
+def test_plan_rejects_bad_kv_shared():
+    b = W.tiny_ragged_prefill()
+    p = rpa._Params(8, 1, 64, 16, 0, 1, 0.0, 0, 0, 0, 2)
+    h = ctypes.c_void_p()
+    qo, kp, kl = (rpa._host_i32(a) for a in (b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len))
+    rc = rpa.load().rpa_plan_create(ctypes.byref(p), 4, qo.ctypes.data, kp.ctypes.data, kl.ctypes.data,
+                                    ctypes.byref(h))
+    assert rpa.STATUS[rc] == "RPA_E_ARG" and b"kv_shared" in rpa.load().rpa_last_error()
+
+
 def test_noncausal_may_have_more_queries_than_keys():
     # non-causal: q_len > kv_len is a valid request (every query sees all keys) ...
     info = make_plan(lengths_batch([40, 3], [5, 2], causal=False)).info

@@ -682,8 +682,12 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     constexpr int KPJ = 64 / CH;          // keys per V load instruction
     constexpr int VJ = KW / KPJ;          // V loads per lane per step
     constexpr int KB = KW / 16;           // 16-key blocks per step
+    // the page table through the constant address space: wave-uniform indices become
+    // scalar loads, counted apart from the K/V loads
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, grp = lane >> 4;
     const int G = A.G;
     const int rows_valid = T.q_count * G;
@@ -713,67 +717,82 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     const uint16_t* kvh = A.kv + (int64_t)T.kv_head * D;
     const int vkey = lane / CH, vch = lane % CH;  // K/V gather: key j*KPJ + vkey, chunk vch
 
-    // Gathers for one step at key `kb0`: page ids, then K and V into natural-layout
-    // registers (each load instruction reads KPJ whole rows).  Keys at or past kv_len
-    // read as zero.
-    int pages[KB];
-    auto load_pages = [&](int kb0) {
+    // Gathers for one step: page ids (scalar loads, requested one step ahead), then K
+    // and V into registers with unconditional loads, so that the compiler's wait
+    // counts stay exact and step n's V can still be in flight while step n's Q K^T
+    // waits for its K.  A 16-key block at or past kv_len reads page 0 (valid memory,
+    // its keys are masked and their V zeroed once landed); a page index outside
+    // [0, num_pages) raises the error flag and its keys read as zero K and V.
+    constexpr int STRIDE = kWaves * KW;
+    auto pages_of = [&](int kb0, int (&pg)[KB]) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            int pg = -1;
-            if (kb0 + 16 * b < T.kv_len) {
-                pg = A.page_idx[T.page_base + (kb0 >> 4) + b];
-                if ((unsigned)pg >= (unsigned)A.num_pages) {
-                    *A.err_flag = 1;
-                    pg = -1;
-                }
+        for (int b = 0; b < KB; ++b)
+            pg[b] = kb0 + 16 * b < T.kv_len ? ((const_i32*)A.page_idx)[T.page_base + (kb0 >> 4) + b] : 0;
+    };
+    // Bad pages of a step: bit b set for block b (wave-uniform); such blocks read page 0.
+    // The error flag is written once after the key loop: a store between the loads
+    // would make the compiler wait for all of them (stores share their counter).
+    int bad_seen = 0;
+    auto check_pages = [&](int (&pg)[KB]) {
+        int bad = 0;
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+            if ((unsigned)pg[b] >= (unsigned)A.num_pages) {
+                bad |= 1 << b;
+                pg[b] = 0;
             }
-            pages[b] = pg;
-        }
+        bad_seen |= bad;
+        return bad;
     };
     u32x4 kr[VJ];      // K rows (KROWS)
     u32x4 kf[KB][DK];  // K in MFMA operand layout
     u32x4 vf[VJ];
-    auto load_k = [&](int kb0) {
+    auto load_k = [&](const int (&pg)[KB]) {
         if constexpr (KROWS) {
 #pragma unroll
             for (int j = 0; j < VJ; ++j) {
                 const int key = j * KPJ + vkey;
-                const int pg = pages[(j * KPJ) >> 4];
-                const bool ok = pg >= 0 && kb0 + key < T.kv_len;
-                kr[j] = ok ? ld_kv<NT>(kvh + ((int64_t)pg * 32 + (key & 15)) * ss + 8 * vch)
-                           : u32x4{0, 0, 0, 0};
+                kr[j] = ld_kv<NT>(kvh + ((int64_t)pg[(j * KPJ) >> 4] * 32 + (key & 15)) * ss + 8 * vch);
             }
         } else {
 #pragma unroll
             for (int b = 0; b < KB; ++b) {
-                const bool ok = pages[b] >= 0 && kb0 + 16 * b + col < T.kv_len;
-                const uint16_t* src = kvh + ((int64_t)pages[b] * 32 + col) * ss + 8 * grp;
+                const uint16_t* src = kvh + ((int64_t)pg[b] * 32 + col) * ss + 8 * grp;
 #pragma unroll
-                for (int kk = 0; kk < DK; ++kk)
-                    kf[b][kk] = ok ? ld_kv<NT>(src + 32 * kk) : u32x4{0, 0, 0, 0};
+                for (int kk = 0; kk < DK; ++kk) kf[b][kk] = ld_kv<NT>(src + 32 * kk);
             }
         }
     };
-    auto load_v = [&](int kb0) {
+    auto load_v = [&](const int (&pg)[KB]) {
 #pragma unroll
         for (int j = 0; j < VJ; ++j) {
-            const int key = j * KPJ + vkey;  // key within the step; its page is pages[key / 16]
-            const int pg = pages[(j * KPJ) >> 4];
-            const bool ok = pg >= 0 && kb0 + key < T.kv_len;
-            vf[j] = ok ? ld_kv<NT>(kvh + ((int64_t)pg * 32 + 16 + (key & 15)) * ss + 8 * vch)
-                       : u32x4{0, 0, 0, 0};
+            const int key = j * KPJ + vkey;  // key within the step; its page is pg[key / 16]
+            vf[j] = ld_kv<NT>(kvh + ((int64_t)pg[(j * KPJ) >> 4] * 32 + 16 + (key & 15)) * ss + 8 * vch);
+        }
+    };
+    // Landed V of a step: zero keys at or past kv_len and keys of bad pages (a mask,
+    // not a branch, so that each load is waited for on its own).
+    auto fix_v = [&](int kb0, int bad) {
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) {
+            const bool z = (bad & (1 << ((j * KPJ) >> 4))) || kb0 + j * KPJ + vkey >= T.kv_len;
+            const uint32_t keep = z ? 0u : ~0u;
+            vf[j] &= u32x4{keep, keep, keep, keep};
         }
     };
 
     // Software pipeline: while step n is computed, step n+1's K (issued right after
-    // step n's Q K^T) and V (issued right after step n's V is staged) are in flight.
-    constexpr int STRIDE = kWaves * KW;
+    // step n's Q K^T) and V (issued right after step n's V is staged) are in flight,
+    // and step n+2's page ids are requested.
     int kbase = T.kv_begin + wave * KW;
+    int pg_cur[KB], pg_nxt[KB];
+    int bad_cur = 0, bad_nxt = 0;
     if (kbase < T.kv_end) {
-        load_pages(kbase);
-        load_k(kbase);
-        load_v(kbase);
+        pages_of(kbase, pg_cur);
+        bad_cur = check_pages(pg_cur);
+        load_k(pg_cur);
+        load_v(pg_cur);
+        if (kbase + STRIDE < T.kv_end) pages_of(kbase + STRIDE, pg_nxt);
     }
     for (; kbase < T.kv_end; kbase += STRIDE) {
         const int knext = kbase + STRIDE;
@@ -799,12 +818,19 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
 #pragma unroll
             for (int kk = 0; kk < DK; ++kk) s[b] = mfma16_qk(kf[b][kk], qf[kk], s[b], BF16);
         }
+        // keys of a bad page count as zero K: score 0 (K registers are not zeroed, which
+        // would have to wait for their loads)
+        if (bad_cur)
+#pragma unroll
+            for (int b = 0; b < KB; ++b)
+                if (bad_cur & (1 << b)) s[b] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (more) {
-            load_pages(knext);
-            load_k(knext);
+            bad_nxt = check_pages(pg_nxt);
+            load_k(pg_nxt);
         }
 
         // ---- stage V (fp16, natural layout) ----
+        if (bad_cur || kbase + KW > T.kv_len) fix_v(kbase, bad_cur);
 #pragma unroll
         for (int j = 0; j < VJ; ++j) {
             u32x4 w = vf[j];
@@ -816,7 +842,11 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
             }
             *(u32x4*)(v_lds + (j * KPJ + vkey) * VS + 8 * vch) = w;
         }
-        if (more) load_v(knext);
+        if (more) {
+            load_v(pg_nxt);
+            bad_cur = bad_nxt;
+            if (knext + STRIDE < T.kv_end) pages_of(knext + STRIDE, pg_nxt);
+        }
 
         // ---- online softmax (lane: row `col`, keys 16b + 4grp + i) ----
         const bool need_mask = (kbase + KW > T.kv_len) || (A.causal && kbase + KW - 1 > pos_min);
@@ -874,6 +904,8 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
             }
         }
     }
+
+    if (bad_seen && lane == 0) *A.err_flag = 1;
 
     // ---- combine the 4 waves ----
     lsum += __shfl_xor(lsum, 16);

@@ -938,7 +938,10 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
 //   * P and the per-row rescale factors go through LDS ([key][row]) and are read
 //     back as broadcasts;
 //   * O: each lane accumulates its 8 d of every row over its keys, fp32 FMAs; the
-//     KPI key groups are summed once at the end.
+//     KPI key groups are summed once at the end;
+//   * page ids are read a step ahead by scalar loads; a step's K and V are
+//     requested at its start (carrying the next step's K/V in registers across the
+//     step, as the MFMA narrow kernel does, costs this kernel a wave per SIMD).
 template <int D, bool BF16, int RM>
 __device__ __forceinline__ void valu_tile(const AttnArgs& A, const Tile& T, char* smem) {
     constexpr int LPR = D / 8;
@@ -947,7 +950,9 @@ __device__ __forceinline__ void valu_tile(const AttnArgs& A, const Tile& T, char
     constexpr int NI = KW / KPI;
     constexpr int KB = KW / 16;  // pages per step
     static_assert(RM <= LPR && KW % KPI == 0, "lane layout");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    typedef __attribute__((address_space(4))) const int32_t const_i32;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane / LPR, j = lane % LPR;
     const int G = A.G;
     const int rows_valid = T.q_count * G;
@@ -976,31 +981,52 @@ __device__ __forceinline__ void valu_tile(const AttnArgs& A, const Tile& T, char
     const int64_t ss = (int64_t)A.Hkv * D;
     const uint16_t* kvh = A.kv + (int64_t)T.kv_head * D + 8 * j;
 
+    // Page ids by scalar loads one step ahead; a step's K and V are requested at its
+    // start with unconditional loads (a 16-key block at or past kv_len reads page 0,
+    // its keys are masked and their V zeroed; a bad page id zeroes its keys' scores
+    // and V and raises the error flag after the loop).
     constexpr int STRIDE = kWaves * KW;
-    for (int kbase = T.kv_begin + wave * KW; kbase < T.kv_end; kbase += STRIDE) {
-        int pages[KB];
+    int bad_seen = 0;
+    auto pages_of = [&](int kb0, int (&pg)[KB]) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-            int pg = -1;
-            if (kbase + 16 * b < T.kv_len) {
-                pg = A.page_idx[T.page_base + (kbase >> 4) + b];
-                if ((unsigned)pg >= (unsigned)A.num_pages) {
-                    *A.err_flag = 1;
-                    pg = -1;
-                }
+        for (int b = 0; b < KB; ++b)
+            pg[b] = kb0 + 16 * b < T.kv_len ? ((const_i32*)A.page_idx)[T.page_base + (kb0 >> 4) + b] : 0;
+    };
+    auto check_pages = [&](int (&pg)[KB]) {
+        int bad = 0;
+#pragma unroll
+        for (int b = 0; b < KB; ++b)
+            if ((unsigned)pg[b] >= (unsigned)A.num_pages) {
+                bad |= 1 << b;
+                pg[b] = 0;
             }
-            pages[b] = pg;
-        }
-        u32x4 kr[NI], vr[NI];
+        bad_seen |= bad;
+        return bad;
+    };
+    u32x4 kr[NI], vr[NI];
+    auto load_k = [&](const int (&pg)[KB]) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int kl = KPI * i + g;  // key within the step
-            const int pg = pages[kl >> 4];
-            const bool ok = pg >= 0 && kbase + kl < T.kv_len;
-            const uint16_t* src = kvh + ((int64_t)pg * 32 + (kl & 15)) * ss;
-            kr[i] = ok ? *(const u32x4*)src : u32x4{0, 0, 0, 0};
-            vr[i] = ok ? *(const u32x4*)(src + 16 * ss) : u32x4{0, 0, 0, 0};
+            kr[i] = *(const u32x4*)(kvh + ((int64_t)pg[(KPI * i) >> 4] * 32 + (kl & 15)) * ss);
         }
+    };
+    auto load_v = [&](const int (&pg)[KB]) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int kl = KPI * i + g;
+            vr[i] = *(const u32x4*)(kvh + ((int64_t)pg[(KPI * i) >> 4] * 32 + 16 + (kl & 15)) * ss);
+        }
+    };
+    int kbase = T.kv_begin + wave * KW;
+    int pg_nxt[KB];
+    if (kbase < T.kv_end) pages_of(kbase, pg_nxt);
+    for (; kbase < T.kv_end; kbase += STRIDE) {
+        const int knext = kbase + STRIDE;
+        const int bad_cur = check_pages(pg_nxt);
+        load_k(pg_nxt);
+        load_v(pg_nxt);
+        if (knext < T.kv_end) pages_of(knext, pg_nxt);
         // ---- scores ----
         float sv[NI];
 #pragma unroll
@@ -1042,6 +1068,11 @@ __device__ __forceinline__ void valu_tile(const AttnArgs& A, const Tile& T, char
             }
             sv[i] = part[0];
         }
+        // keys of a bad page count as zero K: score 0
+        if (bad_cur)
+#pragma unroll
+            for (int i = 0; i < NI; ++i)
+                if (bad_cur & (1 << ((KPI * i) >> 4))) sv[i] = 0.f;
         // ---- online softmax of this lane's row over the step's keys ----
         const bool need_mask = (kbase + KW > T.kv_len) || (A.causal && kbase + KW - 1 > pos_min);
         float bmax = -INFINITY;
@@ -1078,7 +1109,14 @@ __device__ __forceinline__ void valu_tile(const AttnArgs& A, const Tile& T, char
         for (int r = 0; r < RM; ++r)
 #pragma unroll
             for (int e = 0; e < 8; ++e) oacc[r][e] *= ar[r];
-        // ---- O += P V ----
+        // ---- O += P V (V of keys at or past kv_len and of bad pages zeroed first) ----
+        if (bad_cur || kbase + KW > T.kv_len)
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const bool z = (bad_cur & (1 << ((KPI * i) >> 4))) || kbase + KPI * i + g >= T.kv_len;
+                const uint32_t keep = z ? 0u : ~0u;
+                vr[i] &= u32x4{keep, keep, keep, keep};
+            }
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const float* pk = p_lds + (KPI * i + g) * RM;
@@ -1097,6 +1135,7 @@ __device__ __forceinline__ void valu_tile(const AttnArgs& A, const Tile& T, char
                 for (int e = 0; e < 8; ++e) oacc[r][e] = __builtin_fmaf(pr[r], v[e], oacc[r][e]);
         }
     }
+    if (bad_seen && lane == 0) *A.err_flag = 1;
 
     // ---- sum the key groups, then combine the 4 waves ----
 #pragma unroll

@@ -7,7 +7,8 @@
 //   attn_wide_kernel    tiles of up to 128 rows (prefill): S^T = K Q^T and
 //                       O^T += V^T P^T on v_mfma_f32_32x32x16, 32-key units
 //                       loaded straight from the cache into an LDS ring, a
-//                       software pipeline over the units (see wide_tile);
+//                       software pipeline over the units, Q read and O written
+//                       in whole rows through LDS (see wide_tile);
 //   attn_narrow_kernel  tiles of up to 16 rows (decode-like): the 4 waves split
 //                       the keys, v_mfma_f32_16x16x32, K into MFMA registers
 //                       directly or in whole rows through LDS, V read back
@@ -325,11 +326,25 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     const bool row_ok = row < rows_valid;
     const int pos = T.pos0 + tok;
     const int64_t orow = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
-    u32x4 qf[DK];  // Q^T operand, 8 consecutive d per k-step, held for the whole tile
-    {
-        const uint16_t* qp = A.q + orow * D + 8 * half;
+    // Q^T operand, 8 consecutive d per k-step, held for the whole tile.  Read from
+    // memory in whole rows (16-byte chunk c of row 4i + l/16 by lane l, instruction i:
+    // each instruction reads 4 rows of D * 2 contiguous bytes) and moved into the
+    // operand layout through LDS in the prologue (qraw -> qf), since loads in the
+    // operand layout would scatter every instruction over 32 rows.
+    constexpr int QCH = D / 8;               // 16-byte chunks per row
+    constexpr int QRPI = 64 / QCH;           // rows per load instruction
+    constexpr int QI = 32 / QRPI;            // load instructions per wave
+    u32x4 qraw[QI];
+    u32x4 qf[DK];
 #pragma unroll
-        for (int kk = 0; kk < DK; ++kk) qf[kk] = row_ok ? *(const u32x4*)(qp + 16 * kk) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < QI; ++i) {
+        const int r = QRPI * i + lane / QCH, rw = wave * 32 + r;
+        qraw[i] = u32x4{0, 0, 0, 0};
+        if (rw < rows_valid) {
+            const int tk = rw / G, gh = rw - tk * G;
+            const int64_t orw = (int64_t)(T.q_row0 + tk) * A.H + T.kv_head * G + gh;
+            qraw[i] = *(const u32x4*)(A.q + orw * D + 8 * (lane % QCH));
+        }
     }
     const int wpos_min = T.pos0 + (wave * 32) / G;  // smallest position among this wave's rows
 
@@ -567,6 +582,29 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             u32x4 vcv[IPW];
             v_fp16_read(0, vcv);
             v_fp16_write(0, vcv);
+            // Q rows into the operand layout, through ring slot NS - 1 (no unit is
+            // requested into it before the barrier below): 16 rows per wave at a time,
+            // at a stride of D * 2 + 16 bytes (conflict-free 16-byte reads).
+            {
+                constexpr int QS = D + 8;  // staged row stride (elements)
+                static_assert(kWideWaves * 16 * QS * 2 <= SLOT, "Q staging fits one ring slot");
+                uint16_t* qs = reinterpret_cast<uint16_t*>(smem + (NS - 1) * SLOT) + wave * 16 * QS;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int i = 0; i < QI / 2; ++i) {
+                        const int r = QRPI * i + lane / QCH;  // row within this half
+                        *(u32x4*)(qs + r * QS + 8 * (lane % QCH)) = qraw[h * (QI / 2) + i];
+                    }
+                    if ((col >> 4) == h)
+#pragma unroll
+                        for (int kk = 0; kk < DK; ++kk)
+                            qf[kk] = *(const u32x4*)(qs + (col & 15) * QS + 16 * kk + 8 * half);
+                }
+#pragma unroll
+                for (int kk = 0; kk < DK; ++kk)
+                    if (!row_ok) qf[kk] = u32x4{0, 0, 0, 0};
+            }
             barrier();
         }
         f32x16 sa, sb;
@@ -583,31 +621,48 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     const float ltot = lsum + xor32(lsum);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     const float lse_val = ltot > 0.f ? (m_run + __log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
-    if (row_ok) {
-        if (T.part < 0) {
-            uint16_t* op = A.o + orow * D + 4 * half;
+    if (T.part < 0) {
+        // O through LDS, so that 16 lanes store one row's D * 2 contiguous bytes: in
+        // the MFMA layout a lane holds 4-element pieces of one row, and storing them
+        // directly scatters every store instruction over 32 rows.  Each wave stages
+        // its 32 rows in its own part of the ring, which every wave has finished with
+        // at the barrier.
+        constexpr int OSTR = D + 8;  // staged row stride (elements): 16-byte pad
+        static_assert(kWideWaves * 32 * OSTR * 2 <= C::bytes, "O staging fits the ring");
+        __syncthreads();
+        uint16_t* ost = reinterpret_cast<uint16_t*>(smem) + wave * 32 * OSTR;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    u32x2 w;
-                    w[0] = pack_out<BF16>(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
-                    w[1] = pack_out<BF16>(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
-                    *(u32x2*)(op + 32 * db + 8 * jj) = w;
-                }
-            if (A.lse && half == 0) A.lse[orow] = lse_val;
-        } else {
-            float* pp = A.part_o + ((int64_t)T.part + row) * D + 4 * half;
+            for (int jj = 0; jj < 4; ++jj) {
+                u32x2 w;
+                w[0] = pack_out<BF16>(oacc[db][4 * jj + 0] * inv, oacc[db][4 * jj + 1] * inv);
+                w[1] = pack_out<BF16>(oacc[db][4 * jj + 2] * inv, oacc[db][4 * jj + 3] * inv);
+                *(u32x2*)(ost + col * OSTR + 32 * db + 8 * jj + 4 * half) = w;
+            }
+        constexpr int CPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    f32x4 w = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
-                               oacc[db][4 * jj + 3] * inv};
-                    st_dev4(pp + 32 * db + 8 * jj, w);
-                }
-            if (half == 0) st_dev(A.part_lse + T.part + row, lse_val);
+        for (int i = 0; i < 32 * CPR / 64; ++i) {
+            const int idx = 64 * i + lane, r = idx / CPR, c = idx - r * CPR;
+            const int rw = wave * 32 + r;
+            if (rw < rows_valid) {
+                const int tk = rw / G, gh = rw - tk * G;
+                const int64_t orw = (int64_t)(T.q_row0 + tk) * A.H + T.kv_head * G + gh;
+                *(u32x4*)(A.o + orw * D + 8 * c) = *(const u32x4*)(ost + r * OSTR + 8 * c);
+            }
         }
+        if (row_ok && A.lse && half == 0) A.lse[orow] = lse_val;
+    } else if (row_ok) {
+        float* pp = A.part_o + ((int64_t)T.part + row) * D + 4 * half;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                f32x4 w = {oacc[db][4 * jj] * inv, oacc[db][4 * jj + 1] * inv, oacc[db][4 * jj + 2] * inv,
+                           oacc[db][4 * jj + 3] * inv};
+                st_dev4(pp + 32 * db + 8 * jj, w);
+            }
+        if (half == 0) st_dev(A.part_lse + T.part + row, lse_val);
     }
     if (T.part >= 0) finish_split<D, BF16>(A, T);
 }

@@ -241,6 +241,24 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     // ---- launch order: wide tiles (one kernel), then narrow tiles (another) ----------------
     std::vector<Piece> wide, narrow;
     for (auto& pc : pieces) (pc.t.kind == kWide ? wide : narrow).push_back(pc);
+    // A few small narrow tiles beside many wide ones (the last tokens of short prompts)
+    // would cost a second launch for little work: they run in the wide launch instead,
+    // where a tile of up to 16 rows is a valid, partly empty wide tile.
+    if (!p.narrow_valu && !narrow.empty() && narrow.size() * kFoldRatio <= wide.size()) {
+        int64_t keys = 0;
+        for (const auto& pc : narrow) keys += pc.t.kv_end - pc.t.kv_begin;
+        if (keys * int64_t(p.head_dim) * 4 <= kFoldBytes) {
+            for (auto& pc : narrow) {
+                pc.t.kind = kWide;
+                pc.cost = ceil_div(pc.t.kv_end - pc.t.kv_begin, BN) * BN + 64;
+                wide.push_back(pc);
+            }
+            narrow.clear();
+            S.narrow_tiles = 0;
+            S.narrow_max_rows = 0;
+            S.narrow_split = false;
+        }
+    }
     // Narrow tiles read their keys once: longest first (LPT), ties in natural order.
     std::stable_sort(narrow.begin(), narrow.end(), [](const Piece& a, const Piece& b) { return a.cost > b.cost; });
     order_wide_for_xcds(wide);

@@ -23,6 +23,10 @@ constexpr int kValuRows = 8;      // narrow threshold when narrow tiles run on t
 constexpr int kValuKeys = 32;     // keys one wave handles per step on the VALU narrow path
 constexpr int kXcds = 8;          // MI355X: workgroup i of a launch runs on XCD i % 8
 constexpr int kChunkKeys = 256;   // split pieces start at multiples of this many keys
+// Narrow tiles join the wide launch when there are at most 1/kFoldRatio as many of
+// them as wide tiles and their K/V come to at most kFoldBytes.
+constexpr int kFoldRatio = 4;
+constexpr int64_t kFoldBytes = int64_t(8) << 20;
 
 // Keys per inner block (unit) of the wide path, whatever the head_dim.
 constexpr int block_n_for(int) { return 32; }

@@ -101,8 +101,13 @@ def check_schedule(b: W.Batch, plan):
     for (a0, a1), (c0, c1) in zip(part_ranges, part_ranges[1:]):
         assert a1 <= c0
     assert info["partial_rows"] == n_part_rows
-    # 3. tile kind: narrow (decode-like path) exactly when a tile has at most 16 rows
-    assert all((r[F["kind"]] == 1) == (0 < r[F["q_count"]] * G <= 16) for r in t)
+    # 3. tile kind: narrow (decode-like path) exactly when a tile has at most 16 rows,
+    #    unless the plan folded its few, small narrow tiles into the wide launch
+    small = [r for r in t if 0 < r[F["q_count"]] * G <= 16]
+    if small and not any(r[F["kind"]] == 1 for r in t):
+        assert folded(t, b.head_dim, G)
+    else:
+        assert all((r[F["kind"]] == 1) == (0 < r[F["q_count"]] * G <= 16) for r in t)
     # 4. launch order: all wide tiles (one kernel), then all narrow tiles (another).
     #    Narrow tiles go longest first (keys walked, rounded to 64).  Wide tiles go
     #    longest first in small launches; in larger ones, launch slot i runs on XCD
@@ -138,6 +143,38 @@ def check_schedule(b: W.Batch, plan):
     assert info["visible_pairs"] == vis * b.num_qo_heads
     assert info["total_q"] == b.total_q
     return t
+
+
+FOLD_RATIO, FOLD_BYTES = 4, 8 << 20
+
+
+def folded(t, D, G):
+    """Whether the narrow-size tiles of schedule t meet the rule for running in the wide
+    launch: at most a quarter as many as the other tiles, K/V of at most 8 MiB."""
+    small = [r for r in t if 0 < r[F["q_count"]] * G <= 16]
+    others = [r for r in t if r[F["q_count"]] * G > 16]
+    keys = sum(int(r[F["kv_end"]] - r[F["kv_begin"]]) for r in small)
+    return len(small) * FOLD_RATIO <= len(others) and keys * D * 4 <= FOLD_BYTES
+
+
+def test_few_small_narrow_tiles_join_the_wide_launch():
+    # short ragged prompts: the last few tokens of some prompts make tiles of <= 16 rows
+    b = lengths_batch(W.short_prompt_lengths(), W.short_prompt_lengths(), H=32, Hk=8)
+    t = make_plan(b).tiles()
+    assert (t[:, F["kind"]] == 0).all() and ((t[:, F["q_count"]] * 4 <= 16) & (t[:, F["q_count"]] > 0)).any()
+    # decode rows beside long prompts are many and long: they keep the narrow kernel
+    m = lengths_batch([8192] * 4 + [1] * 256, [8192] * 4 + [4096] * 256, H=64, Hk=8)
+    tm = make_plan(m).tiles()
+    assert ((tm[:, F["kind"]] == 1) == ((tm[:, F["q_count"]] > 0) & (tm[:, F["q_count"]] * 8 <= 16))).all()
+    # so do decode-only batches, and mixes where narrow tiles are not few
+    for c in (lengths_batch([1] * 128, [1024] * 128), lengths_batch([17, 3, 5, 1], [17, 30, 5, 48], D=64)):
+        tc = make_plan(c).tiles()
+        assert (tc[:, F["kind"]] == 1).any()
+    # the VALU decode kernel (a comparison) keeps every tile of its size
+    v = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=32, num_kv_heads=8,
+                 head_dim=128, dtype="bf16", narrow_kernel="valu")
+    tv = v.tiles()
+    assert ((tv[:, F["kind"]] == 1) == ((tv[:, F["q_count"]] > 0) & (tv[:, F["q_count"]] * 4 <= 8))).all()
 
 
 def qo_row_in_seq(b, s, r0):

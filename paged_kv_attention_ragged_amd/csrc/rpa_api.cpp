@@ -196,7 +196,8 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
     }
     if (rc != 0) return set_err(rpa_status(rc), err);
     const auto& O = plan->sched;
-    if (S.tiles.size() != O.tiles.size() || S.wide_tiles != O.wide_tiles || S.merges.size() != O.merges.size() ||
+    if (S.tiles.size() != O.tiles.size() || S.wide_tiles != O.wide_tiles || S.fused != O.fused ||
+        S.merges.size() != O.merges.size() ||
         S.partial_rows > O.partial_rows)
         return set_err(RPA_E_UNSUPPORTED,
                        "the new lengths need another launch shape (" + std::to_string(S.tiles.size()) + " tiles, " +
@@ -250,12 +251,27 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
     L.bf16 = P.dtype == RPA_BF16;
     L.n_tiles = int64_t(S.tiles.size());
 
-    // One kernel for the wide tiles (tiles[0, wide)), one for the narrow tiles after them.
+    // One kernel for the wide tiles (tiles[0, wide)), one for the narrow tiles after them,
+    // or, for a plan with both kinds, one mixed kernel over the interleaved tiles.
     // Profiling: an event pair stamped by each dispatch itself (start and end of the kernel).
     const bool prof = g_prof_on;
     ProfEv e0{nullptr, nullptr, 0}, e1{nullptr, nullptr, 1};
     hipError_t e = hipSuccess;
-    if (S.wide_tiles > 0) {
+    // Split key ranges put each narrow tile's last step on the latency-critical path of
+    // the merge, where the extra LDS round trip of row-wise K loads costs more than their
+    // better coalescing gains; unsplit (many-tile) decode is throughput-bound.
+    L.k_rows = !S.narrow_split;
+    // Pages read by one sequence only are streamed past L2 (non-temporal), which keeps the
+    // schedule, page indices and Q resident; shared pages stay cached.
+    L.kv_stream = P.kv_shared == 0;
+    if (S.fused) {  // wide and narrow tiles interleaved in one launch (timed as "wide")
+        if (prof) {
+            e0.a = prof_event();
+            e0.b = prof_event();
+        }
+        e = rpa::launch_mixed(L, st, e0.a, e0.b);
+        if (e != hipSuccess) return hip_err(e, "mixed attention kernel launch");
+    } else if (S.wide_tiles > 0) {
         if (prof) {
             e0.a = prof_event();
             e0.b = prof_event();
@@ -264,7 +280,7 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
         e = rpa::launch_wide(L, st, e0.a, e0.b);
         if (e != hipSuccess) return hip_err(e, "wide attention kernel launch");
     }
-    if (S.narrow_tiles > 0) {
+    if (!S.fused && S.narrow_tiles > 0) {
         if (prof) {
             e1.a = prof_event();
             e1.b = prof_event();
@@ -272,13 +288,6 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
         rpa::LaunchAttn N = L;
         N.a.tiles = L.a.tiles + S.wide_tiles;
         N.n_tiles = S.narrow_tiles;
-        // Split key ranges put each tile's last step on the latency-critical path of the
-        // merge, where the extra LDS round trip of row-wise K loads costs more than their
-        // better coalescing gains; unsplit (many-tile) decode is throughput-bound.
-        N.k_rows = !S.narrow_split;
-        // Pages read by one sequence only are streamed past L2 (non-temporal), which
-        // keeps the schedule, page indices and Q resident; shared pages stay cached.
-        N.kv_stream = P.kv_shared == 0;
         e = P.narrow_kernel == 1 ? rpa::launch_narrow_valu(N, S.narrow_max_rows, st, e1.a, e1.b)
                                  : rpa::launch_narrow(N, st, e1.a, e1.b);
         if (e != hipSuccess) return hip_err(e, "narrow attention kernel launch");

@@ -14,6 +14,8 @@
 //                       directly or in whole rows through LDS, V read back
 //                       transposed (see narrow_tile); K/V loads non-temporal
 //                       unless the caller says pages are shared by sequences;
+//   attn_mixed_kernel   both kinds in one launch, for plans that have both (a
+//                       mixed batch of prompts and decode rows);
 //   attn_narrow_valu_kernel  the same tiles (up to 8 rows) without MFMA, on dot2
 //                       and fp32 FMAs, for comparison (see valu_tile);
 //   merge_states_kernel join of two attention states (cascade halves);
@@ -1258,6 +1260,21 @@ void attn_narrow_kernel(AttnArgs A) {
     narrow_tile<D, BF16, KROWS, NT>(A, T, smem);
 }
 
+// Both kinds in one launch (mixed batches): each workgroup takes its tile's path.  Both
+// paths use 4 waves and fit three workgroups per CU; the LDS is the larger of the two.
+template <int D, bool BF16, bool KROWS, bool NT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
+void attn_mixed_kernel(AttnArgs A) {
+    static_assert(kWaves == kWideWaves, "one workgroup size for both paths");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const Tile T = A.tiles[blockIdx.x];
+    if (T.q_count <= 0) return;
+    if (T.kind == kWide)
+        wide_tile<D, BF16>(A, T, smem);
+    else
+        narrow_tile<D, BF16, KROWS, NT>(A, T, smem);
+}
+
 // ---- host-side launchers -----------------------------------------------------------------
 
 // Merge of two attention states over disjoint key sets A and B of the same query
@@ -1377,6 +1394,28 @@ template <int D, bool BF16>
 hipError_t launch_narrow_d(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     return L.kv_stream ? launch_narrow_nt<D, BF16, true>(L, stream, ev0, ev1)
                        : launch_narrow_nt<D, BF16, false>(L, stream, ev0, ev1);
+}
+
+template <int D, bool BF16, bool KROWS, bool NT>
+hipError_t launch_mixed_k(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    constexpr int lds = WideCfg<D>::bytes > NarrowLds<D>::bytes ? WideCfg<D>::bytes : NarrowLds<D>::bytes;
+    return launch_with_lds<&attn_mixed_kernel<D, BF16, KROWS, NT>>(L, lds, kWaves * 64, stream, ev0, ev1);
+}
+
+template <int D, bool BF16>
+hipError_t launch_mixed_d(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    if (L.k_rows)
+        return L.kv_stream ? launch_mixed_k<D, BF16, true, true>(L, stream, ev0, ev1)
+                           : launch_mixed_k<D, BF16, true, false>(L, stream, ev0, ev1);
+    return L.kv_stream ? launch_mixed_k<D, BF16, false, true>(L, stream, ev0, ev1)
+                       : launch_mixed_k<D, BF16, false, false>(L, stream, ev0, ev1);
+}
+
+hipError_t launch_mixed(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    if (L.n_tiles <= 0) return hipSuccess;
+    if (L.head_dim == 128)
+        return L.bf16 ? launch_mixed_d<128, true>(L, stream, ev0, ev1) : launch_mixed_d<128, false>(L, stream, ev0, ev1);
+    return L.bf16 ? launch_mixed_d<64, true>(L, stream, ev0, ev1) : launch_mixed_d<64, false>(L, stream, ev0, ev1);
 }
 
 hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {

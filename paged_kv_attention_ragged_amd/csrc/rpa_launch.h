@@ -31,7 +31,7 @@ struct LaunchAttn {
     int64_t n_tiles;
     bool k_rows;      // narrow kernel: K loaded in whole rows through LDS (else straight into
                       // MFMA operand layout)
-    bool kv_stream;   // narrow kernel: K/V loads non-temporal (pages not shared by sequences)
+    bool kv_stream;   // narrow tiles: K/V loads non-temporal (pages not shared by sequences)
 };
 
 
@@ -63,6 +63,8 @@ struct AppendArgs {
 // ev0 / ev1: optional events stamped at the start and end of the dispatch (NULL: none).
 hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_narrow(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+// Wide and narrow tiles (each record's kind) in one launch.
+hipError_t launch_mixed(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 // Narrow tiles on the VALU kernel; max_rows (<= kValuRows) picks its row capacity.
 hipError_t launch_narrow_valu(const LaunchAttn& L, int max_rows, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_merge(const MergeArgs& M, bool bf16, hipStream_t stream);

@@ -264,8 +264,25 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     order_wide_for_xcds(wide);
     S.wide_tiles = int64_t(wide.size());
     S.tiles.reserve(wide.size() + narrow.size());
-    for (auto& pc : wide) S.tiles.push_back(pc.t);
-    for (auto& pc : narrow) S.tiles.push_back(pc.t);
+    if (!p.narrow_valu && !wide.empty() && !narrow.empty()) {
+        // Both kinds in one launch (a mixed batch: prompts and decode rows), so that the
+        // decode rows' K/V stream overlaps the prompts' matrix work.  Narrow tiles go in
+        // blocks of kXcds between blocks of kXcds wide tiles, spread evenly over the
+        // launch; a wide tile thus keeps its launch slot modulo kXcds (its XCD), and a
+        // partial block of either kind comes last.
+        S.fused = true;
+        const size_t wb = (wide.size() + kXcds - 1) / kXcds, nb = (narrow.size() + kXcds - 1) / kXcds;
+        size_t next_nb = 0;
+        for (size_t k = 0; k < wb; ++k) {
+            for (size_t i = k * kXcds; i < std::min(wide.size(), (k + 1) * kXcds); ++i) S.tiles.push_back(wide[i].t);
+            for (const size_t upto = (k + 1) * nb / wb; next_nb < upto; ++next_nb)
+                for (size_t i = next_nb * kXcds; i < std::min(narrow.size(), (next_nb + 1) * kXcds); ++i)
+                    S.tiles.push_back(narrow[i].t);
+        }
+    } else {
+        for (auto& pc : wide) S.tiles.push_back(pc.t);
+        for (auto& pc : narrow) S.tiles.push_back(pc.t);
+    }
     *out = std::move(S);
     return OK;
 }

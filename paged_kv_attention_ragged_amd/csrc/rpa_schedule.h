@@ -83,7 +83,8 @@ struct Schedule {
     int32_t tokens_per_tile = 0;
     int32_t block_m = 0;
     int32_t block_n = 0;
-    int64_t wide_tiles = 0;     // tiles[0, wide_tiles) are wide, the rest narrow
+    int64_t wide_tiles = 0;     // tiles[0, wide_tiles) are wide, the rest narrow (unless fused)
+    bool fused = false;         // both kinds, interleaved, in one launch of the mixed kernel
     int32_t max_splits = 1;
     int64_t narrow_tiles = 0;
     int32_t narrow_max_rows = 0;  // largest row count among narrow tiles

@@ -125,9 +125,11 @@ rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
 
 /*
  * Copy of the plan's work items for inspection: up to `cap` records of 16
- * int32 each into `out_h` (host), in launch order.  Wide records with
- * [1] == 0 are empty padding that aligns tiles to XCDs (workgroup i of a launch
- * runs on XCD i % 8).  Fields per record:
+ * int32 each into `out_h` (host), in launch order: the wide records, then the
+ * narrow ones, or, when the plan has both kinds (and narrow_kernel is 0), both
+ * in one launch with narrow records in blocks of 8 between blocks of 8 wide ones.
+ * Wide records with [1] == 0 are empty padding that aligns tiles to XCDs
+ * (workgroup i of a launch runs on XCD i % 8).  Fields per record:
  *   [0] first query row, [1] query tokens, [2] position of the first query,
  *   [3] kv_len, [4] kv_page_indptr[b], [5] kv head, [6] first key, [7] end key,
  *   [8] first partial row (-1: writes O directly), [9] sequence, [10] split
@@ -159,10 +161,11 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
  *   kv_cache  device [num_pages][2][page_size][num_kv_heads][head_dim], same dtype
  *   o         device [total_q][num_qo_heads][head_dim], same dtype (written)
  *   lse       device fp32 [total_q][num_qo_heads] (written), or NULL
- * Enqueues on `stream` one kernel for the plan's wide tiles (up to 128 query
- * rows each) and one for its narrow tiles (up to 16 rows: decode-like; up to 8
- * on the VALU kernel, params.narrow_kernel = 1), each only if the plan has such
- * tiles; when the plan splits key ranges, the piece
+ * Enqueues on `stream` one kernel over the plan's tiles: wide tiles (up to 128
+ * query rows each), narrow tiles (up to 16 rows: decode-like), or both kinds
+ * interleaved in one launch.  With params.narrow_kernel = 1 the narrow tiles (up
+ * to 8 rows) run on the VALU kernel, launched after the wide tiles' kernel.  When
+ * the plan splits key ranges, the piece
  * of each split group that finishes last merges the group inside its kernel.
  * No allocation, no host<->device synchronisation.  One run at a time per
  * (plan, workspace): the partial-result region and the split counters are
@@ -293,8 +296,8 @@ const char* rpa_version(void);
  * Kernel timing (benchmarks): while enabled, rpa_run has a HIP event pair
  * stamped by each kernel dispatch it enqueues (start and end of the kernel).
  * rpa_prof_stop synchronises those events and returns, per kernel kind
- * (0 = wide-tile kernel, 1 = narrow-tile kernel), the number of launches and
- * their summed duration in milliseconds.
+ * (0 = wide-tile or mixed kernel, 1 = narrow-tile kernel), the number of
+ * launches and their summed duration in milliseconds.
  */
 rpa_status rpa_prof_start(void);
 rpa_status rpa_prof_stop(int64_t counts_out[2], double ms_out[2]);

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 import oracle
+import paged_kv_attention_ragged_amd as rpa
 import workloads as W
 from tests.gpu_util import assert_close, on_device, run, say
 
@@ -221,6 +222,30 @@ def mixed_long_sample_rows(b):
             rows.extend(range(a, e, 61))
             rows.extend(range(e - 64, e))
     return sorted(set(rows))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_mixed_launch_prompts_and_split_decode_rows(dtype):
+    """Prompts and decode rows in one plan run in one launch with both kinds of tile
+    interleaved; here the decode rows' key ranges are also split (few tiles), so the
+    launch holds wide tiles, split narrow pieces and their in-kernel merges.  Checked
+    against the oracle, and bitwise against the same plan with cacheable K/V loads."""
+    q_lens = [150, 1, 40, 1, 3, 1]
+    kv_lens = [150, 3000, 900, 1777, 2500, 16]
+    b = W.make_batch("mixed_launch", q_lens, kv_lens, num_qo_heads=16, num_kv_heads=2, head_dim=128,
+                     dtype=dtype, seed=77, spare_pages=5, poison=True)
+    dev = on_device(b)
+    o, l, info = run(b, dev=dev, label="mixed launch")
+    assert info["num_split_groups"] > 0
+    p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=16, num_kv_heads=2,
+                 head_dim=128, dtype=dtype)
+    kinds = p.tiles()[:, 12]
+    p.close()
+    assert (kinds == 0).any() and (kinds == 1).any() and (np.diff(kinds) < 0).any()  # interleaved
+    ro, rl = ref(b)
+    assert_close(o, l, ro, rl, what="mixed launch %s" % dtype)
+    o2, l2, _ = run(b, dev=dev, label="mixed launch, kv_shared", kv_shared=True)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
 
 
 def test_mixed_long_batch_sampled():

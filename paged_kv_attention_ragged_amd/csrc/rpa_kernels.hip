@@ -336,17 +336,16 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     constexpr int QCH = D / 8;               // 16-byte chunks per row
     constexpr int QRPI = 64 / QCH;           // rows per load instruction
     constexpr int QI = 32 / QRPI;            // load instructions per wave
+    // Rows past the tile's last one read its last row instead (unconditional loads, no
+    // wait inside a branch); they are zeroed when the operand is formed.
     u32x4 qraw[QI];
     u32x4 qf[DK];
 #pragma unroll
     for (int i = 0; i < QI; ++i) {
-        const int r = QRPI * i + lane / QCH, rw = wave * 32 + r;
-        qraw[i] = u32x4{0, 0, 0, 0};
-        if (rw < rows_valid) {
-            const int tk = rw / G, gh = rw - tk * G;
-            const int64_t orw = (int64_t)(T.q_row0 + tk) * A.H + T.kv_head * G + gh;
-            qraw[i] = *(const u32x4*)(A.q + orw * D + 8 * (lane % QCH));
-        }
+        const int rw = min(wave * 32 + QRPI * i + lane / QCH, rows_valid - 1);
+        const int tk = rw / G, gh = rw - tk * G;
+        const int64_t orw = (int64_t)(T.q_row0 + tk) * A.H + T.kv_head * G + gh;
+        qraw[i] = *(const u32x4*)(A.q + orw * D + 8 * (lane % QCH));
     }
     const int wpos_min = T.pos0 + (wave * 32) / G;  // smallest position among this wave's rows
 
@@ -756,14 +755,27 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     const int64_t orow = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
     uint16_t* v_lds = reinterpret_cast<uint16_t*>(smem) + wave * KW * VS;
 
-    // Q^T operand (B of 16x16x32): row `col`, d = 32kk + 8grp .. +8.
-    u32x4 qf[DK];
-    {
-        const uint16_t* qp = A.q + orow * D + 8 * grp;
+    // Q^T operand (B of 16x16x32): row `col`, d = 32kk + 8grp .. +8.  Read in whole
+    // rows (16-byte chunk c of row QRPI i + l / CH by lane l, instruction i) and moved
+    // into the operand layout through the wave's LDS area once the first K/V loads
+    // are requested: Q is then in registers before the key loop, so the compiler's
+    // waits inside the loop count only the loop's own loads.
+    constexpr int QRPI = 64 / CH;  // rows per Q load instruction
+    constexpr int QI = 16 / QRPI;  // Q load instructions (16 rows)
+    // (rows past the tile's last one read its last row instead -- unconditional loads,
+    // no wait inside a branch -- and are zeroed when the operand is formed)
+    u32x4 qraw[QI];
 #pragma unroll
-        for (int kk = 0; kk < DK; ++kk)
-            qf[kk] = row_ok ? *(const u32x4*)(qp + 32 * kk) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < QI; ++i) {
+        const int r = min(QRPI * i + lane / CH, rows_valid - 1);
+        const int tk = r / G, gh = r - tk * G;
+        const int64_t orw = (int64_t)(T.q_row0 + tk) * A.H + T.kv_head * G + gh;
+        qraw[i] = *(const u32x4*)(A.q + orw * D + 8 * (lane % CH));
     }
+    // keep the Q loads ahead of the first K/V loads (no memory access moves across an
+    // asm statement that clobbers memory), so that staging Q waits for Q alone
+    asm volatile("" ::: "memory");
+    u32x4 qf[DK];
 
     f32x4 oacc[DB];
 #pragma unroll
@@ -844,16 +856,28 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     int kbase = T.kv_begin + wave * KW;
     int pg_cur[KB], pg_nxt[KB];
     int bad_cur = 0, bad_nxt = 0;
-    if (kbase < T.kv_end) {
-        pages_of(kbase, pg_cur);
-        bad_cur = check_pages(pg_cur);
-        load_k(pg_cur);
-        load_v(pg_cur);
-        if (kbase + STRIDE < T.kv_end) pages_of(kbase + STRIDE, pg_nxt);
-    }
-    for (; kbase < T.kv_end; kbase += STRIDE) {
+    // First step's loads, unconditional: a wave with no keys (a tile of fewer than
+    // kWaves * KW keys) reads page 0 and never uses it.  A branch here would leave the
+    // compiler, where its two paths join, waiting for every load in flight.
+    pages_of(kbase, pg_cur);
+    bad_cur = check_pages(pg_cur);
+    load_k(pg_cur);
+    load_v(pg_cur);
+    if (kbase + STRIDE < T.kv_end) pages_of(kbase + STRIDE, pg_nxt);
+    // Q rows into the operand layout through the wave's LDS area (free until its first
+    // step), while those loads are in flight.
+    static_assert(16 * KS <= KW * VS, "Q staging fits the wave's area");
+#pragma unroll
+    for (int i = 0; i < QI; ++i) *(u32x4*)(v_lds + (QRPI * i + lane / CH) * KS + 8 * (lane % CH)) = qraw[i];
+#pragma unroll
+    for (int kk = 0; kk < DK; ++kk)
+        qf[kk] = row_ok ? *(const u32x4*)(v_lds + col * KS + 32 * kk + 8 * grp) : u32x4{0, 0, 0, 0};
+    // One step at key kbase; MORE: a next step exists and its loads are issued here.  The
+    // last step is a separate copy, so that in the others every load is unconditional and
+    // the compiler waits for exactly the loads each use needs.
+    auto step = [&](int kbase, auto more_tag) {
+        constexpr bool more = decltype(more_tag)::value;
         const int knext = kbase + STRIDE;
-        const bool more = knext < T.kv_end;
 
         // ---- (KROWS) K through the wave's LDS area: rows in, MFMA operands out (lane:
         // key 16b + col, d = 32kk + 8grp .. +8); V reuses the area after Q K^T ----
@@ -881,7 +905,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
 #pragma unroll
             for (int b = 0; b < KB; ++b)
                 if (bad_cur & (1 << b)) s[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (more) {
+        if constexpr (more) {
             bad_nxt = check_pages(pg_nxt);
             load_k(pg_nxt);
         }
@@ -899,7 +923,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
             }
             *(u32x4*)(v_lds + (j * KPJ + vkey) * VS + 8 * vch) = w;
         }
-        if (more) {
+        if constexpr (more) {
             load_v(pg_nxt);
             bad_cur = bad_nxt;
             if (knext + STRIDE < T.kv_end) pages_of(knext + STRIDE, pg_nxt);
@@ -960,7 +984,9 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
                 oacc[db] = mfma16_pv(va, pf, oacc[db]);
             }
         }
-    }
+    };
+    for (; kbase + STRIDE < T.kv_end; kbase += STRIDE) step(kbase, std::true_type{});
+    if (kbase < T.kv_end) step(kbase, std::false_type{});
 
     if (bad_seen && lane == 0) *A.err_flag = 1;
 

@@ -205,7 +205,8 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
                            std::to_string(O.tiles.size()) + ", " + std::to_string(O.merges.size()) +
                            "): create and bind a new plan");
     S.partial_rows = O.partial_rows;  // the workspace layout stays as bound
-    plan->sched = std::move(S);
+    std::swap(plan->sched, S);
+    rpa::recycle_schedule(&S);  // the previous schedule's buffers serve the next update
     if (plan->staging && !plan->sched.tiles.empty())
         std::memcpy(static_cast<char*>(plan->staging) + plan->off_tiles, plan->sched.tiles.data(),
                     plan->sched.tiles.size() * sizeof(rpa::Tile));

@@ -87,7 +87,18 @@ void order_wide_for_xcds(std::vector<Piece>& wide) {
     wide.swap(out);
 }
 
+// Work vectors of the calling thread, kept between calls: a plan is rebuilt for every
+// decode step (rpa_plan_update), and fresh multi-page buffers each time would cost more
+// in page faults than the planning itself.
+thread_local Schedule t_sched;
+thread_local std::vector<QTile> base;
+thread_local std::vector<Piece> wide, narrow;
+
 }  // namespace
+
+void recycle_schedule(Schedule* s) {
+    if (s && s->tiles.capacity() > t_sched.tiles.capacity()) std::swap(*s, t_sched);
+}
 
 int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
                    const int32_t* kv_page_indptr, const int32_t* kv_last_page_len, Schedule* out,
@@ -105,7 +116,20 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     if (G > kMaxGroup) return fail(err, E_SHAPE, "query group %ld exceeds %ld heads per kv head", G, kMaxGroup);
     if (p.max_kv_splits < 0) return fail(err, E_ARG, "max_kv_splits must be >= 0");
 
-    Schedule S;
+    Schedule& S = t_sched;
+    S.tiles.clear();
+    S.merges.clear();
+    S.partial_rows = 0;
+    S.tokens_per_tile = S.block_m = S.block_n = 0;
+    S.wide_tiles = S.narrow_tiles = 0;
+    S.fused = false;
+    S.max_splits = 1;
+    S.narrow_max_rows = 0;
+    S.narrow_split = false;
+    S.total_q = S.visible_pairs = S.kv_tokens = 0;
+    base.clear();
+    wide.clear();
+    narrow.clear();
     S.block_n = block_n_for(p.head_dim);
     S.block_m = block_m_for(p.head_dim);
     S.tokens_per_tile = S.block_m / G;
@@ -114,7 +138,7 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     if (batch > 0 && (qo_indptr[0] != 0 || kv_page_indptr[0] != 0))
         return fail(err, E_INDPTR, "qo_indptr[0] (%ld) and kv_page_indptr[0] (%ld) must be 0", qo_indptr[0],
                     kv_page_indptr[0]);
-    std::vector<QTile> base;
+    base.reserve(size_t(batch) * p.num_kv_heads);
     for (int32_t b = 0; b < batch; ++b) {
         if (qo_indptr[b + 1] < qo_indptr[b]) return fail(err, E_INDPTR, "qo_indptr decreases at %ld", b);
         if (kv_page_indptr[b + 1] < kv_page_indptr[b])
@@ -187,16 +211,18 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     }
 
     // ---- expand into pieces ------------------------------------------------------------
-    std::vector<Piece> pieces;
-    pieces.reserve(base.size());
     int64_t part_next = 0;
     for (size_t i = 0; i < base.size(); ++i) {
         const QTile& q = base[i];
-        const int64_t nchunks = std::max<int64_t>(1, ceil_div(q.kv_end, kChunkKeys));
-        int32_t ns = int32_t(std::max<int64_t>(1, ceil_div(q.kv_end, C)));
-        if (p.max_kv_splits > 0) ns = std::min(ns, p.max_kv_splits);
-        const int64_t per = ceil_div(nchunks, ns) * kChunkKeys;  // keys per piece
-        ns = int32_t(std::max<int64_t>(1, ceil_div(q.kv_end, per)));
+        int32_t ns = 1;
+        int64_t per = int64_t(q.kv_end);  // keys per piece
+        if (q.kv_end > C) {  // (a key range within one piece needs no division)
+            const int64_t nchunks = ceil_div(q.kv_end, kChunkKeys);
+            ns = int32_t(ceil_div(q.kv_end, C));
+            if (p.max_kv_splits > 0) ns = std::min(ns, p.max_kv_splits);
+            per = ceil_div(nchunks, ns) * kChunkKeys;
+            ns = int32_t(std::max<int64_t>(1, ceil_div(q.kv_end, per)));
+        }
         const int32_t rows = q.q_count * G;
         if (ns > 1) {
             Merge m{};
@@ -230,8 +256,10 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
                 if (ns > 1) S.narrow_split = true;
             }
             // cost ~ keys walked (wide tiles: rounded up to whole blocks) plus a fixed overhead
-            const int64_t gran = t.kind == kWide ? BN : (p.narrow_valu ? kValuKeys : kWaveKeys);
-            pieces.push_back({t, ceil_div(t.kv_end - t.kv_begin, gran) * gran + 64});
+            // (every path steps through keys in blocks of 32)
+            static_assert(kValuKeys == 32 && kWaveKeys == 32 && block_n_for(0) == 32, "32-key steps");
+            const int64_t keys = ((int64_t(t.kv_end) - t.kv_begin + 31) & ~int64_t(31)) + 64;
+            (t.kind == kWide ? wide : narrow).push_back({t, keys});
         }
         if (ns > 1) part_next += int64_t(ns) * rows;
     }
@@ -239,8 +267,6 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     S.partial_rows = part_next;
 
     // ---- launch order: wide tiles (one kernel), then narrow tiles (another) ----------------
-    std::vector<Piece> wide, narrow;
-    for (auto& pc : pieces) (pc.t.kind == kWide ? wide : narrow).push_back(pc);
     // A few small narrow tiles beside many wide ones (the last tokens of short prompts)
     // would cost a second launch for little work: they run in the wide launch instead,
     // where a tile of up to 16 rows is a valid, partly empty wide tile.
@@ -260,7 +286,8 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
         }
     }
     // Narrow tiles read their keys once: longest first (LPT), ties in natural order.
-    std::stable_sort(narrow.begin(), narrow.end(), [](const Piece& a, const Piece& b) { return a.cost > b.cost; });
+    auto longer = [](const Piece& a, const Piece& b) { return a.cost > b.cost; };
+    if (!std::is_sorted(narrow.begin(), narrow.end(), longer)) std::stable_sort(narrow.begin(), narrow.end(), longer);
     order_wide_for_xcds(wide);
     S.wide_tiles = int64_t(wide.size());
     S.tiles.reserve(wide.size() + narrow.size());
@@ -283,7 +310,7 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
         for (auto& pc : wide) S.tiles.push_back(pc.t);
         for (auto& pc : narrow) S.tiles.push_back(pc.t);
     }
-    *out = std::move(S);
+    std::swap(*out, S);  // out's previous buffers are reused by the next call
     return OK;
 }
 

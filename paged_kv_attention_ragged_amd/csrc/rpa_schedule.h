@@ -99,4 +99,8 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
                    const int32_t* kv_page_indptr, const int32_t* kv_last_page_len, Schedule* out,
                    std::string* err);
 
+// Hand a schedule that is no longer needed back to the calling thread's planner, whose
+// next build_schedule reuses its buffers (a decode loop re-plans every step).
+void recycle_schedule(Schedule* s);
+
 }  // namespace rpa

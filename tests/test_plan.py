@@ -404,3 +404,26 @@ def test_empty_batch_and_zero_query_sequences():
     b = lengths_batch([0, 0], [5, 0])
     info = make_plan(b).info
     assert info["num_tiles"] == 0 and info["total_q"] == 0
+
+
+def test_planner_buffer_reuse_leaves_no_stale_state():
+    """The planner keeps its work buffers between calls (per thread) and reuses the
+    buffers of schedules replaced by rpa_plan_update: plans built in any order, and a
+    plan updated back and forth, equal freshly built ones."""
+    cases = [lengths_batch([8192] * 4 + [1] * 256, [8192] * 4 + [4096] * 256, H=64, Hk=8),
+             lengths_batch([1] * 128, [1024] * 128),
+             lengths_batch(W.short_prompt_lengths(), W.short_prompt_lengths(), H=32, Hk=8),
+             lengths_batch([17, 3, 5, 1], [17, 30, 5, 48], D=64)]
+    fresh = [make_plan(c).tiles() for c in cases]
+    for c, f in list(zip(cases, fresh))[::-1] + list(zip(cases, fresh)):
+        assert np.array_equal(make_plan(c).tiles(), f)
+    # decode steps: every sequence one token longer, then back
+    a = lengths_batch([1] * 64, [300] * 64, H=32, Hk=8)
+    b2 = lengths_batch([1] * 64, [301] * 64, H=32, Hk=8)
+    p = make_plan(a)
+    ta, tb = p.tiles(), make_plan(b2).tiles()
+    for _ in range(3):
+        p.update(b2.qo_indptr, b2.kv_page_indptr, b2.kv_last_page_len)
+        assert np.array_equal(p.tiles(), tb)
+        p.update(a.qo_indptr, a.kv_page_indptr, a.kv_last_page_len)
+        assert np.array_equal(p.tiles(), ta)

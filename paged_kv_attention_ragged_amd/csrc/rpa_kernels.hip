@@ -1264,7 +1264,7 @@ void attn_narrow_valu_kernel(AttnArgs A) {
     valu_tile<D, BF16, RM>(A, T, smem);
 }
 
-// Wide tiles: two workgroups per CU (two waves per SIMD).
+// Wide tiles: three workgroups per CU (three waves per SIMD; see kWideSlots).
 template <int D, bool BF16>
 __global__ __launch_bounds__(kWideWaves * 64) __attribute__((amdgpu_waves_per_eu(kWideWavesPerEU)))
 void attn_wide_kernel(AttnArgs A) {

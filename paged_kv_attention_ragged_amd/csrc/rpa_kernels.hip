@@ -716,10 +716,15 @@ __device__ __forceinline__ void narrow_combine_store(const AttnArgs& A, const Ti
 // 16-column MFMA block.  The 4 waves split the key range: wave w takes the
 // kWaveKeys-key steps w, w+4, w+8, ... of [kv_begin, kv_end), each with its own running max,
 // sum and O, and the waves are combined through LDS at the end.
-//   * K is loaded in whole rows (each load instruction reads KPJ complete rows)
-//     and passed through the wave's LDS area into the A operand of
-//     v_mfma_f32_16x16x32 (lane l: key 16b + l%16, 8 consecutive d): loads that
-//     touched 16 half rows each made shared-prefix decode 14% slower;
+//   * K goes into the A operand of v_mfma_f32_16x16x32 (lane l: key 16b + l%16, 8
+//     consecutive d) either in whole rows through the wave's LDS area (KROWS; each
+//     load instruction reads KPJ complete rows -- loads that touch 16 half rows
+//     each made shared-prefix decode 14% slower) or, when the plan splits narrow
+//     tiles and the last step sits on the merge's critical path, straight from
+//     memory into the operand registers;
+//   * page ids are scalar loads requested a step ahead, K/V loads carry no
+//     condition, and Q is staged through LDS before the key loop, so that the
+//     compiler's waits in the loop are exact (see the body);
 //   * V is staged in its natural [key][d] layout (fp16; bf16 is converted on the
 //     way) and read back transposed with ds_read_b64_tr_b16: within each 16-lane
 //     group, lane j receives element j%4 of the 8-byte rows addressed by lanes

@@ -61,7 +61,8 @@ typedef enum {
     RPA_E_WORKSPACE = 6,       /* workspace too small or misaligned               */
     RPA_E_UNSUPPORTED = 7,     /* valid request the library does not implement    */
     RPA_E_HIP = 8,             /* a HIP runtime call failed (message has details) */
-    RPA_E_PAGE_OOB = 9         /* a page index outside [0, num_pages)             */
+    RPA_E_PAGE_OOB = 9,        /* a page index outside [0, num_pages)             */
+    RPA_E_V_RANGE = 10         /* bf16 V above 65504 met by the fp16 P V product  */
 } rpa_status;
 
 typedef enum { RPA_F16 = 0, RPA_BF16 = 1 } rpa_dtype;
@@ -106,10 +107,34 @@ typedef struct {
 } rpa_plan_info_t;
 
 /*
- * Plan (the host half of begin_forward): validate the ragged lengths and build
- * the work schedule.  Host-only: no HIP call is made, so it also runs where no
- * GPU is present.  The schedule depends only on the lengths and parameters,
- * never on page ids, so equal lengths give equal schedules.
+ * Workspace size bound (flashinfer issue #323, "How are prefill and decode kernels
+ * different?": the repro allocates one uint8 workspace buffer before it builds the
+ * wrapper and calls begin_forward).  Writes to *bytes_out an upper bound on
+ * rpa_plan_info().workspace_bytes over every batch of `batch` sequences holding
+ * `total_q` query tokens and `total_pages` pages (the sum of their page counts) in
+ * all, whatever the individual lengths, for these params.  A caller can allocate
+ * the workspace once from it and bind any such plan into it.  Host-only.
+ * The bound is loose by design: it covers splitting a few long sequences into
+ * many pieces and the empty tiles that align wide tiles to XCDs.
+ * Errors: E_ARG (NULL pointer, negative size), E_SHAPE.
+ */
+rpa_status rpa_workspace_bytes(const rpa_params* params, int32_t batch, int64_t total_q, int64_t total_pages,
+                               size_t* bytes_out);
+
+/*
+ * Plan (the host half of begin_forward in flashinfer issue #323's repro, which
+ * takes qo_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len, the head
+ * counts, head_dim and page_size): validate the ragged lengths and build the work
+ * schedule.  Host-only: no HIP call is made, so it also runs where no GPU is
+ * present.  The schedule depends only on the lengths and parameters, never on
+ * page ids, so equal lengths give equal schedules.  The path of a query row
+ * (wide tiles of up to 128 rows, or narrow decode tiles of up to 16) is chosen
+ * per sequence: a sequence whose q_len * G rows fit one narrow tile is narrow,
+ * every tile of a longer one is wide; narrow tiles whose K/V total at most 8 MiB
+ * run as wide tiles when the batch has wide tiles.  A ragged prefill batch and
+ * its twin padded to equal lengths (llama.cpp discussion #15958, "Pad for
+ * prefill stage?") thus give bit-identical real rows when the ragged batch has a
+ * sequence of more than 16 rows and neither run splits key ranges.
  *   qo_indptr_h        host int32 [batch+1]; [0] == 0, non-decreasing
  *   kv_page_indptr_h   host int32 [batch+1]; [0] == 0, non-decreasing
  *   kv_last_page_len_h host int32 [batch]; in [1, page_size] for a sequence with pages
@@ -120,11 +145,13 @@ rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_
                            const int32_t* kv_page_indptr_h, const int32_t* kv_last_page_len_h,
                            rpa_plan** out);
 
-/* Summary of a plan (sizes, tile shape, work counts). */
+/* Summary of a plan (sizes, tile shape, work counts): the auxiliary data that
+ * begin_forward builds in flashinfer issue #323, made inspectable.  Host-only. */
 rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
 
 /*
- * Copy of the plan's work items for inspection: up to `cap` records of 16
+ * Copy of the plan's work items for inspection (tests; host-only; no passage of
+ * the pages names this call): up to `cap` records of 16
  * int32 each into `out_h` (host), in launch order: the wide records, then the
  * narrow ones, or, when the plan has both kinds (and narrow_kernel is 0), both
  * in one launch with narrow records in blocks of 8 between blocks of 8 wide ones.
@@ -140,8 +167,10 @@ rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
 rpa_status rpa_plan_tiles(const rpa_plan* plan, int32_t* out_h, int64_t cap, int64_t* n_out);
 
 /*
- * Bind (the device half of begin_forward): upload the schedule into the
- * caller's workspace and remember the page-index array.
+ * Bind (the device half of begin_forward in flashinfer issue #323: the wrapper is
+ * built over a caller-allocated workspace and begin_forward receives the device
+ * kv_page_indices): upload the schedule into the caller's workspace and remember
+ * the page-index array.
  *   kv_page_indices_d  device int32 [kv_page_indptr[batch]], borrowed until the
  *                      plan is destroyed or bound again
  *   num_pages          pages in the cache (rows of its leading axis); a page index
@@ -156,7 +185,9 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
                          void* workspace_d, size_t workspace_bytes, void* stream);
 
 /*
- * Run (forward): attention for every query row of the plan.
+ * Run (forward in flashinfer issue #323's repro: q and the paged kv_cache in, the
+ * output out, repeatable after one begin_forward): attention for every query row
+ * of the plan.
  *   q         device [total_q][num_qo_heads][head_dim], dtype of the plan
  *   kv_cache  device [num_pages][2][page_size][num_kv_heads][head_dim], same dtype
  *   o         device [total_q][num_qo_heads][head_dim], same dtype (written)
@@ -194,27 +225,41 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
 
 /*
  * Enqueue on `stream` the copy of the plan's current schedule into its workspace
- * (the same copy rpa_plan_bind makes; it also clears the error flag and the split
- * counters).  One hipMemcpyAsync from pinned host memory, so it can be captured
- * into a HIP graph.
+ * (the tile records and zeroed split counters, as rpa_plan_bind copies them; the
+ * error word is left as it is).  One hipMemcpyAsync from pinned host memory, so it
+ * can be captured into a HIP graph (the second half of the auxiliary-data reuse
+ * in flashinfer issue #323: begin_forward once, forward per step).
  * Errors: E_ARG (unbound plan), E_HIP.
  */
 rpa_status rpa_plan_upload(const rpa_plan* plan, void* stream);
 
 /*
- * Error flag of a bound plan: synchronises `stream`, then reports whether any
- * run since the last bind met a page index outside [0, num_pages)
- * (*flag_out = 1, and RPA_E_PAGE_OOB is returned) or not (*flag_out = 0).
+ * Error word of a bound plan.  The pages show no error convention beyond the
+ * repro's assertions (flashinfer issue #323); a kernel cannot return a status, so
+ * the runs OR bits into a word of the workspace that this call reads and clears.
+ * Synchronises `stream`, then writes to *flag_out the bits raised by the runs
+ * since the last bind or check (rpa_plan_upload does not clear them):
+ *   1  a page index outside [0, num_pages) was met; its keys read as zero K and V
+ *      (returns RPA_E_PAGE_OOB);
+ *   2  a bf16 V value above 65504, the largest fp16 value, was read by the fp16
+ *      P V product and saturated there: the rows that read it are wrong (returns
+ *      RPA_E_V_RANGE unless bit 1 is also set).  bf16 V below 2^-14 rounds toward
+ *      zero there, an absolute error under 2^-24, and raises nothing.  The VALU
+ *      narrow kernel (narrow_kernel = 1) multiplies in fp32 and never raises it.
+ * 0 returns RPA_OK.
+ * Errors: E_ARG (NULL, unbound plan), E_HIP, E_PAGE_OOB, E_V_RANGE.
  */
 rpa_status rpa_plan_check(const rpa_plan* plan, void* stream, int32_t* flag_out);
 
-/* Free a plan's host memory.  The caller first makes sure no run using it is
- * still in flight.  NULL is ignored. */
+/* Free a plan's host memory (end_forward in flashinfer issue #323's repro).  The
+ * caller first makes sure no run using it is still in flight.  NULL is ignored. */
 void rpa_plan_destroy(rpa_plan* plan);
 
 /*
  * Host-side check of a page table (tests and debugging): every index of every
- * sequence inside [0, num_pages).  Host pointers only.
+ * sequence inside [0, num_pages), the pool of pages the cache holds
+ * (flashinfer issue #323's repro: kv_page_indices index the leading axis of
+ * kv_cache).  Host pointers only.
  * Errors: E_ARG, E_INDPTR, E_PAGE_OOB.
  */
 rpa_status rpa_validate_page_table(int32_t batch, const int32_t* kv_page_indptr_h,

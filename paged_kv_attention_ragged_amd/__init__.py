@@ -29,7 +29,8 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "rpa.h")
 
 STATUS = {0: "RPA_OK", 1: "RPA_E_ARG", 2: "RPA_E_SHAPE", 3: "RPA_E_INDPTR", 4: "RPA_E_LAST_PAGE_LEN",
           5: "RPA_E_QLEN_GT_KVLEN", 6: "RPA_E_WORKSPACE", 7: "RPA_E_UNSUPPORTED", 8: "RPA_E_HIP",
-          9: "RPA_E_PAGE_OOB"}
+          9: "RPA_E_PAGE_OOB", 10: "RPA_E_V_RANGE"}
+ERR_PAGE, ERR_V_RANGE = 1, 2  # bits of a plan's error word (rpa_plan_check)
 
 
 class RPAError(RuntimeError):
@@ -70,6 +71,7 @@ def load():
         st = ctypes.c_int
         sig = {
             "rpa_plan_create": (st, [ctypes.POINTER(_Params), i32, P, P, P, ctypes.POINTER(P)]),
+            "rpa_workspace_bytes": (st, [ctypes.POINTER(_Params), i32, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
             "rpa_plan_info": (st, [P, ctypes.POINTER(_Info)]),
             "rpa_plan_tiles": (st, [P, P, i64, ctypes.POINTER(i64)]),
             "rpa_plan_bind": (st, [P, P, i64, P, ctypes.c_size_t, P]),
@@ -136,6 +138,23 @@ def validate_page_table(kv_page_indptr, kv_page_indices, num_pages: int):
                                           int(num_pages)))
 
 
+def _params(num_qo_heads, num_kv_heads, head_dim, page_size=16, dtype="f16", causal=True, sm_scale=None,
+            max_kv_splits=0, num_cus=0, narrow_kernel="mfma", kv_shared=False) -> _Params:
+    return _Params(num_qo_heads, num_kv_heads, head_dim, page_size, _dtype_code(dtype), 1 if causal else 0,
+                   0.0 if sm_scale is None else float(sm_scale), max_kv_splits, num_cus,
+                   {"mfma": 0, "valu": 1}[narrow_kernel], 1 if kv_shared else 0)
+
+
+def workspace_bytes(batch: int, total_q: int, total_pages: int, **params) -> int:
+    """Upper bound on the workspace of any plan for `batch` sequences with `total_q`
+    query tokens and `total_pages` pages in all (keyword params as for Plan)."""
+    p = _params(**params)
+    out = ctypes.c_size_t()
+    _check(load().rpa_workspace_bytes(ctypes.byref(p), int(batch), int(total_q), int(total_pages),
+                                      ctypes.byref(out)))
+    return int(out.value)
+
+
 class Plan:
     """A schedule for one ragged batch (host page-table lengths), reusable across runs."""
 
@@ -148,10 +167,8 @@ class Plan:
         self._kp = _host_i32(kv_page_indptr)
         self._kl = _host_i32(kv_last_page_len)
         self.batch = len(self._qo) - 1
-        self.params = _Params(num_qo_heads, num_kv_heads, head_dim, page_size, _dtype_code(dtype),
-                              1 if causal else 0, 0.0 if sm_scale is None else float(sm_scale),
-                              max_kv_splits, num_cus, {"mfma": 0, "valu": 1}[narrow_kernel],
-                              1 if kv_shared else 0)
+        self.params = _params(num_qo_heads, num_kv_heads, head_dim, page_size, dtype, causal, sm_scale,
+                              max_kv_splits, num_cus, narrow_kernel, kv_shared)
         h = ctypes.c_void_p()
         p = lambda a: a.ctypes.data if a.size else None
         _check(lib.rpa_plan_create(ctypes.byref(self.params), self.batch, p(self._qo), p(self._kp), p(self._kl),
@@ -240,14 +257,18 @@ class Plan:
             stream = torch.cuda.current_stream()
         _check(load().rpa_plan_upload(self._h, stream.cuda_stream))
 
-    def check(self, stream=None) -> bool:
-        """Synchronise and report whether a run met an out-of-range page index (raises)."""
+    def check(self, stream=None, raise_on_error: bool = True) -> int:
+        """Synchronise, read and clear the plan's error word (ERR_PAGE: an out-of-range
+        page index; ERR_V_RANGE: bf16 V above the fp16 range).  Raises RPAError when a
+        bit is set, unless raise_on_error is False; returns the bits."""
         import torch
         if stream is None:
             stream = torch.cuda.current_stream()
         flag = ctypes.c_int32()
-        _check(load().rpa_plan_check(self._h, stream.cuda_stream, ctypes.byref(flag)))
-        return True
+        rc = load().rpa_plan_check(self._h, stream.cuda_stream, ctypes.byref(flag))
+        if rc != 0 and (raise_on_error or flag.value == 0):
+            _check(rc)
+        return int(flag.value)
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:

@@ -21,9 +21,7 @@ struct rpa_plan {
     rpa_params params{};
     int32_t batch = 0;
     rpa::Schedule sched;
-    // layout of the workspace image (byte offsets)
-    // [tiles][error flag, split-group counters][partial LSE][partial O]
-    size_t off_tiles = 0, off_err = 0, off_counters = 0, off_part_lse = 0, off_part_o = 0, ws_bytes = 0;
+    rpa::WorkspaceLayout ws_layout{};  // byte offsets within the workspace
     // bound state
     const int32_t* page_idx_d = nullptr;
     int64_t num_pages = 0;
@@ -45,8 +43,6 @@ rpa_status set_err(rpa_status s, const std::string& msg) {
 rpa_status hip_err(hipError_t e, const char* what) {
     return set_err(RPA_E_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
-
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // ---- kernel timing (benchmarks only) ----
 std::mutex g_prof_mu;
@@ -106,13 +102,9 @@ rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_
     plan->params = *params;
     plan->batch = batch;
     const auto& S = plan->sched;
-    plan->off_tiles = 0;
-    plan->off_err = align256(S.tiles.size() * sizeof(rpa::Tile));
-    plan->off_counters = plan->off_err + 64;
-    plan->off_part_lse = plan->off_counters + align256(S.merges.size() * sizeof(int32_t) + 1);
-    plan->off_part_o = plan->off_part_lse + align256(size_t(S.partial_rows) * sizeof(float));
-    plan->ws_bytes = plan->off_part_o + align256(size_t(S.partial_rows) * params->head_dim * sizeof(float));
-    plan->staging_bytes = plan->off_part_lse;  // tiles, then the zeroed flag and counters
+    plan->ws_layout = rpa::workspace_layout(int64_t(S.tiles.size()), int64_t(S.merges.size()), S.partial_rows,
+                                            params->head_dim);
+    plan->staging_bytes = plan->ws_layout.off_part_lse;  // tiles, then the zeroed counters and error word
     *out = plan;
     return RPA_OK;
 }
@@ -127,10 +119,24 @@ rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out) {
     out->block_n = S.block_n;
     out->tokens_per_tile = S.tokens_per_tile;
     out->partial_rows = S.partial_rows;
-    out->workspace_bytes = plan->ws_bytes;
+    out->workspace_bytes = plan->ws_layout.bytes;
     out->total_q = S.total_q;
     out->visible_pairs = S.visible_pairs;
     out->kv_tokens = S.kv_tokens;
+    return RPA_OK;
+}
+
+rpa_status rpa_workspace_bytes(const rpa_params* params, int32_t batch, int64_t total_q, int64_t total_pages,
+                               size_t* bytes_out) {
+    if (!params || !bytes_out) return set_err(RPA_E_ARG, "params and bytes_out must be non-NULL");
+    *bytes_out = 0;
+    rpa::PlanParams pp{params->num_qo_heads, params->num_kv_heads, params->head_dim, params->page_size,
+                       params->causal, params->max_kv_splits, params->num_cus, params->narrow_kernel};
+    rpa::ScheduleBound B{};
+    std::string err;
+    const int rc = rpa::schedule_bound(pp, batch, total_q, total_pages, &B, &err);
+    if (rc != 0) return set_err(rpa_status(rc), err);
+    *bytes_out = rpa::workspace_layout(B.tiles, B.merges, B.partial_rows, params->head_dim).bytes;
     return RPA_OK;
 }
 
@@ -154,10 +160,10 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
     if (!workspace_d) return set_err(RPA_E_ARG, "workspace must be non-NULL");
     if (reinterpret_cast<uintptr_t>(workspace_d) % 256 != 0)
         return set_err(RPA_E_WORKSPACE, "workspace must be 256-byte aligned");
-    if (workspace_bytes < plan->ws_bytes) {
+    if (workspace_bytes < plan->ws_layout.bytes) {
         char buf[160];
         std::snprintf(buf, sizeof(buf), "workspace of %zu bytes is too small: this plan needs %zu bytes",
-                      workspace_bytes, plan->ws_bytes);
+                      workspace_bytes, plan->ws_layout.bytes);
         return set_err(RPA_E_WORKSPACE, buf);
     }
     if (!plan->staging) {
@@ -168,7 +174,8 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
         }
         char* img = static_cast<char*>(plan->staging);
         std::memset(img, 0, plan->staging_bytes);
-        if (!S.tiles.empty()) std::memcpy(img + plan->off_tiles, S.tiles.data(), S.tiles.size() * sizeof(rpa::Tile));
+        if (!S.tiles.empty())
+            std::memcpy(img + plan->ws_layout.off_tiles, S.tiles.data(), S.tiles.size() * sizeof(rpa::Tile));
     }
     hipError_t e = hipMemcpyAsync(workspace_d, plan->staging, plan->staging_bytes, hipMemcpyHostToDevice,
                                   static_cast<hipStream_t>(stream));
@@ -196,19 +203,27 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
     }
     if (rc != 0) return set_err(rpa_status(rc), err);
     const auto& O = plan->sched;
+    // The launch a captured graph replays was configured from the old schedule: the
+    // grid (tile counts), the kernel (wide / narrow / mixed, K loads for split narrow
+    // tiles) and, on the VALU kernel, its row capacity.  All must stay.
+    auto valu_rows = [](int32_t r) { return r <= 2 ? 2 : r <= 4 ? 4 : 8; };
+    const bool same_kernel = S.narrow_split == O.narrow_split &&
+                             (P.narrow_kernel != 1 || S.narrow_tiles == 0 ||
+                              valu_rows(S.narrow_max_rows) == valu_rows(O.narrow_max_rows));
     if (S.tiles.size() != O.tiles.size() || S.wide_tiles != O.wide_tiles || S.fused != O.fused ||
-        S.merges.size() != O.merges.size() ||
+        S.narrow_tiles != O.narrow_tiles || S.merges.size() != O.merges.size() || !same_kernel ||
         S.partial_rows > O.partial_rows)
         return set_err(RPA_E_UNSUPPORTED,
                        "the new lengths need another launch shape (" + std::to_string(S.tiles.size()) + " tiles, " +
                            std::to_string(S.merges.size()) + " split groups instead of " +
                            std::to_string(O.tiles.size()) + ", " + std::to_string(O.merges.size()) +
+                           (same_kernel ? "" : "; another kernel configuration") +
                            "): create and bind a new plan");
     S.partial_rows = O.partial_rows;  // the workspace layout stays as bound
     std::swap(plan->sched, S);
     rpa::recycle_schedule(&S);  // the previous schedule's buffers serve the next update
     if (plan->staging && !plan->sched.tiles.empty())
-        std::memcpy(static_cast<char*>(plan->staging) + plan->off_tiles, plan->sched.tiles.data(),
+        std::memcpy(static_cast<char*>(plan->staging) + plan->ws_layout.off_tiles, plan->sched.tiles.data(),
                     plan->sched.tiles.size() * sizeof(rpa::Tile));
     return RPA_OK;
 }
@@ -216,7 +231,8 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
 rpa_status rpa_plan_upload(const rpa_plan* plan, void* stream) {
     if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
     if (!plan->bound) return set_err(RPA_E_ARG, "plan is not bound to a workspace (rpa_plan_bind)");
-    hipError_t e = hipMemcpyAsync(plan->ws, plan->staging, plan->staging_bytes, hipMemcpyHostToDevice,
+    // tiles and zeroed split counters; the error word after them is left as it is
+    hipError_t e = hipMemcpyAsync(plan->ws, plan->staging, plan->ws_layout.off_flags, hipMemcpyHostToDevice,
                                   static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(schedule upload)");
     return RPA_OK;
@@ -232,22 +248,23 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
     hipStream_t st = static_cast<hipStream_t>(stream);
     const float scale = P.sm_scale > 0.f ? P.sm_scale : 1.f / std::sqrt(float(P.head_dim));
     rpa::LaunchAttn L{};
-    L.a.tiles = reinterpret_cast<const rpa::Tile*>(plan->ws + plan->off_tiles);
+    const rpa::WorkspaceLayout& WL = plan->ws_layout;
+    L.a.tiles = reinterpret_cast<const rpa::Tile*>(plan->ws + WL.off_tiles);
     L.a.page_idx = plan->page_idx_d;
     L.a.num_pages = int32_t(plan->num_pages);
     L.a.q = static_cast<const uint16_t*>(q);
     L.a.kv = static_cast<const uint16_t*>(kv_cache);
     L.a.o = static_cast<uint16_t*>(o);
     L.a.lse = lse;
-    L.a.part_o = reinterpret_cast<float*>(plan->ws + plan->off_part_o);
-    L.a.part_lse = reinterpret_cast<float*>(plan->ws + plan->off_part_lse);
+    L.a.part_o = reinterpret_cast<float*>(plan->ws + WL.off_part_o);
+    L.a.part_lse = reinterpret_cast<float*>(plan->ws + WL.off_part_lse);
     L.a.H = P.num_qo_heads;
     L.a.Hkv = P.num_kv_heads;
     L.a.G = P.num_qo_heads / P.num_kv_heads;
     L.a.c_log2 = float(double(scale) * 1.4426950408889634);
     L.a.causal = P.causal;
-    L.a.err_flag = reinterpret_cast<int32_t*>(plan->ws + plan->off_err);
-    L.a.counters = reinterpret_cast<int32_t*>(plan->ws + plan->off_counters);
+    L.a.err_flag = reinterpret_cast<int32_t*>(plan->ws + WL.off_flags);
+    L.a.counters = reinterpret_cast<int32_t*>(plan->ws + WL.off_counters);
     L.head_dim = P.head_dim;
     L.bf16 = P.dtype == RPA_BF16;
     L.n_tiles = int64_t(S.tiles.size());
@@ -306,11 +323,21 @@ rpa_status rpa_plan_check(const rpa_plan* plan, void* stream, int32_t* flag_out)
     if (!plan->bound) return set_err(RPA_E_ARG, "plan is not bound");
     int32_t flag = 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(&flag, plan->ws + plan->off_err, sizeof(flag), hipMemcpyDeviceToHost, st);
+    char* word = plan->ws + plan->ws_layout.off_flags;
+    hipError_t e = hipMemcpyAsync(&flag, word, sizeof(flag), hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess && flag != 0) {  // read and clear: the next check covers later runs
+        static const int32_t zero = 0;
+        e = hipMemcpyAsync(word, &zero, sizeof(zero), hipMemcpyHostToDevice, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+    }
     if (e != hipSuccess) return hip_err(e, "reading the error flag");
     *flag_out = flag;
-    if (flag) return set_err(RPA_E_PAGE_OOB, "a page index outside [0, num_pages) was met; its keys read as zero");
+    if (flag & rpa::kErrPage)
+        return set_err(RPA_E_PAGE_OOB, "a page index outside [0, num_pages) was met; its keys read as zero");
+    if (flag & rpa::kErrVRange)
+        return set_err(RPA_E_V_RANGE, "a bf16 V value above 65504 (the largest fp16 value) was met; the P V "
+                                      "product saturated it, so the rows that read it are wrong");
     return RPA_OK;
 }
 

@@ -139,19 +139,36 @@ __device__ __forceinline__ float elem16(uint32_t w, int hi) {
 
 __device__ __forceinline__ uint32_t pack_p(float a, float b) { return pack_out<false>(a, b); }
 
-// 16-bit element e (0..7) of a 16-byte vector, widened to an fp32 bit pattern
-// for bf16 (exact) -- used only for the bf16 -> fp16 conversion of V.
-__device__ __forceinline__ float bf16_elem(u32x4 v, int e) {
-    const uint32_t w = v[e >> 1];
-    return __builtin_bit_cast(float, (e & 1) ? (w & 0xffff0000u) : (w << 16));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// One packed bf16 pair as a packed fp16 pair: exact for |x| in [2^-14, 65504] and
+// for zeros, infinities and NaN; round-toward-zero below 2^-14 (absolute error
+// < 2^-24); saturation to 65504 above it, which no correct output allows.  No bf16
+// value lies strictly between 65280 and 65536, so an fp16 result of magnitude 65504
+// (0x7bff) comes from saturation only.  vmax keeps the largest fp16 magnitude
+// pattern produced (per 16-bit half: sign cleared, one packed max); a tile that
+// produced 0x7bff or more (saturated, infinite or NaN V) raises kErrVRange.
+__device__ __forceinline__ uint32_t v_pair_fp16(uint32_t w, u16x2& vmax) {
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, w << 16),
+                                                                               __builtin_bit_cast(float, w & 0xffff0000u)));
+    vmax = __builtin_elementwise_max(vmax, __builtin_bit_cast(u16x2, h & 0x7fff7fffu));
+    return h;
 }
 
-// One packed bf16 pair as a packed fp16 pair: exact for |x| in [2^-14, 65504];
-// round-toward-zero below (error < 2^-24) and saturation to 65504 above.
-__device__ __forceinline__ uint32_t v_pair_fp16(uint32_t w) {
-    const fp16x2 h = __builtin_amdgcn_cvt_pkrtz(__builtin_bit_cast(float, w << 16),
-                                                __builtin_bit_cast(float, w & 0xffff0000u));
-    return __builtin_bit_cast(uint32_t, h);
+// fp16 magnitude pattern of 65504, the value bf16 V above the fp16 range saturates to.
+constexpr unsigned short kF16Saturated = 0x7bff;
+
+// Error bits of a plan (device int32, OR-ed by any workgroup; see rpa_launch.h).
+__device__ __forceinline__ void raise_flag(int32_t* flag, int32_t bits) {
+    __hip_atomic_fetch_or(flag, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Whether any lane of the wave converted a bf16 V above 65504 (wave-uniform).
+__device__ __forceinline__ bool wave_v_big(u16x2 vmax) {
+    return __builtin_amdgcn_ballot_w64(vmax[0] >= kF16Saturated || vmax[1] >= kF16Saturated) != 0;
+}
+// Once per wave: raise kErrVRange if any lane converted a bf16 V above 65504.
+__device__ __forceinline__ void flag_v_range(int32_t* flag, u16x2 vmax) {
+    if (wave_v_big(vmax) && (threadIdx.x & 63) == 0) raise_flag(flag, kErrVRange);
 }
 
 // Value of lane l ^ 32: v_permlane32_swap exchanges the two 32-lane halves of a
@@ -372,9 +389,10 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             pg[j] = key0 < T.kv_len ? ((const_i32*)A.page_idx)[T.page_base + (key0 >> 4)] : 0;
         }
     };
-    // Request one unit into one slot.  A page index outside [0, num_pages) raises the
-    // error flag and reads page 0; bad_any then sends every later unit through the
-    // slow check in fix_unit, which zeroes that page's keys.
+    // Request one unit into one slot.  A page index outside [0, num_pages) reads page
+    // 0; bad_any then sends every later unit through the slow check in fix_unit, which
+    // zeroes that page's keys, and raises the error flag after the key loop (a store
+    // among the loads would make the compiler wait for them).
     const uint32_t lds_w = lds_addr(smem) + wave * GS;
     int bad_any = 0;
     auto load_unit = [&](int slot, const int (&pg)[IPW]) {
@@ -382,7 +400,6 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         for (int j = 0; j < IPW; ++j) {
             int p = pg[j];
             if ((unsigned)p >= (unsigned)A.num_pages) {
-                *A.err_flag = 1;
                 p = 0;
                 bad_any = 1;
             }
@@ -423,15 +440,20 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
                 w[j] = *(const u32x4*)(smem + slot * SLOT + MAT + (wave + 4 * j) * GS + 16 * lane);
         }
     };
-    auto v_fp16_write = [&](int slot, const u32x4 (&w)[IPW]) {
+    // vmax: largest fp16 |V| pattern converted from bf16, over the units of this tile
+    // (a slot converted past the last unit holds stale bytes and does not count)
+    u16x2 vmax = {0, 0};
+    auto v_fp16_write = [&](int slot, const u32x4 (&w)[IPW], bool live) {
         if constexpr (BF16) {
+            u16x2 umax = {0, 0};
 #pragma unroll
             for (int j = 0; j < IPW; ++j) {
                 u32x4 h;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = v_pair_fp16(w[j][e]);
+                for (int e = 0; e < 4; ++e) h[e] = v_pair_fp16(w[j][e], umax);
                 *(u32x4*)(smem + slot * SLOT + MAT + (wave + 4 * j) * GS + 16 * lane) = h;
             }
+            if (live) vmax = __builtin_elementwise_max(vmax, umax);
         }
     };
 
@@ -529,7 +551,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         if (more_req) {
             load_unit(ring(SL + NS - 1), pg_next);
         }
-        v_fp16_write(ring(SL + 1), vcv);
+        v_fp16_write(ring(SL + 1), vcv, u + 1 < nunits);
 
         // ---- one basic block: Q K^T (next unit) | exponentials | P V ----
         qk(ring(SL + 1), Sn);
@@ -582,7 +604,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             if (nunits > 1) sync_unit(1, 1, younger_than(1, NS - 2));
             u32x4 vcv[IPW];
             v_fp16_read(0, vcv);
-            v_fp16_write(0, vcv);
+            v_fp16_write(0, vcv, true);
             // Q rows into the operand layout, through ring slot NS - 1 (no unit is
             // requested into it before the barrier below): 16 rows per wave at a time,
             // at a stride of D * 2 + 16 bytes (conflict-free 16-byte reads).
@@ -617,6 +639,9 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             sa = sb;
         }
     }
+
+    if (bad_any && lane == 0) raise_flag(A.err_flag, kErrPage);
+    if constexpr (BF16) flag_v_range(A.err_flag, vmax);
 
     // ---- epilogue ----
     const float ltot = lsum + xor32(lsum);
@@ -753,11 +778,10 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     const int G = A.G;
     const int rows_valid = T.q_count * G;
     const int row = col;
-    const int tok = row / G, g = row - tok * G;
+    const int tok = row / G;
     const bool row_ok = row < rows_valid;
     const int pos = T.pos0 + tok;
     const int pos_min = T.pos0;
-    const int64_t orow = (int64_t)(T.q_row0 + tok) * A.H + T.kv_head * G + g;
     uint16_t* v_lds = reinterpret_cast<uint16_t*>(smem) + wave * KW * VS;
 
     // Q^T operand (B of 16x16x32): row `col`, d = 32kk + 8grp .. +8.  Read in whole
@@ -786,6 +810,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = -INFINITY, lsum = 0.f;
+    int v_big = 0;  // a bf16 V above 65504 was converted (wave-uniform; bf16 only)
 
     const int64_t ss = (int64_t)A.Hkv * D;  // elements between token slots
     const uint16_t* kvh = A.kv + (int64_t)T.kv_head * D;
@@ -917,17 +942,17 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
 
         // ---- stage V (fp16, natural layout) ----
         if (bad_cur || kbase + KW > T.kv_len) fix_v(kbase, bad_cur);
+        u16x2 vmax = {0, 0};  // largest fp16 |V| pattern of this step (bf16 only)
 #pragma unroll
         for (int j = 0; j < VJ; ++j) {
             u32x4 w = vf[j];
             if (BF16) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_elem(vf[j], 2 * e),
-                                                                                   bf16_elem(vf[j], 2 * e + 1)));
+                for (int e = 0; e < 4; ++e) w[e] = v_pair_fp16(vf[j][e], vmax);
             }
             *(u32x4*)(v_lds + (j * KPJ + vkey) * VS + 8 * vch) = w;
         }
+        if (BF16) v_big |= wave_v_big(vmax);
         if constexpr (more) {
             load_v(pg_nxt);
             bad_cur = bad_nxt;
@@ -993,7 +1018,8 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     for (; kbase + STRIDE < T.kv_end; kbase += STRIDE) step(kbase, std::true_type{});
     if (kbase < T.kv_end) step(kbase, std::false_type{});
 
-    if (bad_seen && lane == 0) *A.err_flag = 1;
+    if (bad_seen && lane == 0) raise_flag(A.err_flag, kErrPage);
+    if (v_big && lane == 0) raise_flag(A.err_flag, kErrVRange);
 
     // ---- combine the 4 waves ----
     lsum += __shfl_xor(lsum, 16);
@@ -1223,7 +1249,7 @@ __device__ __forceinline__ void valu_tile(const AttnArgs& A, const Tile& T, char
                 for (int e = 0; e < 8; ++e) oacc[r][e] = __builtin_fmaf(pr[r], v[e], oacc[r][e]);
         }
     }
-    if (bad_seen && lane == 0) *A.err_flag = 1;
+    if (bad_seen && lane == 0) raise_flag(A.err_flag, kErrPage);
 
     // ---- sum the key groups, then combine the 4 waves ----
 #pragma unroll

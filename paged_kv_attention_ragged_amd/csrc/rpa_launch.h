@@ -7,6 +7,12 @@
 
 namespace rpa {
 
+// Bits of a plan's error word (OR-ed by the kernels, read by rpa_plan_check).
+enum ErrBits : int32_t {
+    kErrPage = 1,    // a page index outside [0, num_pages): its keys read as zero K and V
+    kErrVRange = 2,  // a bf16 V value above the largest fp16 value (65504) entered P V
+};
+
 struct AttnArgs {
     const Tile* tiles;
     const int32_t* page_idx;  // kv_page_indices
@@ -20,7 +26,7 @@ struct AttnArgs {
     int32_t H, Hkv, G;
     float c_log2;             // sm_scale * log2(e)
     int32_t causal;
-    int32_t* err_flag;        // set to 1 when a page index is out of range
+    int32_t* err_flag;        // error word: ErrBits OR-ed atomically
     int32_t* counters;        // one per split group: pieces finished (reset to 0 by the last)
 };
 

@@ -96,6 +96,70 @@ thread_local std::vector<Piece> wide, narrow;
 
 }  // namespace
 
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+}  // namespace
+
+WorkspaceLayout workspace_layout(int64_t tiles, int64_t merges, int64_t partial_rows, int head_dim) {
+    WorkspaceLayout L{};
+    L.off_tiles = 0;
+    L.off_counters = align256(size_t(tiles) * sizeof(Tile));
+    L.off_flags = L.off_counters + align256(size_t(merges) * sizeof(int32_t));
+    L.off_part_lse = L.off_flags + 256;
+    L.off_part_o = L.off_part_lse + align256(size_t(partial_rows) * sizeof(float));
+    L.bytes = L.off_part_o + align256(size_t(partial_rows) * size_t(head_dim) * sizeof(float));
+    return L;
+}
+
+// Bounds (see build_schedule for the rules they follow):
+//  * query tiles: sequence b has ceil(q_b / TQ) <= floor(q_b / TQ) + 1 of them per kv
+//    head, and at most min(batch, total_q) sequences have queries, so there are at
+//    most H_kv (floor(total_q / TQ) + min(batch, total_q));
+//  * key ranges are split only when the query tiles number fewer than 2 N (N compute
+//    units).  The piece size C is then 256 keys if that gives fewer than 2 N pieces,
+//    else the largest multiple of 256 still giving at least 2 N; since
+//    ceil(k / C) <= 2 ceil(k / (C + 256)) for C >= 256, that is fewer than 4 N pieces.
+//    Pieces therefore number at most max(query tiles, 4 N - 1), split groups fewer
+//    than 2 N, and partial rows at most (pieces) x (rows of the largest tile);
+//  * XCD padding lays the wide tiles out in 8 runs padded to the longest, so the launch
+//    has at most 8 slots per piece.
+int schedule_bound(const PlanParams& p, int32_t batch, int64_t total_q, int64_t total_pages, ScheduleBound* out,
+                   std::string* err) {
+    if (!out || batch < 0 || total_q < 0 || total_pages < 0)
+        return fail(err, E_ARG, "batch, total_q and total_pages must be >= 0 and out non-NULL");
+    if (p.num_qo_heads < 1 || p.num_kv_heads < 1 || p.num_qo_heads % p.num_kv_heads != 0)
+        return fail(err, E_SHAPE, "num_qo_heads (%ld) must be a positive multiple of num_kv_heads (%ld)",
+                    p.num_qo_heads, p.num_kv_heads);
+    if (p.head_dim != 64 && p.head_dim != 128)
+        return fail(err, E_SHAPE, "head_dim %ld not supported (64 or 128)", p.head_dim);
+    if (p.page_size != kPageSize) return fail(err, E_SHAPE, "page_size %ld not supported (16)", p.page_size);
+    const int32_t G = p.num_qo_heads / p.num_kv_heads;
+    if (G > kMaxGroup) return fail(err, E_SHAPE, "query group %ld exceeds %ld heads per kv head", G, kMaxGroup);
+    if (p.max_kv_splits < 0) return fail(err, E_ARG, "max_kv_splits must be >= 0");
+    const int64_t TQ = block_m_for(p.head_dim) / G;
+    const int64_t seqs = std::min<int64_t>(batch, total_q);
+    const int64_t base = int64_t(p.num_kv_heads) * (total_q / TQ + seqs);
+    const int64_t n_cus = p.num_cus > 0 ? p.num_cus : 256;
+    const int64_t target = 2 * n_cus;
+    // no sequence has more than 16 total_pages keys, so no tile more than this many pieces
+    const int64_t max_chunks = (total_pages * kPageSize + kChunkKeys - 1) / kChunkKeys;
+    int64_t pieces = base, merges = 0, partial = 0;
+    if (p.max_kv_splits != 1 && base > 0 && max_chunks > 1) {
+        const int64_t split_tiles = std::min(base, target - 1);  // query tiles of a split plan
+        int64_t per_tile = max_chunks;
+        if (p.max_kv_splits > 1) per_tile = std::min<int64_t>(per_tile, p.max_kv_splits);
+        const int64_t split_pieces = std::min(2 * target - 1, split_tiles * per_tile);
+        pieces = std::max(base, split_pieces);
+        merges = split_tiles;
+        const int64_t max_rows = std::min<int64_t>(block_m_for(p.head_dim), G * std::min(total_q, TQ));
+        partial = split_pieces * max_rows;
+    }
+    out->tiles = kXcds * pieces;
+    out->merges = merges;
+    out->partial_rows = partial;
+    return OK;
+}
+
 void recycle_schedule(Schedule* s) {
     if (s && s->tiles.capacity() > t_sched.tiles.capacity()) std::swap(*s, t_sched);
 }
@@ -174,7 +238,13 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
                 t.page_base = kv_page_indptr[b];
                 // keys past the last query's position are masked for every row: skip them
                 t.kv_end = p.causal ? std::min(kv_len, t.pos0 + t.q_count) : kv_len;
-                t.kind = t.q_count * G <= (p.narrow_valu ? kValuRows : kNarrowRows) ? kNarrow : kWide;
+                // The path is chosen per sequence, not per tile: a sequence whose rows
+                // all fit one narrow tile (decode rows, a few tokens of few heads) is
+                // narrow; every tile of a longer sequence is wide, its partial last tile
+                // included.  A row's path (and so its rounding) then depends on its own
+                // sequence only: a padded batch and its ragged twin put each real row
+                // in tiles of the same kind, at the same offset.
+                t.kind = int64_t(q_len) * G <= (p.narrow_valu ? kValuRows : kNarrowRows) ? kNarrow : kWide;
                 base.push_back(t);
             }
     }
@@ -267,10 +337,12 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     S.partial_rows = part_next;
 
     // ---- launch order: wide tiles (one kernel), then narrow tiles (another) ----------------
-    // A few small narrow tiles beside many wide ones (the last tokens of short prompts)
-    // would cost a second launch for little work: they run in the wide launch instead,
-    // where a tile of up to 16 rows is a valid, partly empty wide tile.
-    if (!p.narrow_valu && !narrow.empty() && narrow.size() * kFoldRatio <= wide.size()) {
+    // A little narrow work beside wide tiles (the shortest prompts of a ragged prefill
+    // batch) would cost a second launch, or narrow workgroups in the mixed launch, for
+    // little work: it runs in the wide launch instead, where a tile of up to 16 rows is
+    // a valid, partly empty wide tile.  Then every row of such a batch takes the wide
+    // path, as it does in the batch padded to equal lengths.
+    if (!p.narrow_valu && !narrow.empty() && !wide.empty()) {
         int64_t keys = 0;
         for (const auto& pc : narrow) keys += pc.t.kv_end - pc.t.kv_begin;
         if (keys * int64_t(p.head_dim) * 4 <= kFoldBytes) {

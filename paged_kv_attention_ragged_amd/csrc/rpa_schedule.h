@@ -17,15 +17,14 @@ constexpr int kWaves = 4;       // wavefronts per narrow-tile workgroup
 constexpr int kWideWaves = 4;  // wavefronts per wide-tile workgroup, 32 query rows each
 constexpr int block_m_for(int head_dim) { return head_dim > 0 ? 32 * kWideWaves : 32 * kWideWaves; }
 
-constexpr int kNarrowRows = 16;  // tiles with at most this many rows take the narrow path
+constexpr int kNarrowRows = 16;  // sequences with at most this many rows (q_len * G) take the narrow path
 constexpr int kWaveKeys = 32;     // keys one wave handles per step on the narrow path
 constexpr int kValuRows = 8;      // narrow threshold when narrow tiles run on the VALU kernel
 constexpr int kValuKeys = 32;     // keys one wave handles per step on the VALU narrow path
 constexpr int kXcds = 8;          // MI355X: workgroup i of a launch runs on XCD i % 8
 constexpr int kChunkKeys = 256;   // split pieces start at multiples of this many keys
-// Narrow tiles join the wide launch when there are at most 1/kFoldRatio as many of
-// them as wide tiles and their K/V come to at most kFoldBytes.
-constexpr int kFoldRatio = 4;
+// Narrow tiles join the wide launch when the plan has wide tiles and the narrow
+// tiles' K/V come to at most kFoldBytes.
 constexpr int64_t kFoldBytes = int64_t(8) << 20;
 
 // Keys per inner block (unit) of the wide path, whatever the head_dim.
@@ -102,5 +101,25 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
 // Hand a schedule that is no longer needed back to the calling thread's planner, whose
 // next build_schedule reuses its buffers (a decode loop re-plans every step).
 void recycle_schedule(Schedule* s);
+
+// Upper bounds on the sizes of every schedule build_schedule can produce for a batch
+// of `batch` sequences holding `total_q` query tokens and `total_pages` pages in all,
+// whatever their individual lengths.
+struct ScheduleBound {
+    int64_t tiles;         // launch slots (split pieces and XCD padding included)
+    int64_t merges;        // split groups
+    int64_t partial_rows;  // fp32 partial rows
+};
+int schedule_bound(const PlanParams& p, int32_t batch, int64_t total_q, int64_t total_pages, ScheduleBound* out,
+                   std::string* err);
+
+// Byte layout of a plan's workspace: [tiles][split counters][error word][partial LSE]
+// [partial O].  rpa_plan_bind copies [0, off_part_lse) (tiles, zeroed counters, zeroed
+// error word); rpa_plan_upload copies [0, off_flags) only, so the error word keeps
+// what earlier runs raised until rpa_plan_check reads it.
+struct WorkspaceLayout {
+    size_t off_tiles, off_counters, off_flags, off_part_lse, off_part_o, bytes;
+};
+WorkspaceLayout workspace_layout(int64_t tiles, int64_t merges, int64_t partial_rows, int head_dim);
 
 }  // namespace rpa

@@ -118,6 +118,9 @@ def test_graph_captured_decode_loop_matches_eager_and_oracle():
         g.replay()
         torch.cuda.synchronize()
         assert flag.item() == 0
+        # the plan's error word (bad pages, bf16 V range) survives the graph's upload
+        # node and is read and cleared here, step by step
+        assert plan.check() == 0
         o_g, l_g = o_buf.clone(), l_buf.clone()
         # eager: a new plan for the same lengths over the same (already appended) cache
         e = rpa.Plan(d.qo_indptr, d.kv_page_indptr, d.kv_last_page_len, num_qo_heads=H, num_kv_heads=Hk,

@@ -101,13 +101,20 @@ def check_schedule(b: W.Batch, plan):
     for (a0, a1), (c0, c1) in zip(part_ranges, part_ranges[1:]):
         assert a1 <= c0
     assert info["partial_rows"] == n_part_rows
-    # 3. tile kind: narrow (decode-like path) exactly when a tile has at most 16 rows,
-    #    unless the plan folded its few, small narrow tiles into the wide launch
-    small = [r for r in t if 0 < r[F["q_count"]] * G <= 16]
-    if small and not any(r[F["kind"]] == 1 for r in t):
-        assert folded(t, b.head_dim, G)
+    # 3. tile kind, chosen per sequence: narrow (decode-like path) exactly for the tiles
+    #    of sequences whose q_len * G rows fit one narrow tile (16 rows; 8 on the VALU
+    #    kernel), unless the plan has wide tiles and the narrow ones carry at most 8 MiB
+    #    of K/V: then they run as wide tiles too
+    thr = 8 if plan.params.narrow_kernel == 1 else 16
+    real = [r for r in t if r[F["q_count"]] > 0]
+    narrow_seq = [int(q_lens[r[F["seq"]]]) * G <= thr for r in real]
+    if any(narrow_seq) and not any(r[F["kind"]] == 1 for r in t):
+        assert plan.params.narrow_kernel == 0 and not all(narrow_seq)
+        assert fold_bytes([r for r, n in zip(real, narrow_seq) if n], b.head_dim) <= FOLD_BYTES
     else:
-        assert all((r[F["kind"]] == 1) == (0 < r[F["q_count"]] * G <= 16) for r in t)
+        assert [int(r[F["kind"]]) for r in real] == [int(n) for n in narrow_seq]
+        if any(narrow_seq) and not all(narrow_seq) and plan.params.narrow_kernel == 0:
+            assert fold_bytes([r for r, n in zip(real, narrow_seq) if n], b.head_dim) > FOLD_BYTES
     # 4. launch order: all wide tiles (one kernel), then all narrow tiles (another).
     #    Narrow tiles go longest first (keys walked, rounded to 64).  Wide tiles go
     #    longest first in small launches; in larger ones, launch slot i runs on XCD
@@ -153,36 +160,41 @@ def check_schedule(b: W.Batch, plan):
     return t
 
 
-FOLD_RATIO, FOLD_BYTES = 4, 8 << 20
+FOLD_BYTES = 8 << 20
 
 
-def folded(t, D, G):
-    """Whether the narrow-size tiles of schedule t meet the rule for running in the wide
-    launch: at most a quarter as many as the other tiles, K/V of at most 8 MiB."""
-    small = [r for r in t if 0 < r[F["q_count"]] * G <= 16]
-    others = [r for r in t if r[F["q_count"]] * G > 16]
-    keys = sum(int(r[F["kv_end"]] - r[F["kv_begin"]]) for r in small)
-    return len(small) * FOLD_RATIO <= len(others) and keys * D * 4 <= FOLD_BYTES
+def fold_bytes(recs, D):
+    """K/V bytes of narrow tiles as the planner counts them for the fold rule."""
+    return sum(int(r[F["kv_end"]] - r[F["kv_begin"]]) for r in recs) * D * 4
 
 
-def test_few_small_narrow_tiles_join_the_wide_launch():
-    # short ragged prompts: the last few tokens of some prompts make tiles of <= 16 rows
-    b = lengths_batch(W.short_prompt_lengths(), W.short_prompt_lengths(), H=32, Hk=8)
+def test_small_narrow_work_joins_the_wide_launch():
+    # short ragged prompts: every tile is wide, the partial last tiles of long prompts
+    # (<= 16 rows) and the prompts of at most 4 tokens (4 heads per kv head) included
+    lens = W.short_prompt_lengths() + [1, 2, 4]
+    b = lengths_batch(lens, lens, H=32, Hk=8)
     t = make_plan(b).tiles()
     assert (t[:, F["kind"]] == 0).all() and ((t[:, F["q_count"]] * 4 <= 16) & (t[:, F["q_count"]] > 0)).any()
-    # decode rows beside long prompts are many and long: they keep the narrow kernel
-    m = lengths_batch([8192] * 4 + [1] * 256, [8192] * 4 + [4096] * 256, H=64, Hk=8)
+    # the same without any prompt of more than 16 rows: all narrow (no wide launch to join)
+    s = lengths_batch([1, 2, 4, 3], [1, 2, 4, 3], H=32, Hk=8)
+    assert (make_plan(s).tiles()[:, F["kind"]] == 1).all()
+    # a partial last tile of a long prompt is wide even when narrow tiles keep their kernel
+    m = lengths_batch([8192 + 2] * 4 + [1] * 256, [8192 + 2] * 4 + [4096] * 256, H=64, Hk=8)
     tm = make_plan(m).tiles()
-    assert ((tm[:, F["kind"]] == 1) == ((tm[:, F["q_count"]] > 0) & (tm[:, F["q_count"]] * 8 <= 16))).all()
-    # so do decode-only batches, and mixes where narrow tiles are not few
-    for c in (lengths_batch([1] * 128, [1024] * 128), lengths_batch([17, 3, 5, 1], [17, 30, 5, 48], D=64)):
-        tc = make_plan(c).tiles()
-        assert (tc[:, F["kind"]] == 1).any()
-    # the VALU decode kernel (a comparison) keeps every tile of its size
+    part = tm[(tm[:, F["q_count"]] == 2)]
+    assert len(part) == 32 and (part[:, F["kind"]] == 0).all()
+    # decode rows beside long prompts carry much K/V: they keep the narrow kernel
+    assert ((tm[:, F["kind"]] == 1) == ((tm[:, F["q_count"]] == 1))).all()
+    # so do decode-only batches
+    tc = make_plan(lengths_batch([1] * 128, [1024] * 128)).tiles()
+    assert (tc[:, F["kind"]] == 1).all()
+    # the VALU decode kernel (a comparison) keeps every sequence of its size (q_len * G <= 8)
     v = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=32, num_kv_heads=8,
                  head_dim=128, dtype="bf16", narrow_kernel="valu")
     tv = v.tiles()
-    assert ((tv[:, F["kind"]] == 1) == ((tv[:, F["q_count"]] > 0) & (tv[:, F["q_count"]] * 4 <= 8))).all()
+    ql = np.array(lens)[tv[:, F["seq"]]]
+    assert ((tv[:, F["kind"]] == 1) == ((tv[:, F["q_count"]] > 0) & (ql * 4 <= 8))).all()
+    assert (tv[:, F["kind"]] == 1).sum() >= 8 * 2  # at least the added prompts of 1 and 2 tokens
 
 
 def qo_row_in_seq(b, s, r0):
@@ -206,6 +218,7 @@ def qo_row_in_seq(b, s, r0):
 def test_schedule_properties(case, max_kv_splits):
     plan = make_plan(case, max_kv_splits=max_kv_splits)
     t = check_schedule(case, plan)
+    check_schedule(case, make_plan(case, max_kv_splits=max_kv_splits, narrow_kernel="valu"))
     if max_kv_splits == 1:
         assert (t[:, F["n_splits"]] == 1).all()
     if max_kv_splits == 3:
@@ -427,3 +440,88 @@ def test_planner_buffer_reuse_leaves_no_stale_state():
         assert np.array_equal(p.tiles(), tb)
         p.update(a.qo_indptr, a.kv_page_indptr, a.kv_last_page_len)
         assert np.array_equal(p.tiles(), ta)
+
+
+# ----------------------------------------------------------------------------------------------
+# Workspace bound: rpa_workspace_bytes(batch, total_q, total_pages) covers every plan of
+# those totals.
+# ----------------------------------------------------------------------------------------------
+
+def bound_of(b: W.Batch, **kw):
+    return rpa.workspace_bytes(b.batch, b.total_q, int(b.kv_page_indptr[-1]), num_qo_heads=b.num_qo_heads,
+                               num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, causal=b.causal, **kw)
+
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+SHAPES_WS = [(8, 1, 128), (32, 8, 128), (64, 8, 128), (8, 8, 64), (12, 1, 128), (16, 2, 64)]
+
+
+@settings(max_examples=80, deadline=None)
+@given(data=st.data())
+def test_workspace_bound_covers_random_batches(data):
+    H, Hk, D = data.draw(st.sampled_from(SHAPES_WS))
+    causal = data.draw(st.booleans())
+    kw = dict(max_kv_splits=data.draw(st.sampled_from([0, 1, 2, 3])),
+              num_cus=data.draw(st.sampled_from([0, 0, 4, 64, 1024])),
+              narrow_kernel=data.draw(st.sampled_from(["mfma", "valu"])))
+    B = data.draw(st.integers(1, 24))
+    q = data.draw(st.lists(st.integers(0, 300), min_size=B, max_size=B))
+    extra = data.draw(st.lists(st.sampled_from([0, 1, 15, 16, 200, 1000, 5000]), min_size=B, max_size=B))
+    kv = [qq + e if causal else max(1, e) if qq else e for qq, e in zip(q, extra)]
+    b = lengths_batch(q, kv, H=H, Hk=Hk, D=D, causal=causal)
+    need = make_plan(b, **kw).info["workspace_bytes"]
+    assert need <= bound_of(b, **kw)
+
+
+@pytest.mark.parametrize("num_cus", [0, 32])
+def test_workspace_bound_covers_adversarial_length_mixes(num_cus):
+    """Fixed totals, lengths placed to maximise each term of the bound: one long
+    sequence holding every query (largest split tiles), every query a decode row over
+    one long sequence's pages, and one very long prompt beside many one-token prompts
+    (the longest XCD padding run)."""
+    for H, Hk in ((8, 1), (32, 8), (64, 8)):
+        B, T, P = 64, 64 * 16, 64 * 300
+        cases = [
+            ([T] + [0] * (B - 1), [16 * P] + [0] * (B - 1)),                       # one sequence has all
+            ([16] * B, [16 * 300] * B),                                            # even
+            ([1] * (B - 1) + [T - B + 1], [16] * (B - 1) + [16 * (P - B + 1)]),    # one long prompt
+            ([T // B] * B, [16 * (P - B + 1)] + [16] * (B - 1)),                   # keys on one sequence
+        ]
+        for q, kv in cases:
+            assert sum(q) == T and sum(W.pages_for(k) for k in kv) == P
+            b = lengths_batch(q, kv, H=H, Hk=Hk)
+            for splits in (0, 1, 4):
+                need = make_plan(b, max_kv_splits=splits, num_cus=num_cus).info["workspace_bytes"]
+                assert need <= bound_of(b, max_kv_splits=splits, num_cus=num_cus), (H, q[:3], kv[:3], splits)
+
+
+def test_workspace_bound_of_the_decode_workload_is_usable():
+    # the flashinfer #323 repro's shape: 128 decode rows over 64 pages each
+    b = lengths_batch([1] * 128, [1024] * 128)
+    need, bound = make_plan(b).info["workspace_bytes"], bound_of(b)
+    assert need <= bound <= 128 << 20  # within the repro's 128 MiB workspace
+    with pytest.raises(rpa.RPAError) as e:
+        rpa.workspace_bytes(4, 10, 10, num_qo_heads=8, num_kv_heads=3, head_dim=128)
+    assert e.value.status == "RPA_E_SHAPE"
+    with pytest.raises(rpa.RPAError) as e:
+        rpa.workspace_bytes(-1, 10, 10, num_qo_heads=8, num_kv_heads=1, head_dim=128)
+    assert e.value.status == "RPA_E_ARG"
+
+
+def test_plan_update_refuses_another_kernel_configuration():
+    """A captured graph replays the launch configured for the bound schedule; update
+    must refuse lengths that would need another kernel: the VALU kernel's row
+    capacity (2 -> 4 rows per tile) here, with the tile counts unchanged."""
+    b1 = lengths_batch([1] * 8, [700] * 8, H=4, Hk=2)  # 2 rows per tile
+    b2 = lengths_batch([2] * 8, [700] * 8, H=4, Hk=2)  # 4 rows per tile
+    p = make_plan(b1, narrow_kernel="valu", max_kv_splits=1)
+    before = p.tiles().copy()
+    with pytest.raises(rpa.RPAError) as e:
+        p.update(b2.qo_indptr, b2.kv_page_indptr, b2.kv_last_page_len)
+    assert e.value.status == "RPA_E_UNSUPPORTED" and "kernel" in str(e.value)
+    assert np.array_equal(p.tiles(), before)
+    # the MFMA narrow kernel takes both row counts with one configuration
+    m = make_plan(b1, max_kv_splits=1)
+    m.update(b2.qo_indptr, b2.kv_page_indptr, b2.kv_last_page_len)
+    assert np.array_equal(m.tiles(), make_plan(b2, max_kv_splits=1).tiles())

@@ -207,6 +207,30 @@ rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, vo
                    void* stream);
 
 /*
+ * Run without a workspace, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same computation and kernels as rpa_run, for a plan that need not be bound: the
+ * schedule, the split counters, the error word and the fp32 partials live in a
+ * 16 MiB scratch array that the library holds in device memory (one per GPU, from
+ * the first call on that GPU until the process ends).  Each call copies the plan's
+ * schedule into it from the plan's host memory (hipMemcpyAsync; the plan must not
+ * be updated or destroyed before `stream` has passed this call) and clears the
+ * counters and error word with a kernel, then launches the attention kernels.
+ *   kv_page_indices_d, num_pages  as for rpa_plan_bind
+ *   q, kv_cache, o, lse           as for rpa_run
+ *   err_flag_d  device int32 the kernels OR error bits into (1: page index out of
+ *               range, 2: bf16 V above 65504; see rpa_plan_check), never cleared
+ *               by the library; or NULL to drop them
+ * Calls that overlap on one GPU (other streams, other threads) share the scratch
+ * and race: order them.  No allocation of any kind (device, pinned or library).
+ * Errors: E_WORKSPACE (the plan needs more than 16 MiB of scratch, checked before
+ * any HIP call; rpa_plan_info().workspace_bytes tells), E_ARG, E_HIP.
+ */
+rpa_status rpa_run_noalloc(const rpa_plan* plan, const int32_t* kv_page_indices_d, int64_t num_pages,
+                           const void* q, const void* kv_cache, void* o, float* lse, int32_t* err_flag_d,
+                           void* stream);
+
+/*
  * Re-plan in place for new lengths of the same batch (a decode step: every
  * sequence one token longer), keeping the launch shape: the new schedule must
  * have the same number of tiles, wide tiles and split groups, and no more partial

@@ -76,6 +76,7 @@ def load():
             "rpa_plan_tiles": (st, [P, P, i64, ctypes.POINTER(i64)]),
             "rpa_plan_bind": (st, [P, P, i64, P, ctypes.c_size_t, P]),
             "rpa_run": (st, [P, P, P, P, P, P]),
+            "rpa_run_noalloc": (st, [P, P, i64, P, P, P, P, P, P]),
             "rpa_plan_check": (st, [P, P, ctypes.POINTER(i32)]),
             "rpa_plan_destroy": (None, [P]),
             "rpa_validate_page_table": (st, [i32, P, P, i64]),
@@ -239,6 +240,20 @@ class Plan:
         _check(load().rpa_run(self._h, q.data_ptr(), kv_cache.data_ptr(), out.data_ptr(),
                               lse.data_ptr() if lse is not None else None, stream.cuda_stream))
         return (out, lse) if return_lse else out
+
+    def run_noalloc(self, q, kv_cache, kv_page_indices, out, lse=None, err_flag=None, stream=None):
+        """rpa_run_noalloc: the same computation without a bound workspace (the library's
+        static device scratch holds the schedule and partials).  Every tensor is the
+        caller's: q, kv_cache, kv_page_indices (int32), out, and optional lse (fp32)
+        and err_flag (int32 [1], OR-ed with error bits)."""
+        import torch
+        if stream is None:
+            stream = torch.cuda.current_stream(q.device)
+        ptr = lambda t: t.data_ptr() if t is not None and t.numel() else None
+        _check(load().rpa_run_noalloc(self._h, ptr(kv_page_indices), int(kv_cache.shape[0]), q.data_ptr(),
+                                      kv_cache.data_ptr(), out.data_ptr(), ptr(lse), ptr(err_flag),
+                                      stream.cuda_stream))
+        return out
 
     def update(self, qo_indptr, kv_page_indptr, kv_last_page_len):
         """Re-plan in place for new lengths with the same launch shape (raises

@@ -63,6 +63,84 @@ hipEvent_t prof_event() {
     return e;
 }
 
+// Enqueue the plan's attention kernels over a workspace image at `ws` (tiles, split
+// counters and partials at the offsets of plan->ws_layout); error bits go to err_flag.
+rpa_status launch_plan(const rpa_plan* plan, char* ws, const int32_t* page_idx, int64_t num_pages, int32_t* err_flag,
+                       const void* q, const void* kv_cache, void* o, float* lse, hipStream_t st) {
+    const auto& S = plan->sched;
+    const rpa_params& P = plan->params;
+    const float scale = P.sm_scale > 0.f ? P.sm_scale : 1.f / std::sqrt(float(P.head_dim));
+    rpa::LaunchAttn L{};
+    const rpa::WorkspaceLayout& WL = plan->ws_layout;
+    L.a.tiles = reinterpret_cast<const rpa::Tile*>(ws + WL.off_tiles);
+    L.a.page_idx = page_idx;
+    L.a.num_pages = int32_t(num_pages);
+    L.a.q = static_cast<const uint16_t*>(q);
+    L.a.kv = static_cast<const uint16_t*>(kv_cache);
+    L.a.o = static_cast<uint16_t*>(o);
+    L.a.lse = lse;
+    L.a.part_o = reinterpret_cast<float*>(ws + WL.off_part_o);
+    L.a.part_lse = reinterpret_cast<float*>(ws + WL.off_part_lse);
+    L.a.H = P.num_qo_heads;
+    L.a.Hkv = P.num_kv_heads;
+    L.a.G = P.num_qo_heads / P.num_kv_heads;
+    L.a.c_log2 = float(double(scale) * 1.4426950408889634);
+    L.a.causal = P.causal;
+    L.a.err_flag = err_flag;
+    L.a.counters = reinterpret_cast<int32_t*>(ws + WL.off_counters);
+    L.head_dim = P.head_dim;
+    L.bf16 = P.dtype == RPA_BF16;
+    L.n_tiles = int64_t(S.tiles.size());
+
+    // One kernel for the wide tiles (tiles[0, wide)), one for the narrow tiles after them,
+    // or, for a plan with both kinds, one mixed kernel over the interleaved tiles.
+    // Profiling: an event pair stamped by each dispatch itself (start and end of the kernel).
+    const bool prof = g_prof_on;
+    ProfEv e0{nullptr, nullptr, 0}, e1{nullptr, nullptr, 1};
+    hipError_t e = hipSuccess;
+    // Split key ranges put each narrow tile's last step on the latency-critical path of
+    // the merge, where the extra LDS round trip of row-wise K loads costs more than their
+    // better coalescing gains; unsplit (many-tile) decode is throughput-bound.
+    L.k_rows = !S.narrow_split;
+    // Pages read by one sequence only are streamed past L2 (non-temporal), which keeps the
+    // schedule, page indices and Q resident; shared pages stay cached.
+    L.kv_stream = P.kv_shared == 0;
+    if (S.fused) {  // wide and narrow tiles interleaved in one launch (timed as "wide")
+        if (prof) {
+            e0.a = prof_event();
+            e0.b = prof_event();
+        }
+        e = rpa::launch_mixed(L, st, e0.a, e0.b);
+        if (e != hipSuccess) return hip_err(e, "mixed attention kernel launch");
+    } else if (S.wide_tiles > 0) {
+        if (prof) {
+            e0.a = prof_event();
+            e0.b = prof_event();
+        }
+        L.n_tiles = S.wide_tiles;
+        e = rpa::launch_wide(L, st, e0.a, e0.b);
+        if (e != hipSuccess) return hip_err(e, "wide attention kernel launch");
+    }
+    if (!S.fused && S.narrow_tiles > 0) {
+        if (prof) {
+            e1.a = prof_event();
+            e1.b = prof_event();
+        }
+        rpa::LaunchAttn N = L;
+        N.a.tiles = L.a.tiles + S.wide_tiles;
+        N.n_tiles = S.narrow_tiles;
+        e = P.narrow_kernel == 1 ? rpa::launch_narrow_valu(N, S.narrow_max_rows, st, e1.a, e1.b)
+                                 : rpa::launch_narrow(N, st, e1.a, e1.b);
+        if (e != hipSuccess) return hip_err(e, "narrow attention kernel launch");
+    }
+    if (prof) {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (e0.a && e0.b) g_prof_events.push_back(e0);
+        if (e1.a && e1.b) g_prof_events.push_back(e1);
+    }
+    return RPA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,81 +319,46 @@ rpa_status rpa_plan_upload(const rpa_plan* plan, void* stream) {
 rpa_status rpa_run(const rpa_plan* plan, const void* q, const void* kv_cache, void* o, float* lse, void* stream) {
     if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
     if (!plan->bound) return set_err(RPA_E_ARG, "plan is not bound to a workspace (rpa_plan_bind)");
-    const auto& S = plan->sched;
-    if (S.tiles.empty()) return RPA_OK;
+    if (plan->sched.tiles.empty()) return RPA_OK;
     if (!q || !kv_cache || !o) return set_err(RPA_E_ARG, "q, kv_cache and o must be non-NULL");
-    const rpa_params& P = plan->params;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const float scale = P.sm_scale > 0.f ? P.sm_scale : 1.f / std::sqrt(float(P.head_dim));
-    rpa::LaunchAttn L{};
-    const rpa::WorkspaceLayout& WL = plan->ws_layout;
-    L.a.tiles = reinterpret_cast<const rpa::Tile*>(plan->ws + WL.off_tiles);
-    L.a.page_idx = plan->page_idx_d;
-    L.a.num_pages = int32_t(plan->num_pages);
-    L.a.q = static_cast<const uint16_t*>(q);
-    L.a.kv = static_cast<const uint16_t*>(kv_cache);
-    L.a.o = static_cast<uint16_t*>(o);
-    L.a.lse = lse;
-    L.a.part_o = reinterpret_cast<float*>(plan->ws + WL.off_part_o);
-    L.a.part_lse = reinterpret_cast<float*>(plan->ws + WL.off_part_lse);
-    L.a.H = P.num_qo_heads;
-    L.a.Hkv = P.num_kv_heads;
-    L.a.G = P.num_qo_heads / P.num_kv_heads;
-    L.a.c_log2 = float(double(scale) * 1.4426950408889634);
-    L.a.causal = P.causal;
-    L.a.err_flag = reinterpret_cast<int32_t*>(plan->ws + WL.off_flags);
-    L.a.counters = reinterpret_cast<int32_t*>(plan->ws + WL.off_counters);
-    L.head_dim = P.head_dim;
-    L.bf16 = P.dtype == RPA_BF16;
-    L.n_tiles = int64_t(S.tiles.size());
+    return launch_plan(plan, plan->ws, plan->page_idx_d, plan->num_pages,
+                       reinterpret_cast<int32_t*>(plan->ws + plan->ws_layout.off_flags), q, kv_cache, o, lse,
+                       static_cast<hipStream_t>(stream));
+}
 
-    // One kernel for the wide tiles (tiles[0, wide)), one for the narrow tiles after them,
-    // or, for a plan with both kinds, one mixed kernel over the interleaved tiles.
-    // Profiling: an event pair stamped by each dispatch itself (start and end of the kernel).
-    const bool prof = g_prof_on;
-    ProfEv e0{nullptr, nullptr, 0}, e1{nullptr, nullptr, 1};
-    hipError_t e = hipSuccess;
-    // Split key ranges put each narrow tile's last step on the latency-critical path of
-    // the merge, where the extra LDS round trip of row-wise K loads costs more than their
-    // better coalescing gains; unsplit (many-tile) decode is throughput-bound.
-    L.k_rows = !S.narrow_split;
-    // Pages read by one sequence only are streamed past L2 (non-temporal), which keeps the
-    // schedule, page indices and Q resident; shared pages stay cached.
-    L.kv_stream = P.kv_shared == 0;
-    if (S.fused) {  // wide and narrow tiles interleaved in one launch (timed as "wide")
-        if (prof) {
-            e0.a = prof_event();
-            e0.b = prof_event();
-        }
-        e = rpa::launch_mixed(L, st, e0.a, e0.b);
-        if (e != hipSuccess) return hip_err(e, "mixed attention kernel launch");
-    } else if (S.wide_tiles > 0) {
-        if (prof) {
-            e0.a = prof_event();
-            e0.b = prof_event();
-        }
-        L.n_tiles = S.wide_tiles;
-        e = rpa::launch_wide(L, st, e0.a, e0.b);
-        if (e != hipSuccess) return hip_err(e, "wide attention kernel launch");
+rpa_status rpa_run_noalloc(const rpa_plan* plan, const int32_t* kv_page_indices_d, int64_t num_pages, const void* q,
+                           const void* kv_cache, void* o, float* lse, int32_t* err_flag_d, void* stream) {
+    if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
+    const auto& S = plan->sched;
+    const rpa::WorkspaceLayout& WL = plan->ws_layout;
+    // size first: a plan too large for the static scratch is refused before any HIP call
+    if (WL.bytes > rpa::kStaticScratchBytes) {
+        char buf[200];
+        std::snprintf(buf, sizeof(buf),
+                      "this plan needs %zu bytes of scratch; rpa_run_noalloc has %zu: use rpa_plan_bind and "
+                      "rpa_run with a workspace", WL.bytes, size_t(rpa::kStaticScratchBytes));
+        return set_err(RPA_E_WORKSPACE, buf);
     }
-    if (!S.fused && S.narrow_tiles > 0) {
-        if (prof) {
-            e1.a = prof_event();
-            e1.b = prof_event();
-        }
-        rpa::LaunchAttn N = L;
-        N.a.tiles = L.a.tiles + S.wide_tiles;
-        N.n_tiles = S.narrow_tiles;
-        e = P.narrow_kernel == 1 ? rpa::launch_narrow_valu(N, S.narrow_max_rows, st, e1.a, e1.b)
-                                 : rpa::launch_narrow(N, st, e1.a, e1.b);
-        if (e != hipSuccess) return hip_err(e, "narrow attention kernel launch");
-    }
-    if (prof) {
-        std::lock_guard<std::mutex> lk(g_prof_mu);
-        if (e0.a && e0.b) g_prof_events.push_back(e0);
-        if (e1.a && e1.b) g_prof_events.push_back(e1);
-    }
-    return RPA_OK;
+    if (num_pages < 0 || num_pages > INT32_MAX) return set_err(RPA_E_ARG, "num_pages outside [0, 2^31)");
+    if (S.tiles.empty()) return RPA_OK;
+    if (!kv_page_indices_d) return set_err(RPA_E_ARG, "kv_page_indices must be non-NULL");
+    if (num_pages < 1) return set_err(RPA_E_ARG, "num_pages must be >= 1 for a non-empty batch");
+    if (!q || !kv_cache || !o) return set_err(RPA_E_ARG, "q, kv_cache and o must be non-NULL");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* scratch = nullptr;
+    hipError_t e = rpa::static_scratch(&scratch);
+    if (e != hipSuccess) return hip_err(e, "locating the static scratch (hipGetSymbolAddress)");
+    char* ws = static_cast<char*>(scratch);
+    // the schedule, from the plan's host memory; then counters and error word cleared by a
+    // kernel (what the previous call left there is not zero)
+    e = hipMemcpyAsync(ws + WL.off_tiles, S.tiles.data(), S.tiles.size() * sizeof(rpa::Tile),
+                       hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(schedule into the static scratch)");
+    int32_t* cleared = reinterpret_cast<int32_t*>(ws + WL.off_counters);
+    e = rpa::launch_clear(cleared, int64_t((WL.off_part_lse - WL.off_counters) / sizeof(int32_t)), st);
+    if (e != hipSuccess) return hip_err(e, "clear kernel launch");
+    int32_t* flag = err_flag_d ? err_flag_d : reinterpret_cast<int32_t*>(ws + WL.off_flags);
+    return launch_plan(plan, ws, kv_page_indices_d, num_pages, flag, q, kv_cache, o, lse, st);
 }
 
 rpa_status rpa_plan_check(const rpa_plan* plan, void* stream, int32_t* flag_out) {

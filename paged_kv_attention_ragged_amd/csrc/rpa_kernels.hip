@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -1505,6 +1506,41 @@ hipError_t launch_append(const AppendArgs& A, hipStream_t stream) {
     if (A.n_new <= 0) return hipSuccess;
     hipLaunchKernelGGL(append_kv_kernel, dim3((unsigned)A.n_new), dim3(256), 0, stream, A);
     return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void clear_i32_kernel(int32_t* p, int64_t n) {
+    const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+hipError_t launch_clear(int32_t* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(clear_i32_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+// The scratch of rpa_run_noalloc (tile records, split counters, error word, partials),
+// for callers that cannot allocate device memory.  Each GPU the library runs on holds
+// its own copy at its own address; calls that overlap on one GPU share it and race.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {  // once per device, with that device current
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_merge(const MergeArgs& M, bool bf16, hipStream_t stream) {

@@ -75,5 +75,14 @@ hipError_t launch_mixed(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0,
 hipError_t launch_narrow_valu(const LaunchAttn& L, int max_rows, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_merge(const MergeArgs& M, bool bf16, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& A, hipStream_t stream);
+// Zero n int32 at p (a kernel: no memset node in a captured graph).
+hipError_t launch_clear(int32_t* p, int64_t n, hipStream_t stream);
+
+// Device scratch of rpa_run_noalloc: a file-scope __device__ array of this many bytes,
+// one copy per GPU, held until the process ends.
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+// Device address of the current device's copy of that array, resolved once per device
+// with hipGetSymbolAddress (the array's name in host code is only a host-side stand-in).
+hipError_t static_scratch(void** ptr);
 
 }  // namespace rpa

@@ -1,31 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark: ragged paged-KV attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-Default workload (the headline line): decode, batch 128 x q_len 1 x kv_len
-1024, 8 qo / 1 kv heads, D 128, fp16, 64 contiguous pages per sequence (the
-flashinfer issue #323 repro shape).  A step is one forward call (one launch of
-the narrow-tile kernel, split pieces merged inside it) over the whole batch, with the plan built once
+Headline line: decode, batch 128 x q_len 1 x kv_len 1024, 8 qo / 1 kv heads, D
+128, fp16, 64 contiguous pages per sequence (the flashinfer issue #323 repro
+shape).  A step is one forward call (one launch of the narrow-tile kernel, split
+pieces merged inside it) over the whole batch, with the plan built once
 beforehand (as begin_forward is in the pages) and its build time reported
 separately.  Eight copies of the KV cache are rotated so consecutive steps do
-not hit in the 256 MB last-level cache.
+not hit in the 256 MB last-level cache; a cache-resident ("hot") time with one
+copy is reported beside it.
 
 value = KV GB/s = unique KV bytes of valid tokens / step time.
-roofline = the decode kernel's (attn_narrow_kernel) algorithmic bytes per
-launch (KV + Q + O + LSE + page table) / its average duration from HIP events
-stamped by each dispatch on the launch stream, against 8 TB/s HBM.
-cpu_baseline = the fp64 oracle on a bounded sample of the same batch.
-prefill = a secondary measurement on the long-prompt part of the mixed
-workload (4 causal prompts x 8192, 64 qo / 8 kv heads, bf16): TFLOP/s and
-fraction of the 2.5 PFLOP/s dense bf16/fp16 MFMA peak.
-secondary = the pages' other workloads (ragged vs padded short prompts, the
-shared-prefix suffix prefill and decode step directly and as a cascade, the
-mixed long batch's decode rows and the whole batch).
+roofline = the decode kernel's algorithmic bytes per launch (KV + Q + O + LSE +
+page table) / its average duration from HIP events stamped by each dispatch on
+the launch stream, against 8 TB/s HBM; also against the HBM read rate measured
+on the box (floors.hbm_stream_gbs).  traffic = HBM bytes per launch from the
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/, while it was taken on
+the current kernel source.
+floors = measured on the box in this run: an empty launch, a plain HBM read
+stream, the decode kernel's paged gather alone (same grid, no arithmetic), and
+dense bf16 MFMA throughput.
+prefill = the long prompts of the mixed workload (4 causal prompts x 8192, 64 qo /
+8 kv heads, bf16) against the 2.5 PFLOP/s dense bf16 MFMA peak.
+secondary = the pages' other workloads, each with median / mean per call, kernel
+time and a roofline entry: ragged vs padded short prompts; the shared-prefix
+suffix prefill and a decode step (direct and as a cascade); a long shared
+prefix; the decode loop eager vs graph; the VALU decode kernel; the mixed long
+batch's decode rows and whole batch; a batch-size sweep at 8192 total tokens.
+cpu_baseline = the fp64 oracle on a bounded sample of the headline batch, plus a
+labelled row sample of the mixed long batch.
 """
 import argparse
+import ctypes
 import json
 import os
+import platform
 import sys
 import time
 
@@ -38,9 +49,9 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "attention TFLOP/s (prefill) + KV GB/s (decode), % roofline, 1 MI355X"
 
-
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_attention_ragged_amd", "csrc", "rpa_kernels.hip")
 COUNTERS = os.path.join(ROOT, "profiles", "attn_narrow_kernel_decode_b128_kv1024_counters.txt")
+FLOORS_LIB = os.path.join(ROOT, "paged_kv_attention_ragged_amd", "librpa_floors.so")
 
 
 def log(msg):
@@ -54,7 +65,7 @@ def kernel_source_hash():
 
 
 def recorded_traffic():
-    """HBM bytes per launch of the decode kernel on this workload, from the
+    """HBM bytes per launch of the decode kernel on the headline workload, from the
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/, or None when that
     summary is missing or was taken on a different kernel source."""
     try:
@@ -84,18 +95,196 @@ def calibrate_copy():
     log("copy calibration: 3 x %d bytes" % n)
 
 
-def algorithmic(b, info):
-    """Algorithmic work of one forward over batch b: visible-pair flops and bytes."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+# ----------------------------------------------------------------------------------------------
+# Algorithmic work and rooflines
+# ----------------------------------------------------------------------------------------------
+
+def algorithmic(b, info, unique_kv_tokens=None):
+    """Algorithmic work of one forward over batch b: (flops, KV bytes, all bytes).
+    Flops: 4 D per visible (query, key, qo head) pair.  Bytes: K/V of valid tokens,
+    each physical slot once (unique_kv_tokens when pages are shared, else the sum of
+    kv_len), + Q + O + LSE + page table."""
     elt = 2
     D, H, Hk = b.head_dim, b.num_qo_heads, b.num_kv_heads
     flops = 4.0 * D * info["visible_pairs"]
-    kv_bytes = float(info["kv_tokens"]) * Hk * D * 2 * elt  # unique: pages are private here
+    tokens = float(info["kv_tokens"] if unique_kv_tokens is None else unique_kv_tokens)
+    kv_bytes = tokens * Hk * D * 2 * elt
     q_bytes = float(b.total_q) * H * D * elt
-    o_bytes = q_bytes
     lse_bytes = float(b.total_q) * H * 4
     pt_bytes = 4.0 * (len(b.kv_page_indices) + 2 * (b.batch + 1) + b.batch)
-    return flops, kv_bytes, kv_bytes + q_bytes + o_bytes + lse_bytes + pt_bytes
+    return flops, kv_bytes, kv_bytes + 2 * q_bytes + lse_bytes + pt_bytes
 
+
+def roofline(flops, nbytes, ms, floors=None, bound=None, kernel=None):
+    """Roofline entry of one launch (or call) of `ms` milliseconds doing `flops` and
+    moving `nbytes` algorithmic bytes.  bound: 'hbm', 'mfma', or None for whichever
+    ideal time is longer (a max-bound mixed call)."""
+    t = ms * 1e-3
+    if bound is None:
+        bound = "mfma" if flops / (MFMA_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+    if bound == "hbm":
+        ach, peak, unit = nbytes / t / 1e9, HBM_PEAK_GBS, "GB/s"
+        meas = floors.get("hbm_stream_gbs") if floors else None
+    else:
+        ach, peak, unit = flops / t / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s"
+        meas = floors.get("mfma_tflops") if floors else None
+    r = {"bound": bound, "achieved": ach, "peak": peak, "unit": unit, "frac": ach / peak,
+         "measured_peak": meas, "frac_of_measured_peak": ach / meas if meas else None, "ms": ms}
+    if kernel:
+        r["kernel"] = kernel
+    return r
+
+
+# ----------------------------------------------------------------------------------------------
+# Timing helpers
+# ----------------------------------------------------------------------------------------------
+
+def bound_plan(b, narrow="mfma", kv_shared=False, **kw):
+    import torch
+    import paged_kv_attention_ragged_amd as rpa
+    p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
+                 num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal,
+                 narrow_kernel=narrow, kv_shared=kv_shared, **kw)
+    p.bind(torch.from_numpy(b.kv_page_indices).cuda(), num_pages=b.kv_cache.shape[0])
+    return p
+
+
+def per_call_ms(fn, steps, warmup):
+    """Per-call times of fn() (GPU work on the current stream) from an event pair
+    around each call, plus the mean over a loop bracketed by one event pair."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, c in ev:
+        a.record()
+        fn()
+        c.record()
+    torch.cuda.synchronize()
+    calls = [a.elapsed_time(c) for a, c in ev]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"median_ms": float(np.median(calls)), "mean_ms": e0.elapsed_time(e1) / steps,
+            "min_ms": float(np.min(calls))}
+
+
+def kernel_ms(fn, steps):
+    """Mean kernel time per call of fn() from the library's dispatch-stamped events:
+    (total, per kind {'wide': ms, 'narrow': ms}, launches per call)."""
+    import torch
+    import paged_kv_attention_ragged_amd as rpa
+    torch.cuda.synchronize()
+    rpa.prof_start()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    kt = rpa.prof_stop()
+    per = {k: (ms / steps if n else 0.0) for k, (n, ms) in kt.items()}
+    return sum(per.values()), per, sum(n for n, _ in kt.values()) / steps
+
+
+def measure(b, steps, warmup=3, rotate=1, unique_kv_tokens=None, floors=None, **plan_kw):
+    """One workload: per-call and kernel times, algorithmic work and its roofline.
+    rotate > 1 cycles through copies of the KV cache (misses in the last-level cache)."""
+    import torch
+    p = bound_plan(b, **plan_kw)
+    q, kv0 = b.q.cuda(), b.kv_cache.cuda()
+    kvs = [kv0] + [kv0.clone() for _ in range(rotate - 1)]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    it = iter(range(1 << 40))
+    fn = lambda: p.run(q, kvs[next(it) % rotate], out=o, lse=lse, return_lse=True)
+    t = per_call_ms(fn, steps, warmup)
+    kms, per_kind, launches = kernel_ms(fn, steps)
+    p.check()
+    info = p.info
+    p.close()
+    flops, kv_bytes, nbytes = algorithmic(b, info, unique_kv_tokens)
+    t.update({"kernel_ms": kms, "launches_per_call": launches, "tflops": flops / (t["mean_ms"] * 1e-3) / 1e12,
+              "kv_gbs": kv_bytes / (t["mean_ms"] * 1e-3) / 1e9,
+              "algorithmic": {"flops": flops, "kv_bytes": kv_bytes, "bytes": nbytes},
+              "roofline": roofline(flops, nbytes, kms, floors)})
+    if per_kind["wide"] and per_kind["narrow"]:
+        t["kernel_ms_by_kind"] = per_kind
+    return t
+
+
+# ----------------------------------------------------------------------------------------------
+# Floors measured on the box
+# ----------------------------------------------------------------------------------------------
+
+def bench_floors(steps=20):
+    """Empty launch, plain HBM read, the decode batch's paged gather alone (same grid
+    and page table as the decode kernel: 128 sequences x 4 pieces of 256 keys), and
+    dense bf16 MFMA throughput."""
+    import torch
+    import workloads as W
+    lib = ctypes.CDLL(FLOORS_LIB)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.rpa_floor_empty.argtypes = [i32, P]
+    lib.rpa_floor_stream.argtypes = [P, i64, P, i32, P]
+    lib.rpa_floor_gather.argtypes = [P, P, i32, i32, i32, i32, P, P]
+    lib.rpa_floor_mfma.argtypes = [P, i32, i32, P]
+
+    def ok(rc):
+        if rc != 0:
+            raise RuntimeError("floor kernel launch failed: hipError %d" % rc)
+
+    st = lambda: torch.cuda.current_stream().cuda_stream
+    out = {}
+    # empty launch, the decode grid
+    t = per_call_ms(lambda: ok(lib.rpa_floor_empty(512, st())), steps * 5, 5)
+    out["empty_launch_us"] = t["median_ms"] * 1e3
+    out["empty_launch_back_to_back_us"] = t["mean_ms"] * 1e3
+    # plain read of 2 GiB (> the last-level cache), 4 workgroups per CU, each its own share
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.empty(1024 * 256, dtype=torch.int32, device="cuda")
+    t = per_call_ms(lambda: ok(lib.rpa_floor_stream(buf.data_ptr(), nbytes, sink.data_ptr(), 1024, st())), steps, 3)
+    out["hbm_stream_gbs"] = nbytes / (t["median_ms"] * 1e-3) / 1e9
+    del buf
+    # the decode batch's gather: K and V of 128 x 1024 tokens, 8 rotated cache copies
+    b = W.decode_b128_kv1024(device="cuda")
+    kvs = [b.kv_cache] + [b.kv_cache.clone() for _ in range(7)]
+    idx = torch.from_numpy(b.kv_page_indices).cuda()
+    gsink = torch.empty(512 * 256, dtype=torch.int32, device="cuda")
+    it = iter(range(1 << 40))
+    gb = 128 * 1024 * 128 * 2 * 2.0
+    t = per_call_ms(lambda: ok(lib.rpa_floor_gather(kvs[next(it) % 8].data_ptr(), idx.data_ptr(), 128, 64, 4, 1,
+                                                    gsink.data_ptr(), st())), steps * 5, 5)
+    out["decode_gather_us"] = t["median_ms"] * 1e3
+    out["decode_gather_gbs"] = gb / (t["median_ms"] * 1e-3) / 1e9
+    del kvs, b
+    # dense MFMA: 1024 workgroups x 4 waves x 4 chains x iters 32x32x16 bf16 products
+    msink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")
+    iters = 4096
+    t = per_call_ms(lambda: ok(lib.rpa_floor_mfma(msink.data_ptr(), 1024, iters, st())), 10, 2)
+    flops = 1024 * 4 * 4 * iters * 32768.0
+    out["mfma_tflops"] = flops / (t["median_ms"] * 1e-3) / 1e12
+    torch.cuda.empty_cache()
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Headline: decode 128 x 1024
+# ----------------------------------------------------------------------------------------------
 
 def time_steps(plan, q, kvs, o, lse, steps, warmup):
     import torch
@@ -114,56 +303,8 @@ def time_steps(plan, q, kvs, o, lse, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def kernel_times(plan, q, kvs, o, lse, steps):
+def bench_decode(args, floors):
     import torch
-    import paged_kv_attention_ragged_amd as rpa
-    torch.cuda.synchronize()
-    rpa.prof_start()
-    for i in range(steps):
-        plan.run(q, kvs[i % len(kvs)], out=o, lse=lse, return_lse=True)
-    torch.cuda.synchronize()
-    return rpa.prof_stop()
-
-
-def cpu_baseline(b, target_s=10.0):
-    """The oracle (as is) on the first n sequences of the batch, with n sized
-    from a short trial so the run takes about `target_s`; rate scaled to KV GB/s."""
-    import oracle
-    import workloads as W
-    threads = len(os.sched_getaffinity(0))
-    q_host = oracle._u16(b.q)
-    kv_host = oracle._u16(b.kv_cache)
-
-    def sample(n):
-        sub = W.Batch(b.name, b.qo_indptr[:n + 1].copy(), b.kv_page_indptr[:n + 1].copy(),
-                      b.kv_page_indices[:b.kv_page_indptr[n]].copy(), b.kv_last_page_len[:n].copy(),
-                      None, None, b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype)
-        kw = sub.oracle_kwargs()
-        kw["q"] = q_host[:b.qo_indptr[n]]
-        kw["kv_cache"] = kv_host
-        t0 = time.perf_counter()
-        oracle.run(**kw, nthreads=threads)
-        return sub, time.perf_counter() - t0
-
-    n = min(b.batch, 2)
-    sub, dt = sample(n)
-    if n < b.batch:
-        n = min(b.batch, max(n, int(n * target_s / max(dt, 1e-3))))
-        sub, dt = sample(n)
-    reps = 1
-    while dt * reps < target_s and reps < 200:  # the whole batch is quick: repeat it
-        _, t = sample(n)
-        dt = (dt * reps + t) / (reps + 1)
-        reps += 1
-    kv_bytes = float(sub.kv_lens.sum()) * b.num_kv_heads * b.head_dim * 2 * 2
-    return {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "first %d of %d sequences (%d query rows x %d heads, all their keys), mean of %d runs, "
-                      "%.3f s each" % (n, b.batch, sub.total_q, b.num_qo_heads, reps, dt)}
-
-
-def bench_decode(args):
-    import torch
-    import numpy as np
     import paged_kv_attention_ragged_amd as rpa
     import workloads as W
     b = W.decode_b128_kv1024(device="cuda")
@@ -180,13 +321,16 @@ def bench_decode(args):
     o = torch.empty_like(b.q)
     lse = torch.empty((b.total_q, b.num_qo_heads), dtype=torch.float32, device="cuda")
     ms, wall = time_steps(plan, b.q, kvs, o, lse, args.steps, args.warmup)
-    kt = kernel_times(plan, b.q, kvs, o, lse, args.steps)
+    it = iter(range(1 << 40))
+    fn = lambda: plan.run(b.q, kvs[next(it) % 8], out=o, lse=lse, return_lse=True)
+    per_call = per_call_ms(fn, args.steps, 2)
+    attn_avg, per_kind, launches = kernel_ms(fn, args.steps)
+    assert per_kind["wide"] == 0 and launches == 1  # every tile of a q_len = 1, G = 8 batch is narrow
+    hot = per_call_ms(lambda: plan.run(b.q, kvs[0], out=o, lse=lse, return_lse=True), args.steps, 2)
+    plan.check()
     flops, kv_bytes, alg_bytes = algorithmic(b, info)
-    n_attn, ms_attn = kt["narrow"]  # every tile of a q_len = 1, G = 8 batch is narrow
-    n_wide, _ = kt["wide"]
-    assert n_wide == 0 and n_attn == args.steps
-    attn_avg = ms_attn / max(n_attn, 1)
     achieved = alg_bytes / (attn_avg * 1e-3) / 1e9
+    meas = floors.get("hbm_stream_gbs")
     res = {
         "metric": METRIC, "value": kv_bytes / (ms * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -197,10 +341,13 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(),
                      "kernel": "attn_narrow_kernel" if args.narrow_kernel == "mfma" else "attn_narrow_valu_kernel",
-                     "avg_ms": attn_avg,
-                     "algorithmic_bytes_per_launch": alg_bytes},
+                     "avg_ms": attn_avg, "algorithmic_bytes_per_launch": alg_bytes,
+                     "frac_per_step": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "measured_peak": meas, "frac_of_measured_peak": achieved / meas if meas else None},
         "tflops": flops / (ms * 1e-3) / 1e12,
-        "kernels": {"narrow_avg_ms": attn_avg, "launches_per_step": (n_attn + n_wide) / args.steps},
+        "per_call": {"median_ms": per_call["median_ms"], "mean_ms": per_call["mean_ms"],
+                     "hot_median_ms": hot["median_ms"],
+                     "hot_note": "one cache copy, resident in the last-level cache"},
         "plan": {"host_ms": plan_ms, "tiles": info["num_tiles"], "split_groups": info["num_split_groups"],
                  "max_splits": info["max_splits"]},
         "wall_s_timed": wall,
@@ -209,80 +356,35 @@ def bench_decode(args):
     return res, b
 
 
-def bench_prefill(args):
-    """Long causal prompts: 4 x 8192, 64 qo / 8 kv heads, bf16."""
-    import torch
-    import paged_kv_attention_ragged_amd as rpa
+def bench_prefill(args, floors):
+    """Long causal prompts: 4 x 8192, 64 qo / 8 kv heads, bf16 (every tile wide)."""
     import workloads as W
     b = W.mixed_long_batch(part="prompts", device="cuda")
-    idx = torch.from_numpy(b.kv_page_indices).cuda()
-    plan = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
-                    num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype)
-    plan.bind(idx, num_pages=b.num_pages)
-    info = plan.info
-    o = torch.empty_like(b.q)
-    lse = torch.empty((b.total_q, b.num_qo_heads), dtype=torch.float32, device="cuda")
-    steps = max(3, args.steps // 10)
-    ms, _ = time_steps(plan, b.q, [b.kv_cache], o, lse, steps, 2)
-    kt = kernel_times(plan, b.q, [b.kv_cache], o, lse, steps)
-    flops, kv_bytes, alg_bytes = algorithmic(b, info)
-    n_attn, ms_attn = kt["wide"]  # causal prompts: every tile is wide
-    attn_avg = ms_attn / max(n_attn, 1)
-    tf = flops / (attn_avg * 1e-3) / 1e12
-    plan.close()
-    return {"workload": "mixed_long_prompts_4x8192", "ms_per_step": ms, "tflops": flops / (ms * 1e-3) / 1e12,
-            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / MFMA_PEAK_TFLOPS, "kernel": "attn_wide_kernel", "avg_ms": attn_avg,
-                         "algorithmic_flops_per_launch": flops},
-            "dtype": b.dtype, "tiles": info["num_tiles"]}
+    r = measure(b, steps=max(3, args.steps // 10), warmup=2, floors=floors)
+    rf = roofline(r["algorithmic"]["flops"], r["algorithmic"]["bytes"], r["kernel_ms"], floors, bound="mfma",
+                  kernel="attn_wide_kernel")
+    rf["algorithmic_flops_per_launch"] = r["algorithmic"]["flops"]
+    return {"workload": "mixed_long_prompts_4x8192", "ms_per_step": r["mean_ms"], "median_ms": r["median_ms"],
+            "tflops": r["tflops"], "roofline": rf, "dtype": b.dtype}
 
 
-def time_fn(fn, steps, warmup):
-    """Mean ms per call of fn() (GPU work on the current stream), by events around `steps` calls."""
-    import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+# ----------------------------------------------------------------------------------------------
+# The other workloads
+# ----------------------------------------------------------------------------------------------
+
+def shared_unique_tokens(b):
+    """Distinct physical token slots a shared-prefix batch reads: the shared full pages
+    once, then each request's own tokens."""
+    n_sh = len(b.extra["shared"]) if hasattr(b, "extra") else 0
+    return int(n_sh * 16 + (np.asarray(b.kv_lens) - n_sh * 16).sum())
 
 
-def bound_plan(b, narrow="mfma", kv_shared=False):
-    import torch
-    import paged_kv_attention_ragged_amd as rpa
-    p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
-                 num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal,
-                 narrow_kernel=narrow, kv_shared=kv_shared)
-    p.bind(torch.from_numpy(b.kv_page_indices).cuda(), num_pages=b.kv_cache.shape[0])
-    return p
-
-
-def bench_secondary(args):
-    """The other workloads of the pages, one line each: ragged vs padded short
-    prompts, the shared-prefix suffix prefill and a decode step (direct and as a
-    cascade), and the mixed long batch's parts."""
+def bench_secondary(args, floors):
     import torch
     import paged_kv_attention_ragged_amd as rpa
     import workloads as W
     steps = max(5, args.steps // 10)
     out = {}
-
-    def direct(b, rotate=1, narrow="mfma", kv_shared=False):
-        p = bound_plan(b, narrow, kv_shared)
-        q, kv0 = b.q.cuda(), b.kv_cache.cuda()
-        kvs = [kv0] + [kv0.clone() for _ in range(rotate - 1)]
-        o = torch.empty_like(q)
-        lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
-        it = iter(range(1 << 30))
-        ms = time_fn(lambda: p.run(q, kvs[next(it) % rotate], out=o, lse=lse, return_lse=True), steps, 3)
-        info = p.info
-        p.close()
-        return ms, info
 
     def cascade(b, prefix):
         sh, pr = W.cascade_view(b, prefix=prefix, poison=False)
@@ -296,67 +398,61 @@ def bench_secondary(args):
             pa.run(q, kv, out=oa, lse=la, return_lse=True)
             pb.run(q, kv, out=ob, lse=lb, return_lse=True)
             rpa.merge_states(oa, la, ob, lb, out=oa, lse_out=la)
-        ms = time_fn(step, steps, 3)
+        t = per_call_ms(step, steps, 3)
         pa.close()
         pb.close()
-        return ms
+        return t
 
     # short ragged prompts (lengths U{1..200}) vs the same prompts padded to 200
     log("short prompts: ragged vs padded")
-    sp = W.short_prompt_prefill()
-    spp = W.short_prompt_prefill(padded=True)
-    ms_r, inf_r = direct(sp)
-    ms_p, inf_p = direct(spp)
-    out["short_prompts"] = {"ragged_ms": ms_r, "padded_ms": ms_p, "time_ratio": ms_r / ms_p,
-                            "flops_ratio": inf_r["visible_pairs"] / inf_p["visible_pairs"],
-                            "ragged_tflops": 4.0 * sp.head_dim * inf_r["visible_pairs"] / ms_r / 1e9}
+    sp, spp = W.short_prompt_prefill(), W.short_prompt_prefill(padded=True)
+    r, p = measure(sp, steps, floors=floors), measure(spp, steps, floors=floors)
+    out["short_prompts"] = {"ragged": r, "padded": p, "time_ratio": r["mean_ms"] / p["mean_ms"],
+                            "kernel_time_ratio": r["kernel_ms"] / p["kernel_ms"],
+                            "flops_ratio": r["algorithmic"]["flops"] / p["algorithmic"]["flops"],
+                            "bytes_ratio": r["algorithmic"]["bytes"] / p["algorithmic"]["bytes"]}
     # shared prefix (256 requests x 200 shared + 30 own tokens), then one decode step
     log("shared prefix: direct vs cascade")
     b = W.shared_prefix_suffix()
-    pre_direct, inf = direct(b)
-    pre_cascade = cascade(b, 200)
+    pre = measure(b, steps, unique_kv_tokens=shared_unique_tokens(b), floors=floors)
+    pre["cascade_median_ms"] = cascade(b, 200)["median_ms"]
     d = W.decode_step(b, 1)
-    dec_direct, inf_d = direct(d, rotate=6, kv_shared=True)  # 12 pages shared by all requests
-    dec_cascade = cascade(d, 200)
-    logical = float(inf_d["kv_tokens"]) * d.num_kv_heads * d.head_dim * 4
-    out["shared_prefix"] = {"suffix_prefill_direct_ms": pre_direct, "suffix_prefill_cascade_ms": pre_cascade,
-                            "decode_step_direct_ms": dec_direct, "decode_step_cascade_ms": dec_cascade,
-                            "decode_direct_logical_kv_gbs": logical / dec_direct / 1e6,
-                            "suffix_prefill_tflops_direct": 4.0 * b.head_dim * inf["visible_pairs"] / pre_direct / 1e9}
+    d.extra = b.extra
+    dec = measure(d, steps, rotate=6, unique_kv_tokens=shared_unique_tokens(d), floors=floors, kv_shared=True)
+    logical = float(d.kv_lens.sum()) * d.num_kv_heads * d.head_dim * 4
+    dec["logical_kv_bytes"] = logical
+    dec["logical_kv_gbs"] = logical / (dec["kernel_ms"] * 1e-3) / 1e9
+    dec["cascade_median_ms"] = cascade(d, 200)["median_ms"]
+    dec["streamed_kv_median_ms"] = measure(d, steps, rotate=6, floors=floors)["median_ms"]
+    dec["valu_median_ms"] = measure(d, steps, rotate=6, floors=floors, narrow="valu", kv_shared=True)["median_ms"]
+    out["shared_prefix"] = {"suffix_prefill": pre, "decode_step": dec}
     # a long shared prefix (4096 tokens) under the same 256 requests: one decode step
     log("long shared prefix decode: direct vs cascade")
     lb = W.decode_step(W.shared_prefix_suffix(prefix=4096, decode_steps=1), 1)
-    ld_direct, inf_l = direct(lb, kv_shared=True)
-    ld_cascade = cascade(lb, 4096)
-    out["long_prefix_4096"] = {"decode_step_direct_ms": ld_direct, "decode_step_cascade_ms": ld_cascade,
-                               "logical_kv_gb": float(inf_l["kv_tokens"]) * lb.num_kv_heads * lb.head_dim * 4 / 1e9}
+    ld = measure(lb, steps, kv_shared=True, floors=floors)
+    out["long_prefix_4096"] = {"decode_step_direct_median_ms": ld["median_ms"],
+                               "decode_step_cascade_median_ms": cascade(lb, 4096)["median_ms"],
+                               "logical_kv_gb": float(lb.kv_lens.sum()) * lb.num_kv_heads * lb.head_dim * 4 / 1e9}
     del lb
-    # the decode loop: eager vs graph-captured steps
     log("decode loop: eager vs graph")
     out["decode_loop"] = bench_decode_loop()
-    # decode tiles on the VALU kernel instead of MFMA (the pages' CUDA-core decode)
     log("decode on the VALU kernel")
     db = W.decode_b128_kv1024(device="cuda")
-    v_ms, _ = direct(db, rotate=8, narrow="valu")
-    m_ms, _ = direct(db, rotate=8)
-    out["decode_b128_kv1024_valu_vs_mfma"] = {"valu_ms": v_ms, "mfma_ms": m_ms}
+    out["decode_b128_kv1024_valu_vs_mfma"] = {
+        "valu": measure(db, steps, rotate=8, narrow="valu", floors=floors),
+        "mfma_median_ms": measure(db, steps, rotate=8, floors=floors)["median_ms"]}
     del db
-    out["shared_prefix"]["decode_step_valu_ms"] = direct(d, rotate=6, narrow="valu", kv_shared=True)[0]
-    out["shared_prefix"]["decode_step_streamed_kv_ms"] = direct(d, rotate=6)[0]  # without the hint
-    # mixed long batch: its decode rows alone and the whole batch in one call
     log("mixed long batch: decode rows, whole batch")
     for part in ("decode", "all"):
         mb = W.mixed_long_batch(part=part, device="cuda")
-        ms, info = direct(mb)
-        kvb = float(info["kv_tokens"]) * mb.num_kv_heads * mb.head_dim * 4
-        ent = {"ms": ms, "tflops": 4.0 * mb.head_dim * info["visible_pairs"] / ms / 1e9}
+        ent = measure(mb, steps, floors=floors)
         if part == "decode":
-            ent["kv_gbs"] = kvb / ms / 1e6
-            ent["hbm_frac"] = ent["kv_gbs"] / HBM_PEAK_GBS
-            ent["valu_ms"] = direct(mb, narrow="valu")[0]
+            ent["valu_median_ms"] = measure(mb, steps, narrow="valu", floors=floors)["median_ms"]
         out["mixed_long_" + part] = ent
         del mb
         torch.cuda.empty_cache()
+    log("batch-size sweep at 8192 total tokens")
+    out["sweep"] = bench_sweep(batches=(1, 8, 64, 256), steps=5, floors=floors, quiet=True)
     return out
 
 
@@ -367,7 +463,6 @@ def bench_decode_loop(steps=50):
     append, run] replayed after an in-place plan update.  Both synchronise every
     step, as a decode loop must; inputs of all steps are prepared beforehand."""
     import torch
-    import numpy as np
     import paged_kv_attention_ragged_amd as rpa
     import workloads as W
     base = W.shared_prefix_suffix()
@@ -431,7 +526,7 @@ def bench_decode_loop(steps=50):
         plan.run(q_buf, kv, out=o_buf, lse=l_buf, return_lse=True)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    gpu_ms = 0.0
+    gpu_ms = []
     t0 = time.perf_counter()
     for i in range(steps):
         if i > 0:
@@ -441,17 +536,20 @@ def bench_decode_loop(steps=50):
         g.replay()
         e1.record()
         torch.cuda.synchronize()
-        gpu_ms += e0.elapsed_time(e1)
+        gpu_ms.append(e0.elapsed_time(e1))
     graph = (time.perf_counter() - t0) / steps * 1e3
+    plan.check()
     plan.close()
-    return {"steps": steps, "eager_step_ms": eager, "graph_step_ms": graph, "graph_replay_gpu_ms": gpu_ms / steps}
+    return {"steps": steps, "eager_step_ms": eager, "graph_step_ms": graph,
+            "graph_replay_gpu_median_ms": float(np.median(gpu_ms))}
 
 
-def bench_sweep(total_tokens=8192, batches=(1, 2, 4, 8, 16, 32, 64, 128, 256), steps=10):
+def bench_sweep(total_tokens=8192, batches=(1, 2, 4, 8, 16, 32, 64, 128, 256), steps=10, floors=None,
+                quiet=False):
     """Batch-size sweep at constant total tokens (llama.cpp discussion #15958: batching
     prompts helps little unless they are very short): B causal prompts of
     total_tokens / B tokens each (32 qo / 8 kv heads, D 128, bf16), as one ragged
-    call, against the same prompts run one call each.  One JSON line per B."""
+    call, against the same prompts run one call each."""
     import torch
     import workloads as W
     rows = []
@@ -463,22 +561,101 @@ def bench_sweep(total_tokens=8192, batches=(1, 2, 4, 8, 16, 32, 64, 128, 256), s
         o = torch.empty_like(q)
         p = bound_plan(b)
         info = p.info
-        batched = time_fn(lambda: p.run(q, kv, out=o), steps, 2)
+        batched = per_call_ms(lambda: p.run(q, kv, out=o), steps, 2)
+        kms = kernel_ms(lambda: p.run(q, kv, out=o), steps)[0]
         p.close()
         one = W.Batch("one", np.array([0, L], np.int32), np.array([0, b.kv_page_indptr[1]], np.int32),
                       b.kv_page_indices[:b.kv_page_indptr[1]].copy(), b.kv_last_page_len[:1].copy(), q[:L], kv,
                       b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype)
         p1 = bound_plan(one)
-        single = time_fn(lambda: p1.run(q[:L], kv, out=o[:L]), steps, 2)
+        single = per_call_ms(lambda: p1.run(q[:L], kv, out=o[:L]), steps, 2)["median_ms"]
         p1.close()
+        flops, _, nbytes = algorithmic(b, info)
         r = {"sweep": "constant_total_tokens", "total_tokens": total_tokens, "batch": B, "prompt_len": L,
-             "batched_ms": batched, "one_by_one_ms": single * B, "speedup": single * B / batched,
-             "tflops_batched": 4.0 * b.head_dim * info["visible_pairs"] / batched / 1e9}
-        print(json.dumps(r), flush=True)
+             "batched_median_ms": batched["median_ms"], "one_by_one_ms": single * B,
+             "speedup": single * B / batched["median_ms"],
+             "tflops_batched": flops / (batched["median_ms"] * 1e-3) / 1e12,
+             "roofline": roofline(flops, nbytes, kms, floors)}
+        if not quiet:
+            print(json.dumps(r), flush=True)
         rows.append(r)
         del b, q, kv, o
         torch.cuda.empty_cache()
     return rows
+
+
+# ----------------------------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on the machine's host cores
+# ----------------------------------------------------------------------------------------------
+
+def oracle_time(b, rows, threads, q_host, kv_host):
+    import oracle
+    kw = b.oracle_kwargs()
+    kw["q"], kw["kv_cache"] = q_host, kv_host
+    t0 = time.perf_counter()
+    oracle.run(**kw, rows=rows, nthreads=threads)
+    return time.perf_counter() - t0
+
+
+def visible_of_rows(b, rows):
+    """Visible keys of each listed row (causal: its position + 1), summed."""
+    seq = np.searchsorted(b.qo_indptr, np.asarray(rows), side="right") - 1
+    kvl, ql = b.kv_lens[seq], b.q_lens[seq]
+    pos = kvl - ql + (np.asarray(rows) - b.qo_indptr[seq])
+    return int((pos + 1).sum()) if b.causal else int(kvl.sum())
+
+
+def cpu_baseline(b, target_s=10.0):
+    """The oracle (as is) on the first n sequences of the headline batch, n sized from
+    a short trial so the run takes about `target_s`; rate in KV GB/s, with fp64
+    GFLOP/s and rows/s; then a labelled row sample of the mixed long batch."""
+    import oracle
+    import workloads as W
+    threads = len(os.sched_getaffinity(0))
+    q_host, kv_host = oracle._u16(b.q), oracle._u16(b.kv_cache)
+
+    def sample(n):
+        sub = W.Batch(b.name, b.qo_indptr[:n + 1].copy(), b.kv_page_indptr[:n + 1].copy(),
+                      b.kv_page_indices[:b.kv_page_indptr[n]].copy(), b.kv_last_page_len[:n].copy(),
+                      None, None, b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype)
+        return sub, oracle_time(sub, None, threads, q_host[:b.qo_indptr[n]], kv_host)
+
+    n = min(b.batch, 2)
+    sub, dt = sample(n)
+    if n < b.batch:
+        n = min(b.batch, max(n, int(n * target_s / max(dt, 1e-3))))
+        sub, dt = sample(n)
+    reps = 1
+    while dt * reps < target_s and reps < 200:  # the whole batch is quick: repeat it
+        _, t = sample(n)
+        dt = (dt * reps + t) / (reps + 1)
+        reps += 1
+    kv_bytes = float(sub.kv_lens.sum()) * b.num_kv_heads * b.head_dim * 2 * 2
+    flops = 4.0 * b.head_dim * b.num_qo_heads * float(sub.kv_lens.sum())  # one row per sequence
+    res = {"value": kv_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": "first %d of %d sequences of decode_b128_kv1024 (%d query rows x %d heads, all their keys), "
+                     "mean of %d runs, %.3f s each" % (n, b.batch, sub.total_q, b.num_qo_heads, reps, dt),
+           "fp64_gflops": flops / dt / 1e9, "rows_per_s": sub.total_q / dt, "seconds": dt, "cpu_model": cpu_model()}
+    # the mixed long batch (4 prompts x 8192 + 256 decode rows, 64 qo heads): every 4th
+    # decode row and the last 4 rows of each prompt, the rows that see the most keys
+    log("oracle on a row sample of the mixed long batch")
+    import torch
+    m = W.mixed_long_batch(device="cuda")
+    rows = [int(m.qo_indptr[s]) for s in range(4, m.batch, 4)]
+    for s in range(4):
+        e = int(m.qo_indptr[s + 1])
+        rows += list(range(e - 4, e))
+    rows = sorted(rows)
+    mq, mkv = oracle._u16(m.q), oracle._u16(m.kv_cache)
+    m.q, m.kv_cache = None, None  # host copies only from here
+    torch.cuda.empty_cache()
+    t = oracle_time(m, rows, threads, mq, mkv)
+    fl = 4.0 * m.head_dim * m.num_qo_heads * visible_of_rows(m, rows)
+    res["mixed_long_sample"] = {"rows": len(rows), "seconds": t, "rows_per_s": len(rows) / t,
+                                "fp64_gflops": fl / t / 1e9,
+                                "sample": "every 4th of the 256 decode rows and the last 4 rows of each of the "
+                                          "4 prompts of mixed_long_batch, all 64 heads"}
+    return res
 
 
 def main():
@@ -492,7 +669,7 @@ def main():
     ap.add_argument("--narrow-kernel", choices=("mfma", "valu"), default="mfma",
                     help="kernel for the headline decode tiles (default: the MFMA one)")
     ap.add_argument("--sweep", action="store_true",
-                    help="only the batch-size sweep at constant total tokens (one JSON line per batch size)")
+                    help="only the full batch-size sweep at constant total tokens (one JSON line per batch size)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -509,13 +686,16 @@ def main():
         return
     if args.calibrate_copy:
         calibrate_copy()
+    log("floors: empty launch, HBM stream, decode gather, MFMA")
+    floors = bench_floors()
     log("decode_b128_kv1024: %d warmup + %d timed steps" % (args.warmup, args.steps))
-    res, b = bench_decode(args)
+    res, b = bench_decode(args, floors)
+    res["floors"] = floors
     if not args.no_prefill:
         log("long prefill 4x8192")
-        res["prefill"] = bench_prefill(args)
+        res["prefill"] = bench_prefill(args, floors)
     if not args.no_secondary:
-        res["secondary"] = bench_secondary(args)
+        res["secondary"] = bench_secondary(args, floors)
     if not args.no_cpu_baseline:
         log("oracle baseline on host cores")
         res["cpu_baseline"] = cpu_baseline(b)

@@ -18,6 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "librpa.so")
+FLOORS_LIB = os.path.join(HERE, "librpa_floors.so")  # benchmark microkernels (bench.py only)
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
@@ -38,8 +39,13 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False, extra_hip_flags=()) -> str:
-    """Compile every source and link librpa.so; always rebuilds."""
+    """Compile every source and link librpa.so (and the benchmark's
+    librpa_floors.so); always rebuilds."""
     inc = ["-I", INCLUDE, "-I", CSRC]
+    hipcc = os.path.join(ROCM, "bin", "hipcc")
+    tmp_floors = FLOORS_LIB + ".tmp%d" % os.getpid()
+    _run([hipcc] + HIP_FLAGS + ["-shared", "-o", tmp_floors, os.path.join(CSRC, "rpa_floors.hip")], verbose)
+    os.replace(tmp_floors, FLOORS_LIB)
     with tempfile.TemporaryDirectory(prefix="rpa_build_") as tmp:
         objs = []
         o = os.path.join(tmp, "rpa_schedule.o")
@@ -50,11 +56,11 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
               "-c", os.path.join(CSRC, "rpa_api.cpp"), "-o", o], verbose)
         objs.append(o)
         o = os.path.join(tmp, "rpa_kernels.o")
-        _run([os.path.join(ROCM, "bin", "hipcc")] + HIP_FLAGS + list(extra_hip_flags) + inc +
+        _run([hipcc] + HIP_FLAGS + list(extra_hip_flags) + inc +
              ["-c", os.path.join(CSRC, "rpa_kernels.hip"), "-o", o], verbose)
         objs.append(o)
         tmp_lib = LIB + ".tmp%d" % os.getpid()
-        _run([os.path.join(ROCM, "bin", "hipcc"), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp_lib]
+        _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp_lib]
              + objs + ["-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib")],
              verbose)
         os.replace(tmp_lib, LIB)

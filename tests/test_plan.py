@@ -525,3 +525,13 @@ def test_plan_update_refuses_another_kernel_configuration():
     m = make_plan(b1, max_kv_splits=1)
     m.update(b2.qo_indptr, b2.kv_page_indptr, b2.kv_last_page_len)
     assert np.array_equal(m.tiles(), make_plan(b2, max_kv_splits=1).tiles())
+
+
+def test_benchmark_floors_library_loads():
+    """The benchmark's microkernel library is built beside librpa.so and exports its
+    four floors (launched only by bench.py, on a GPU)."""
+    import os
+    path = os.path.join(os.path.dirname(rpa.LIB_PATH), "librpa_floors.so")
+    lib = ctypes.CDLL(path)
+    for name in ("rpa_floor_empty", "rpa_floor_stream", "rpa_floor_gather", "rpa_floor_mfma"):
+        assert hasattr(lib, name), name

@@ -151,6 +151,7 @@ def roofline(flops, nbytes, ms, floors=None, bound=None, kernel=None):
 # ----------------------------------------------------------------------------------------------
 
 def bound_plan(b, narrow="mfma", kv_shared=False, **kw):
+    """A plan for batch b bound to its page table (kw: further Plan arguments)."""
     import torch
     import paged_kv_attention_ragged_amd as rpa
     p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
@@ -418,22 +419,36 @@ def bench_secondary(args, floors):
     pre["cascade_median_ms"] = cascade(b, 200)["median_ms"]
     d = W.decode_step(b, 1)
     d.extra = b.extra
-    dec = measure(d, steps, rotate=6, unique_kv_tokens=shared_unique_tokens(d), floors=floors, kv_shared=True)
+    n_sh = len(b.extra["shared"])
+    # the library's plan for it: the shared prefix declared, decode rows grouped over it
+    dec = measure(d, steps, rotate=6, unique_kv_tokens=shared_unique_tokens(d), floors=floors, kv_shared=True,
+                  shared_pages=n_sh)
     logical = float(d.kv_lens.sum()) * d.num_kv_heads * d.head_dim * 4
+    dec["plan"] = "shared prefix declared (%d pages): decode rows grouped 4 per tile" % n_sh
     dec["logical_kv_bytes"] = logical
     dec["logical_kv_gbs"] = logical / (dec["kernel_ms"] * 1e-3) / 1e9
+    direct = measure(d, steps, rotate=6, unique_kv_tokens=shared_unique_tokens(d), floors=floors, kv_shared=True)
+    dec["direct"] = {"median_ms": direct["median_ms"], "kernel_ms": direct["kernel_ms"],
+                     "roofline_frac": direct["roofline"]["frac"]}
     dec["cascade_median_ms"] = cascade(d, 200)["median_ms"]
-    dec["streamed_kv_median_ms"] = measure(d, steps, rotate=6, floors=floors)["median_ms"]
-    dec["valu_median_ms"] = measure(d, steps, rotate=6, floors=floors, narrow="valu", kv_shared=True)["median_ms"]
+    dec["direct_streamed_kv_median_ms"] = measure(d, steps, rotate=6, floors=floors)["median_ms"]
+    dec["direct_valu_median_ms"] = measure(d, steps, rotate=6, floors=floors, narrow="valu",
+                                           kv_shared=True)["median_ms"]
     out["shared_prefix"] = {"suffix_prefill": pre, "decode_step": dec}
     # a long shared prefix (4096 tokens) under the same 256 requests: one decode step
-    log("long shared prefix decode: direct vs cascade")
-    lb = W.decode_step(W.shared_prefix_suffix(prefix=4096, decode_steps=1), 1)
+    log("long shared prefix decode: direct, grouped, cascade")
+    lbase = W.shared_prefix_suffix(prefix=4096, decode_steps=1)
+    lb = W.decode_step(lbase, 1)
+    lb.extra = lbase.extra
     ld = measure(lb, steps, kv_shared=True, floors=floors)
+    lg = measure(lb, steps, kv_shared=True, floors=floors, unique_kv_tokens=shared_unique_tokens(lb),
+                 shared_pages=len(lbase.extra["shared"]))
     out["long_prefix_4096"] = {"decode_step_direct_median_ms": ld["median_ms"],
+                               "decode_step_grouped_median_ms": lg["median_ms"],
+                               "decode_step_grouped_roofline": lg["roofline"],
                                "decode_step_cascade_median_ms": cascade(lb, 4096)["median_ms"],
                                "logical_kv_gb": float(lb.kv_lens.sum()) * lb.num_kv_heads * lb.head_dim * 4 / 1e9}
-    del lb
+    del lb, lbase
     log("decode loop: eager vs graph")
     out["decode_loop"] = bench_decode_loop()
     log("decode on the VALU kernel")

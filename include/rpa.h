@@ -145,6 +145,27 @@ rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_
                            const int32_t* kv_page_indptr_h, const int32_t* kv_last_page_len_h,
                            rpa_plan** out);
 
+/*
+ * Plan a batch whose sequences share a prefix stored once (vLLM issue #227,
+ * "Question about efficient memory sharing": many requests over one system prompt,
+ * its KV pages shared): as rpa_plan_create, with the caller's declaration that the
+ * first `shared_pages` entries of the page list of every sequence that has at least
+ * that many pages name the same physical pages.  Decode rows (q_len 1) that see the whole prefix are then
+ * grouped, up to 16 / G consecutive sequences per tile, so that the prefix's K and
+ * V are read once per group instead of once per sequence; their own keys follow,
+ * visible to their own rows only.  Other sequences are planned as by
+ * rpa_plan_create.  The declaration is trusted, not checked: if the pages differ,
+ * the grouped rows attend to the first sequence's prefix.  The schedule still
+ * depends only on the lengths and shared_pages.  Results equal those of
+ * rpa_plan_create within the oracle tolerance (the keys are combined in another
+ * order); rpa_plan_update keeps the declaration.  With narrow_kernel = 1, or more
+ * than 8 query heads per kv head, nothing is grouped.
+ * Errors: those of rpa_plan_create; E_ARG for shared_pages < 0.
+ */
+rpa_status rpa_plan_create_shared(const rpa_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                                  const int32_t* kv_page_indptr_h, const int32_t* kv_last_page_len_h,
+                                  int32_t shared_pages, rpa_plan** out);
+
 /* Summary of a plan (sizes, tile shape, work counts): the auxiliary data that
  * begin_forward builds in flashinfer issue #323, made inspectable.  Host-only. */
 rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
@@ -161,7 +182,9 @@ rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
  *   [3] kv_len, [4] kv_page_indptr[b], [5] kv head, [6] first key, [7] end key,
  *   [8] first partial row (-1: writes O directly), [9] sequence, [10] split
  *   index, [11] split count, [12] kind (0: wide, up to 128 rows; 1: narrow, up to
- *   16 rows), [13] split group (-1 if not split), [14..15] reserved.
+ *   16 rows; 2: a group of [1] decode rows of sequences [9].. over a shared prefix
+ *   of [3] keys, then [2] private 32-key steps per member), [13] split group (-1 if
+ *   not split), [14..15] reserved.
  * *n_out receives the number of records in the plan.
  */
 rpa_status rpa_plan_tiles(const rpa_plan* plan, int32_t* out_h, int64_t cap, int64_t* n_out);

@@ -71,6 +71,7 @@ def load():
         st = ctypes.c_int
         sig = {
             "rpa_plan_create": (st, [ctypes.POINTER(_Params), i32, P, P, P, ctypes.POINTER(P)]),
+            "rpa_plan_create_shared": (st, [ctypes.POINTER(_Params), i32, P, P, P, i32, ctypes.POINTER(P)]),
             "rpa_workspace_bytes": (st, [ctypes.POINTER(_Params), i32, i64, i64, ctypes.POINTER(ctypes.c_size_t)]),
             "rpa_plan_info": (st, [P, ctypes.POINTER(_Info)]),
             "rpa_plan_tiles": (st, [P, P, i64, ctypes.POINTER(i64)]),
@@ -162,7 +163,10 @@ class Plan:
     def __init__(self, qo_indptr, kv_page_indptr, kv_last_page_len, *, num_qo_heads: int, num_kv_heads: int,
                  head_dim: int, page_size: int = 16, dtype="f16", causal: bool = True,
                  sm_scale: Optional[float] = None, max_kv_splits: int = 0, num_cus: int = 0,
-                 narrow_kernel: str = "mfma", kv_shared: bool = False):
+                 narrow_kernel: str = "mfma", kv_shared: bool = False, shared_pages: int = 0):
+        """shared_pages > 0 declares that every sequence's first shared_pages page ids
+        name the same pages (rpa_plan_create_shared): decode rows are then grouped
+        so the shared prefix is read once per group."""
         lib = load()
         self._qo = _host_i32(qo_indptr)
         self._kp = _host_i32(kv_page_indptr)
@@ -172,8 +176,13 @@ class Plan:
                               max_kv_splits, num_cus, narrow_kernel, kv_shared)
         h = ctypes.c_void_p()
         p = lambda a: a.ctypes.data if a.size else None
-        _check(lib.rpa_plan_create(ctypes.byref(self.params), self.batch, p(self._qo), p(self._kp), p(self._kl),
-                                   ctypes.byref(h)))
+        if shared_pages:
+            _check(lib.rpa_plan_create_shared(ctypes.byref(self.params), self.batch, p(self._qo), p(self._kp),
+                                              p(self._kl), int(shared_pages), ctypes.byref(h)))
+        else:
+            _check(lib.rpa_plan_create(ctypes.byref(self.params), self.batch, p(self._qo), p(self._kp),
+                                       p(self._kl), ctypes.byref(h)))
+        self.shared_pages = int(shared_pages)
         self._h = h
         self._keep = ()
         self.workspace = None

@@ -20,6 +20,7 @@
 struct rpa_plan {
     rpa_params params{};
     int32_t batch = 0;
+    int32_t shared_pages = 0;  // declared shared prefix (rpa_plan_create_shared)
     rpa::Schedule sched;
     rpa::WorkspaceLayout ws_layout{};  // byte offsets within the workspace
     // bound state
@@ -63,6 +64,16 @@ hipEvent_t prof_event() {
     return e;
 }
 
+// The schedule's part of a workspace image: tile records and the sequence table (the
+// counters and error word after them stay zero).
+void write_image(const rpa_plan* plan, char* img) {
+    const auto& S = plan->sched;
+    if (!S.tiles.empty())
+        std::memcpy(img + plan->ws_layout.off_tiles, S.tiles.data(), S.tiles.size() * sizeof(rpa::Tile));
+    if (!S.seqtab.empty())
+        std::memcpy(img + plan->ws_layout.off_seqtab, S.seqtab.data(), S.seqtab.size() * sizeof(int32_t));
+}
+
 // Enqueue the plan's attention kernels over a workspace image at `ws` (tiles, split
 // counters and partials at the offsets of plan->ws_layout); error bits go to err_flag.
 rpa_status launch_plan(const rpa_plan* plan, char* ws, const int32_t* page_idx, int64_t num_pages, int32_t* err_flag,
@@ -88,6 +99,7 @@ rpa_status launch_plan(const rpa_plan* plan, char* ws, const int32_t* page_idx, 
     L.a.causal = P.causal;
     L.a.err_flag = err_flag;
     L.a.counters = reinterpret_cast<int32_t*>(ws + WL.off_counters);
+    L.a.seqtab = reinterpret_cast<const int32_t*>(ws + WL.off_seqtab);
     L.head_dim = P.head_dim;
     L.bf16 = P.dtype == RPA_BF16;
     L.n_tiles = int64_t(S.tiles.size());
@@ -105,6 +117,7 @@ rpa_status launch_plan(const rpa_plan* plan, char* ws, const int32_t* page_idx, 
     // Pages read by one sequence only are streamed past L2 (non-temporal), which keeps the
     // schedule, page indices and Q resident; shared pages stay cached.
     L.kv_stream = P.kv_shared == 0;
+    L.group = S.group_tiles > 0;
     if (S.fused) {  // wide and narrow tiles interleaved in one launch (timed as "wide")
         if (prof) {
             e0.a = prof_event();
@@ -152,6 +165,12 @@ const char* rpa_version(void) { return "0.1.0"; }
 rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_t* qo_indptr_h,
                            const int32_t* kv_page_indptr_h, const int32_t* kv_last_page_len_h,
                            rpa_plan** out) {
+    return rpa_plan_create_shared(params, batch, qo_indptr_h, kv_page_indptr_h, kv_last_page_len_h, 0, out);
+}
+
+rpa_status rpa_plan_create_shared(const rpa_params* params, int32_t batch, const int32_t* qo_indptr_h,
+                                  const int32_t* kv_page_indptr_h, const int32_t* kv_last_page_len_h,
+                                  int32_t shared_pages, rpa_plan** out) {
     if (!params || !out) return set_err(RPA_E_ARG, "params and out must be non-NULL");
     *out = nullptr;
     if (params->dtype != RPA_F16 && params->dtype != RPA_BF16)
@@ -161,8 +180,10 @@ rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_
     if (params->narrow_kernel != 0 && params->narrow_kernel != 1)
         return set_err(RPA_E_ARG, "narrow_kernel must be 0 (MFMA) or 1 (VALU)");
     if (params->kv_shared != 0 && params->kv_shared != 1) return set_err(RPA_E_ARG, "kv_shared must be 0 or 1");
+    if (shared_pages < 0) return set_err(RPA_E_ARG, "shared_pages must be >= 0");
     rpa::PlanParams pp{params->num_qo_heads, params->num_kv_heads, params->head_dim, params->page_size,
-                       params->causal, params->max_kv_splits, params->num_cus, params->narrow_kernel};
+                       params->causal,       params->max_kv_splits, params->num_cus,  params->narrow_kernel,
+                       shared_pages};
     rpa_plan* plan = new (std::nothrow) rpa_plan();
     if (!plan) return set_err(RPA_E_ARG, "out of host memory");
     std::string err;
@@ -179,9 +200,10 @@ rpa_status rpa_plan_create(const rpa_params* params, int32_t batch, const int32_
     }
     plan->params = *params;
     plan->batch = batch;
+    plan->shared_pages = shared_pages;
     const auto& S = plan->sched;
-    plan->ws_layout = rpa::workspace_layout(int64_t(S.tiles.size()), int64_t(S.merges.size()), S.partial_rows,
-                                            params->head_dim);
+    plan->ws_layout = rpa::workspace_layout(int64_t(S.tiles.size()), int64_t(S.seqtab.size()),
+                                            int64_t(S.merges.size()), S.partial_rows, params->head_dim);
     plan->staging_bytes = plan->ws_layout.off_part_lse;  // tiles, then the zeroed counters and error word
     *out = plan;
     return RPA_OK;
@@ -209,12 +231,13 @@ rpa_status rpa_workspace_bytes(const rpa_params* params, int32_t batch, int64_t 
     if (!params || !bytes_out) return set_err(RPA_E_ARG, "params and bytes_out must be non-NULL");
     *bytes_out = 0;
     rpa::PlanParams pp{params->num_qo_heads, params->num_kv_heads, params->head_dim, params->page_size,
-                       params->causal, params->max_kv_splits, params->num_cus, params->narrow_kernel};
+                       params->causal,       params->max_kv_splits, params->num_cus,  params->narrow_kernel,
+                       0};
     rpa::ScheduleBound B{};
     std::string err;
     const int rc = rpa::schedule_bound(pp, batch, total_q, total_pages, &B, &err);
     if (rc != 0) return set_err(rpa_status(rc), err);
-    *bytes_out = rpa::workspace_layout(B.tiles, B.merges, B.partial_rows, params->head_dim).bytes;
+    *bytes_out = rpa::workspace_layout(B.tiles, B.seqtab, B.merges, B.partial_rows, params->head_dim).bytes;
     return RPA_OK;
 }
 
@@ -250,10 +273,8 @@ rpa_status rpa_plan_bind(rpa_plan* plan, const int32_t* kv_page_indices_d, int64
             plan->staging = nullptr;
             return hip_err(e, "hipHostMalloc(schedule staging)");
         }
-        char* img = static_cast<char*>(plan->staging);
-        std::memset(img, 0, plan->staging_bytes);
-        if (!S.tiles.empty())
-            std::memcpy(img + plan->ws_layout.off_tiles, S.tiles.data(), S.tiles.size() * sizeof(rpa::Tile));
+        std::memset(plan->staging, 0, plan->staging_bytes);
+        write_image(plan, static_cast<char*>(plan->staging));
     }
     hipError_t e = hipMemcpyAsync(workspace_d, plan->staging, plan->staging_bytes, hipMemcpyHostToDevice,
                                   static_cast<hipStream_t>(stream));
@@ -269,8 +290,8 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
                            const int32_t* kv_last_page_len_h) {
     if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
     const rpa_params& P = plan->params;
-    rpa::PlanParams pp{P.num_qo_heads, P.num_kv_heads, P.head_dim, P.page_size, P.causal, P.max_kv_splits,
-                       P.num_cus, P.narrow_kernel};
+    rpa::PlanParams pp{P.num_qo_heads, P.num_kv_heads, P.head_dim,      P.page_size,       P.causal,
+                       P.max_kv_splits,  P.num_cus,      P.narrow_kernel, plan->shared_pages};
     rpa::Schedule S;
     std::string err;
     int rc = 0;
@@ -285,7 +306,7 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
     // grid (tile counts), the kernel (wide / narrow / mixed, K loads for split narrow
     // tiles) and, on the VALU kernel, its row capacity.  All must stay.
     auto valu_rows = [](int32_t r) { return r <= 2 ? 2 : r <= 4 ? 4 : 8; };
-    const bool same_kernel = S.narrow_split == O.narrow_split &&
+    const bool same_kernel = S.narrow_split == O.narrow_split && S.group_tiles == O.group_tiles &&
                              (P.narrow_kernel != 1 || S.narrow_tiles == 0 ||
                               valu_rows(S.narrow_max_rows) == valu_rows(O.narrow_max_rows));
     if (S.tiles.size() != O.tiles.size() || S.wide_tiles != O.wide_tiles || S.fused != O.fused ||
@@ -300,9 +321,7 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
     S.partial_rows = O.partial_rows;  // the workspace layout stays as bound
     std::swap(plan->sched, S);
     rpa::recycle_schedule(&S);  // the previous schedule's buffers serve the next update
-    if (plan->staging && !plan->sched.tiles.empty())
-        std::memcpy(static_cast<char*>(plan->staging) + plan->ws_layout.off_tiles, plan->sched.tiles.data(),
-                    plan->sched.tiles.size() * sizeof(rpa::Tile));
+    if (plan->staging) write_image(plan, static_cast<char*>(plan->staging));
     return RPA_OK;
 }
 
@@ -353,6 +372,9 @@ rpa_status rpa_run_noalloc(const rpa_plan* plan, const int32_t* kv_page_indices_
     // kernel (what the previous call left there is not zero)
     e = hipMemcpyAsync(ws + WL.off_tiles, S.tiles.data(), S.tiles.size() * sizeof(rpa::Tile),
                        hipMemcpyHostToDevice, st);
+    if (e == hipSuccess && !S.seqtab.empty())
+        e = hipMemcpyAsync(ws + WL.off_seqtab, S.seqtab.data(), S.seqtab.size() * sizeof(int32_t),
+                           hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync(schedule into the static scratch)");
     int32_t* cleared = reinterpret_cast<int32_t*>(ws + WL.off_counters);
     e = rpa::launch_clear(cleared, int64_t((WL.off_part_lse - WL.off_counters) / sizeof(int32_t)), st);

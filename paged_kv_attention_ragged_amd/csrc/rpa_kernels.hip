@@ -695,6 +695,13 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
 }
 
 
+// Keys of one 32-key step of a narrow tile (wave-uniform): first key's position, keys
+// that exist from it (masked at or past this count), offset of its first page id in
+// kv_page_indices, and the kGroup member whose rows alone see it (-1: all rows).
+struct StepKeys {
+    int key0, valid, pidx, owner;
+};
+
 // Combine of the 4 waves of a narrow tile (each walked its own keys) and the tile's
 // output: c_o holds each wave's unnormalised O rows ([wave * 16 + row][D + 4] fp32),
 // c_m / c_l its running max (log2 units) and sum per row.  Writes O (and LSE), or
@@ -758,7 +765,7 @@ __device__ __forceinline__ void narrow_combine_store(const AttnArgs& A, const Ti
 //     one d per lane -- the V^T operand layout;
 //   * S^T = K Q^T gives each lane one row (column l%16) and 4 consecutive keys per
 //     16-key block; the running max needs two cross-lane exchanges per step.
-template <int D, bool BF16, bool KROWS, bool NT>
+template <int D, bool BF16, bool KROWS, bool NT, bool GROUP>
 __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, char* smem) {
     constexpr int KW = NarrowLds<D>::KW;  // keys per wave step
     constexpr int VS = NarrowLds<D>::VS;  // V staging row stride (elements)
@@ -824,10 +831,38 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     // its keys are masked and their V zeroed once landed); a page index outside
     // [0, num_pages) raises the error flag and its keys read as zero K and V.
     constexpr int STRIDE = kWaves * KW;
-    auto pages_of = [&](int kb0, int (&pg)[KB]) {
+    // The keys of the step at (virtual) key v, wave-uniform: the first key's position,
+    // how many of its keys exist (at or past `valid` they are masked and their V
+    // zeroed), where its page ids start in kv_page_indices, and, in a kGroup tile, the
+    // member whose rows alone see it (-1: every row).  An ordinary tile walks its own
+    // keys: v is the key.  A kGroup tile walks S0 shared steps, then pos0 steps per
+    // member over that member's keys past the prefix (page base and length from the
+    // sequence table, scalar loads).
+    const int S0 = GROUP ? (T.kv_len + KW - 1) / KW : 0;
+    auto step_keys = [&](int v) -> StepKeys {
+        if constexpr (!GROUP) {
+            return StepKeys{v, T.kv_len - v, T.page_base + (v >> 4), -1};
+        } else {
+            // past the last step (the first step of a wave with no keys): nothing to read
+            if (v >= T.kv_end) return StepKeys{v, 0, 0, -1};
+            const int st = v / KW;
+            if (st < S0) return StepKeys{v, min(KW, T.kv_len - v), T.page_base + (v >> 4), -1};
+            // here pos0 > 0, since kv_end = 32 (S0 + q_count pos0) > v; i < q_count
+            const int i = (st - S0) / T.pos0, j = st - S0 - i * T.pos0;
+            const int pb = ((const_i32*)A.seqtab)[2 * (T.seq + i)];
+            const int kvl = ((const_i32*)A.seqtab)[2 * (T.seq + i) + 1];
+            const int key = T.kv_len + KW * j;
+            return StepKeys{key, min(KW, kvl - key), pb + (key >> 4), i};
+        }
+    };
+    auto pages_of = [&](const StepKeys& sk, int (&pg)[KB]) {
 #pragma unroll
-        for (int b = 0; b < KB; ++b)
-            pg[b] = kb0 + 16 * b < T.kv_len ? ((const_i32*)A.page_idx)[T.page_base + (kb0 >> 4) + b] : 0;
+        for (int b = 0; b < KB; ++b) {
+            if constexpr (GROUP)
+                pg[b] = 16 * b < sk.valid ? ((const_i32*)A.page_idx)[sk.pidx + b] : 0;
+            else
+                pg[b] = sk.key0 + 16 * b < T.kv_len ? ((const_i32*)A.page_idx)[T.page_base + (sk.key0 >> 4) + b] : 0;
+        }
     };
     // Bad pages of a step: bit b set for block b (wave-uniform); such blocks read page 0.
     // The error flag is written once after the key loop: a store between the loads
@@ -872,10 +907,11 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     };
     // Landed V of a step: zero keys at or past kv_len and keys of bad pages (a mask,
     // not a branch, so that each load is waited for on its own).
-    auto fix_v = [&](int kb0, int bad) {
+    auto fix_v = [&](const StepKeys& sk, int bad) {
 #pragma unroll
         for (int j = 0; j < VJ; ++j) {
-            const bool z = (bad & (1 << ((j * KPJ) >> 4))) || kb0 + j * KPJ + vkey >= T.kv_len;
+            const bool past = GROUP ? j * KPJ + vkey >= sk.valid : sk.key0 + j * KPJ + vkey >= T.kv_len;
+            const bool z = (bad & (1 << ((j * KPJ) >> 4))) || past;
             const uint32_t keep = z ? 0u : ~0u;
             vf[j] &= u32x4{keep, keep, keep, keep};
         }
@@ -886,16 +922,21 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     // and step n+2's page ids are requested.
     int kbase = T.kv_begin + wave * KW;
     int pg_cur[KB], pg_nxt[KB];
+    StepKeys sk_cur = step_keys(kbase), sk_nxt = sk_cur;
     int bad_cur = 0, bad_nxt = 0;
     // First step's loads, unconditional: a wave with no keys (a tile of fewer than
     // kWaves * KW keys) reads page 0 and never uses it.  A branch here would leave the
     // compiler, where its two paths join, waiting for every load in flight.
-    pages_of(kbase, pg_cur);
+    pages_of(sk_cur, pg_cur);
     bad_cur = check_pages(pg_cur);
     load_k(pg_cur);
     load_v(pg_cur);
-    if (kbase + STRIDE < T.kv_end) pages_of(kbase + STRIDE, pg_nxt);
-    // Q rows into the operand layout through the wave's LDS area (free until its first
+    if (kbase + STRIDE < T.kv_end) {
+        sk_nxt = step_keys(kbase + STRIDE);
+        pages_of(sk_nxt, pg_nxt);
+    }
+    // (kGroup tiles carry the descriptors of the current and next steps, which cost
+    // scalar loads; an ordinary tile recomputes its own from the key position) through the wave's LDS area (free until its first
     // step), while those loads are in flight.
     static_assert(16 * KS <= KW * VS, "Q staging fits the wave's area");
 #pragma unroll
@@ -909,6 +950,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     auto step = [&](int kbase, auto more_tag) {
         constexpr bool more = decltype(more_tag)::value;
         const int knext = kbase + STRIDE;
+        const StepKeys cur = GROUP ? sk_cur : step_keys(kbase);
 
         // ---- (KROWS) K through the wave's LDS area: rows in, MFMA operands out (lane:
         // key 16b + col, d = 32kk + 8grp .. +8); V reuses the area after Q K^T ----
@@ -942,7 +984,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
         }
 
         // ---- stage V (fp16, natural layout) ----
-        if (bad_cur || kbase + KW > T.kv_len) fix_v(kbase, bad_cur);
+        if (bad_cur || (GROUP ? cur.valid < KW : kbase + KW > T.kv_len)) fix_v(cur, bad_cur);
         u16x2 vmax = {0, 0};  // largest fp16 |V| pattern of this step (bf16 only)
 #pragma unroll
         for (int j = 0; j < VJ; ++j) {
@@ -957,11 +999,22 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
         if constexpr (more) {
             load_v(pg_nxt);
             bad_cur = bad_nxt;
-            if (knext + STRIDE < T.kv_end) pages_of(knext + STRIDE, pg_nxt);
+            if constexpr (GROUP) sk_cur = sk_nxt;
+            if (knext + STRIDE < T.kv_end) {
+                if constexpr (GROUP) {
+                    sk_nxt = step_keys(knext + STRIDE);
+                    pages_of(sk_nxt, pg_nxt);
+                } else {
+                    pages_of(step_keys(knext + STRIDE), pg_nxt);
+                }
+            }
         }
 
         // ---- online softmax (lane: row `col`, keys 16b + 4grp + i) ----
-        const bool need_mask = (kbase + KW > T.kv_len) || (A.causal && kbase + KW - 1 > pos_min);
+        // (kGroup rows are decode rows: every key of their steps is at or before their
+        // position, so only members and the valid count mask them)
+        const bool need_mask = GROUP ? cur.valid < KW || cur.owner >= 0
+                                     : (kbase + KW > T.kv_len) || (A.causal && kbase + KW - 1 > pos_min);
         float bmax = -INFINITY;
 #pragma unroll
         for (int b = 0; b < KB; ++b)
@@ -969,8 +1022,13 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
             for (int i = 0; i < 4; ++i) {
                 float x = s[b][i] * A.c_log2;
                 if (need_mask) {
-                    const int key = kbase + 16 * b + 4 * grp + i;
-                    if (key >= T.kv_len || (A.causal && key > pos)) x = -INFINITY;
+                    if constexpr (GROUP) {
+                        const int koff = 16 * b + 4 * grp + i;
+                        if (koff >= cur.valid || (cur.owner >= 0 && tok != cur.owner)) x = -INFINITY;
+                    } else {
+                        const int key = kbase + 16 * b + 4 * grp + i;
+                        if (key >= T.kv_len || (A.causal && key > pos)) x = -INFINITY;
+                    }
                 }
                 s[b][i] = x;
                 bmax = fmaxf(bmax, x);
@@ -1309,18 +1367,23 @@ void attn_wide_kernel(AttnArgs A) {
 // Narrow tiles: three workgroups per CU (32-key wave steps keep the kernel within
 // the 168 registers and 53 KiB of LDS that allows), so more tiles' loads are in
 // flight per CU.
-template <int D, bool BF16, bool KROWS, bool NT>
+// GRP: the plan has kGroup tiles (a separate instantiation, so that plans without them
+// keep the register allocation of the plain narrow path).
+template <int D, bool BF16, bool KROWS, bool NT, bool GRP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_narrow_kernel(AttnArgs A) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const Tile T = A.tiles[blockIdx.x];
     if (T.q_count <= 0) return;
-    narrow_tile<D, BF16, KROWS, NT>(A, T, smem);
+    if (GRP && T.kind == kGroup)
+        narrow_tile<D, BF16, KROWS, NT, true>(A, T, smem);
+    else
+        narrow_tile<D, BF16, KROWS, NT, false>(A, T, smem);
 }
 
 // Both kinds in one launch (mixed batches): each workgroup takes its tile's path.  Both
 // paths use 4 waves and fit three workgroups per CU; the LDS is the larger of the two.
-template <int D, bool BF16, bool KROWS, bool NT>
+template <int D, bool BF16, bool KROWS, bool NT, bool GRP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_mixed_kernel(AttnArgs A) {
     static_assert(kWaves == kWideWaves, "one workgroup size for both paths");
@@ -1329,8 +1392,10 @@ void attn_mixed_kernel(AttnArgs A) {
     if (T.q_count <= 0) return;
     if (T.kind == kWide)
         wide_tile<D, BF16>(A, T, smem);
+    else if (GRP && T.kind == kGroup)
+        narrow_tile<D, BF16, KROWS, NT, true>(A, T, smem);
     else
-        narrow_tile<D, BF16, KROWS, NT>(A, T, smem);
+        narrow_tile<D, BF16, KROWS, NT, false>(A, T, smem);
 }
 
 // ---- host-side launchers -----------------------------------------------------------------
@@ -1442,10 +1507,16 @@ hipError_t launch_wide(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, 
                   : launch_with_lds<&attn_wide_kernel<64, false>>(L, WideCfg<64>::bytes, kWideWaves * 64, stream, ev0, ev1);
 }
 
+template <int D, bool BF16, bool NT, bool GRP>
+hipError_t launch_narrow_g(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+    return L.k_rows ? launch_with_lds<&attn_narrow_kernel<D, BF16, true, NT, GRP>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1)
+                    : launch_with_lds<&attn_narrow_kernel<D, BF16, false, NT, GRP>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1);
+}
+
 template <int D, bool BF16, bool NT>
 hipError_t launch_narrow_nt(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
-    return L.k_rows ? launch_with_lds<&attn_narrow_kernel<D, BF16, true, NT>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1)
-                    : launch_with_lds<&attn_narrow_kernel<D, BF16, false, NT>>(L, NarrowLds<D>::bytes, kWaves * 64, stream, ev0, ev1);
+    return L.group ? launch_narrow_g<D, BF16, NT, true>(L, stream, ev0, ev1)
+                   : launch_narrow_g<D, BF16, NT, false>(L, stream, ev0, ev1);
 }
 
 template <int D, bool BF16>
@@ -1457,7 +1528,8 @@ hipError_t launch_narrow_d(const LaunchAttn& L, hipStream_t stream, hipEvent_t e
 template <int D, bool BF16, bool KROWS, bool NT>
 hipError_t launch_mixed_k(const LaunchAttn& L, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int lds = WideCfg<D>::bytes > NarrowLds<D>::bytes ? WideCfg<D>::bytes : NarrowLds<D>::bytes;
-    return launch_with_lds<&attn_mixed_kernel<D, BF16, KROWS, NT>>(L, lds, kWaves * 64, stream, ev0, ev1);
+    return L.group ? launch_with_lds<&attn_mixed_kernel<D, BF16, KROWS, NT, true>>(L, lds, kWaves * 64, stream, ev0, ev1)
+                   : launch_with_lds<&attn_mixed_kernel<D, BF16, KROWS, NT, false>>(L, lds, kWaves * 64, stream, ev0, ev1);
 }
 
 template <int D, bool BF16>

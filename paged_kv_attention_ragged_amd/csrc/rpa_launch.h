@@ -28,6 +28,7 @@ struct AttnArgs {
     int32_t causal;
     int32_t* err_flag;        // error word: ErrBits OR-ed atomically
     int32_t* counters;        // one per split group: pieces finished (reset to 0 by the last)
+    const int32_t* seqtab;    // kGroup tiles: {kv_page_indptr[b], kv_len} per sequence
 };
 
 struct LaunchAttn {
@@ -38,6 +39,7 @@ struct LaunchAttn {
     bool k_rows;      // narrow kernel: K loaded in whole rows through LDS (else straight into
                       // MFMA operand layout)
     bool kv_stream;   // narrow tiles: K/V loads non-temporal (pages not shared by sequences)
+    bool group;       // the tiles include kGroup tiles (the kernel instantiation that runs them)
 };
 
 

@@ -92,7 +92,8 @@ void order_wide_for_xcds(std::vector<Piece>& wide) {
 // in page faults than the planning itself.
 thread_local Schedule t_sched;
 thread_local std::vector<QTile> base;
-thread_local std::vector<Piece> wide, narrow;
+thread_local std::vector<Piece> wide, narrow, group;
+thread_local std::vector<std::pair<int32_t, int32_t>> elig;  // (sequence, kv_len) of groupable decode rows
 
 }  // namespace
 
@@ -100,10 +101,12 @@ namespace {
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
-WorkspaceLayout workspace_layout(int64_t tiles, int64_t merges, int64_t partial_rows, int head_dim) {
+WorkspaceLayout workspace_layout(int64_t tiles, int64_t seqtab_entries, int64_t merges, int64_t partial_rows,
+                                 int head_dim) {
     WorkspaceLayout L{};
     L.off_tiles = 0;
-    L.off_counters = align256(size_t(tiles) * sizeof(Tile));
+    L.off_seqtab = align256(size_t(tiles) * sizeof(Tile));
+    L.off_counters = L.off_seqtab + align256(size_t(seqtab_entries) * sizeof(int32_t));
     L.off_flags = L.off_counters + align256(size_t(merges) * sizeof(int32_t));
     L.off_part_lse = L.off_flags + 256;
     L.off_part_o = L.off_part_lse + align256(size_t(partial_rows) * sizeof(float));
@@ -155,6 +158,9 @@ int schedule_bound(const PlanParams& p, int32_t batch, int64_t total_q, int64_t 
         partial = split_pieces * max_rows;
     }
     out->tiles = kXcds * pieces;
+    // kGroup tiles replace at least two narrow tiles each (the counts above hold), and
+    // their sequence table holds two entries per sequence
+    out->seqtab = 2 * int64_t(batch);
     out->merges = merges;
     out->partial_rows = partial;
     return OK;
@@ -183,6 +189,8 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     Schedule& S = t_sched;
     S.tiles.clear();
     S.merges.clear();
+    S.seqtab.clear();
+    S.group_tiles = 0;
     S.partial_rows = 0;
     S.tokens_per_tile = S.block_m = S.block_n = 0;
     S.wide_tiles = S.narrow_tiles = 0;
@@ -194,6 +202,9 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     base.clear();
     wide.clear();
     narrow.clear();
+    group.clear();
+    elig.clear();
+    if (p.shared_pages < 0) return fail(err, E_ARG, "shared_pages must be >= 0");
     S.block_n = block_n_for(p.head_dim);
     S.block_m = block_m_for(p.head_dim);
     S.tokens_per_tile = S.block_m / G;
@@ -203,6 +214,34 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
         return fail(err, E_INDPTR, "qo_indptr[0] (%ld) and kv_page_indptr[0] (%ld) must be 0", qo_indptr[0],
                     kv_page_indptr[0]);
     base.reserve(size_t(batch) * p.num_kv_heads);
+    // query tiles of one sequence: tokens in chunks of TQ, per kv head
+    auto add_seq_tiles = [&](int32_t b, int32_t q_len, int32_t kv_len) {
+        for (int32_t hk = 0; hk < p.num_kv_heads; ++hk)
+            for (int32_t t0 = 0; t0 < q_len; t0 += TQ) {
+                QTile t;
+                t.seq = b;
+                t.kv_head = hk;
+                t.q_row0 = qo_indptr[b] + t0;
+                t.q_count = std::min(TQ, q_len - t0);
+                t.pos0 = kv_len - q_len + t0;
+                t.kv_len = kv_len;
+                t.page_base = kv_page_indptr[b];
+                // keys past the last query's position are masked for every row: skip them
+                t.kv_end = p.causal ? std::min(kv_len, t.pos0 + t.q_count) : kv_len;
+                // The path is chosen per sequence, not per tile: a sequence whose rows
+                // all fit one narrow tile (decode rows, a few tokens of few heads) is
+                // narrow; every tile of a longer sequence is wide, its partial last tile
+                // included.  A row's path (and so its rounding) then depends on its own
+                // sequence only: a padded batch and its ragged twin put each real row
+                // in tiles of the same kind, at the same offset.
+                t.kind = int64_t(q_len) * G <= (p.narrow_valu ? kValuRows : kNarrowRows) ? kNarrow : kWide;
+                base.push_back(t);
+            }
+    };
+    // Shared-prefix grouping (kGroup tiles): MFMA narrow path only, at least two rows'
+    // worth of sequences per tile.
+    const int64_t shared_keys = int64_t(p.shared_pages) * kPageSize;
+    const int32_t group_rows = p.shared_pages > 0 && !p.narrow_valu ? kNarrowRows / G : 0;
     for (int32_t b = 0; b < batch; ++b) {
         if (qo_indptr[b + 1] < qo_indptr[b]) return fail(err, E_INDPTR, "qo_indptr decreases at %ld", b);
         if (kv_page_indptr[b + 1] < kv_page_indptr[b])
@@ -226,28 +265,73 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
         const int64_t d = kv_len - q_len;
         S.visible_pairs += p.causal ? (int64_t(q_len) * d + int64_t(q_len) * (q_len + 1) / 2) * p.num_qo_heads
                                     : int64_t(q_len) * kv_len * p.num_qo_heads;
-        for (int32_t hk = 0; hk < p.num_kv_heads; ++hk)
-            for (int32_t t0 = 0; t0 < q_len; t0 += TQ) {
-                QTile t;
-                t.seq = b;
-                t.kv_head = hk;
-                t.q_row0 = qo_indptr[b] + t0;
-                t.q_count = std::min(TQ, q_len - t0);
-                t.pos0 = kv_len - q_len + t0;
-                t.kv_len = kv_len;
-                t.page_base = kv_page_indptr[b];
-                // keys past the last query's position are masked for every row: skip them
-                t.kv_end = p.causal ? std::min(kv_len, t.pos0 + t.q_count) : kv_len;
-                // The path is chosen per sequence, not per tile: a sequence whose rows
-                // all fit one narrow tile (decode rows, a few tokens of few heads) is
-                // narrow; every tile of a longer sequence is wide, its partial last tile
-                // included.  A row's path (and so its rounding) then depends on its own
-                // sequence only: a padded batch and its ragged twin put each real row
-                // in tiles of the same kind, at the same offset.
-                t.kind = int64_t(q_len) * G <= (p.narrow_valu ? kValuRows : kNarrowRows) ? kNarrow : kWide;
-                base.push_back(t);
-            }
+        // A decode row that sees the whole declared shared prefix can join a kGroup tile.
+        if (group_rows >= 2 && q_len == 1 && kv_len >= shared_keys) {
+            elig.push_back({b, kv_len});
+            continue;
+        }
+        add_seq_tiles(b, q_len, kv_len);
     }
+    if (batch > 0 && int64_t(qo_indptr[batch]) * p.num_qo_heads * p.head_dim > (int64_t(1) << 40))
+        return fail(err, E_ARG, "batch too large");
+
+    // ---- kGroup tiles: consecutive decode rows over a shared prefix -----------------------
+    // Up to group_rows (16 / G) consecutive sequences per tile, so that the prefix is read
+    // once for all of them.  Members' own keys are walked in whole 32-key steps padded to
+    // the longest member; a group ends early rather than pad more than a quarter of its
+    // private steps.  A lone sequence keeps an ordinary narrow tile.
+    if (!elig.empty()) {
+        const int32_t S0 = int32_t(ceil_div(shared_keys, 32));
+        auto priv_steps = [&](int32_t kv_len) { return int32_t(ceil_div(kv_len - shared_keys, 32)); };
+        size_t i = 0;
+        while (i < elig.size()) {
+            size_t j = i + 1;
+            int64_t sum = priv_steps(elig[i].second);
+            int32_t pmax = int32_t(sum);
+            while (j < elig.size() && int64_t(j - i) < group_rows && elig[j].first == elig[j - 1].first + 1) {
+                const int32_t pj = priv_steps(elig[j].second);
+                const int32_t pm = std::max(pmax, pj);
+                if (4 * (sum + pj) < 3 * int64_t(j - i + 1) * pm) break;  // padding would waste > 1/4
+                sum += pj;
+                pmax = pm;
+                ++j;
+            }
+            const int32_t b0 = elig[i].first, n = int32_t(j - i);
+            if (n == 1) {
+                add_seq_tiles(b0, 1, elig[i].second);
+            } else {
+                for (int32_t hk = 0; hk < p.num_kv_heads; ++hk) {
+                    Tile t{};
+                    t.q_row0 = qo_indptr[b0];
+                    t.q_count = n;
+                    t.pos0 = pmax;  // private steps per member
+                    t.kv_len = int32_t(shared_keys);
+                    t.page_base = kv_page_indptr[b0];
+                    t.kv_head = hk;
+                    t.kv_begin = 0;
+                    t.kv_end = 32 * (S0 + n * pmax);
+                    t.part = -1;
+                    t.seq = b0;
+                    t.split = 0;
+                    t.n_splits = 1;
+                    t.kind = kGroup;
+                    t.group = -1;
+                    group.push_back({t, int64_t(t.kv_end) + 64});
+                }
+            }
+            i = j;
+        }
+    }
+    if (!group.empty()) {
+        S.group_tiles = int64_t(group.size());
+        S.seqtab.resize(2 * size_t(batch));
+        for (int32_t b = 0; b < batch; ++b) {
+            const int32_t n_pages = kv_page_indptr[b + 1] - kv_page_indptr[b];
+            S.seqtab[2 * b] = kv_page_indptr[b];
+            S.seqtab[2 * b + 1] = n_pages == 0 ? 0 : (n_pages - 1) * kPageSize + kv_last_page_len[b];
+        }
+    }
+
     if (batch > 0 && int64_t(qo_indptr[batch]) * p.num_qo_heads * p.head_dim > (int64_t(1) << 40))
         return fail(err, E_ARG, "batch too large");
 
@@ -262,12 +346,12 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     for (auto& t : base) max_keys = std::max(max_keys, t.kv_end);
     const int32_t max_chunks = int32_t(ceil_div(max_keys, kChunkKeys));
     auto units = [&](int64_t chunk_keys) {
-        int64_t u = 0;
+        int64_t u = int64_t(group.size());  // kGroup tiles: one work item each, never split
         for (auto& t : base) u += std::max<int64_t>(1, ceil_div(t.kv_end, chunk_keys));
         return u;
     };
     int64_t C = int64_t(max_chunks) * kChunkKeys;
-    if (p.max_kv_splits != 1 && int64_t(base.size()) < target && max_chunks > 1) {
+    if (p.max_kv_splits != 1 && int64_t(base.size() + group.size()) < target && max_chunks > 1) {
         if (units(kChunkKeys) < target) {
             C = kChunkKeys;
         } else {  // largest c in [1, max_chunks] with units(c * kChunkKeys) >= target
@@ -356,6 +440,12 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
             S.narrow_max_rows = 0;
             S.narrow_split = false;
         }
+    }
+    // kGroup tiles run on the narrow path, never as wide tiles.
+    for (const auto& pc : group) {
+        narrow.push_back(pc);
+        ++S.narrow_tiles;
+        S.narrow_max_rows = std::max(S.narrow_max_rows, pc.t.q_count * G);
     }
     // Narrow tiles read their keys once: longest first (LPT), ties in natural order.
     auto longer = [](const Piece& a, const Piece& b) { return a.cost > b.cost; };

@@ -33,7 +33,18 @@ constexpr int block_n_for(int) { return 32; }
 enum TileKind : int32_t {
     kWide = 0,    // up to 128 rows; 4 waves split the rows, walk keys together
     kNarrow = 1,  // up to 16 rows (decode-like); 4 waves split the keys
+    kGroup = 2,   // up to 16 rows of several decode sequences that share a prefix; run
+                  // by the narrow path over a virtual key range (see below)
 };
+
+// A kGroup tile holds the decode rows (q_len 1) of q_count consecutive sequences
+// seq .. seq + q_count - 1 whose first kv_len keys (the shared prefix, a multiple of
+// 16) lie in the same physical pages.  Its keys are walked as virtual 32-key steps:
+// S0 = ceil(kv_len / 32) shared steps (pages from page_base = the first sequence's
+// kv_page_indptr), visible to every row, then pos0 steps per member sequence i (its
+// own keys kv_len + 32 j, pages from its own page table), visible to its rows only;
+// kv_end = 32 (S0 + q_count pos0).  The members' page bases and lengths come from the
+// per-sequence table (Schedule::seqtab).  Never split.
 
 // One unit of attention work: the rows (tokens q_row0 .. q_row0+q_count-1, all
 // qo heads of kv head `kv_head`) against keys [kv_begin, kv_end) of one sequence.
@@ -73,11 +84,15 @@ struct PlanParams {
     int32_t max_kv_splits;  // 0 = decide, 1 = never, n = cap
     int32_t num_cus;
     int32_t narrow_valu;    // 1: narrow tiles (<= kValuRows rows) run on the VALU kernel
+    int32_t shared_pages;   // > 0: every sequence's first shared_pages page ids are the same
+                            // pages; decode rows are grouped into kGroup tiles
 };
 
 struct Schedule {
     std::vector<Tile> tiles;    // launch order
     std::vector<Merge> merges;
+    std::vector<int32_t> seqtab;  // with kGroup tiles: {kv_page_indptr[b], kv_len} per sequence
+    int64_t group_tiles = 0;      // kGroup tiles among the narrow ones
     int64_t partial_rows = 0;
     int32_t tokens_per_tile = 0;
     int32_t block_m = 0;
@@ -107,19 +122,21 @@ void recycle_schedule(Schedule* s);
 // whatever their individual lengths.
 struct ScheduleBound {
     int64_t tiles;         // launch slots (split pieces and XCD padding included)
+    int64_t seqtab;        // sequence-table entries (int32)
     int64_t merges;        // split groups
     int64_t partial_rows;  // fp32 partial rows
 };
 int schedule_bound(const PlanParams& p, int32_t batch, int64_t total_q, int64_t total_pages, ScheduleBound* out,
                    std::string* err);
 
-// Byte layout of a plan's workspace: [tiles][split counters][error word][partial LSE]
-// [partial O].  rpa_plan_bind copies [0, off_part_lse) (tiles, zeroed counters, zeroed
-// error word); rpa_plan_upload copies [0, off_flags) only, so the error word keeps
-// what earlier runs raised until rpa_plan_check reads it.
+// Byte layout of a plan's workspace: [tiles][sequence table][split counters][error word]
+// [partial LSE][partial O].  rpa_plan_bind copies [0, off_part_lse) (tiles, sequence
+// table, zeroed counters, zeroed error word); rpa_plan_upload copies [0, off_flags)
+// only, so the error word keeps what earlier runs raised until rpa_plan_check reads it.
 struct WorkspaceLayout {
-    size_t off_tiles, off_counters, off_flags, off_part_lse, off_part_o, bytes;
+    size_t off_tiles, off_seqtab, off_counters, off_flags, off_part_lse, off_part_o, bytes;
 };
-WorkspaceLayout workspace_layout(int64_t tiles, int64_t merges, int64_t partial_rows, int head_dim);
+WorkspaceLayout workspace_layout(int64_t tiles, int64_t seqtab_entries, int64_t merges, int64_t partial_rows,
+                                 int head_dim);
 
 }  // namespace rpa

@@ -535,3 +535,94 @@ def test_benchmark_floors_library_loads():
     lib = ctypes.CDLL(path)
     for name in ("rpa_floor_empty", "rpa_floor_stream", "rpa_floor_gather", "rpa_floor_mfma"):
         assert hasattr(lib, name), name
+
+
+# ----------------------------------------------------------------------------------------------
+# Shared-prefix plans (rpa_plan_create_shared): decode rows grouped over the prefix.
+# ----------------------------------------------------------------------------------------------
+
+def check_groups(b, plan, shared_pages):
+    """Group tiles of a shared-prefix plan: every eligible decode row (q_len 1, kv_len at
+    least the prefix) of every kv head is in exactly one tile of its own kind, group
+    members are consecutive sequences (consecutive query rows), a tile holds at most 16
+    rows, and its virtual steps cover the prefix and each member's own keys."""
+    t = plan.tiles()
+    G = b.num_qo_heads // b.num_kv_heads
+    Ks = 16 * shared_pages
+    grp = t[t[:, F["kind"]] == 2]
+    covered = {}
+    for r in grp:
+        n, b0, hk = int(r[F["q_count"]]), int(r[F["seq"]]), int(r[F["kv_head"]])
+        assert 2 <= n and n * G <= 16 and r[F["kv_len"]] == Ks and r[F["n_splits"]] == 1 and r[F["part"]] == -1
+        pm = int(r[F["pos0"]])
+        S0 = -(-Ks // 32)
+        assert r[F["kv_begin"]] == 0 and r[F["kv_end"]] == 32 * (S0 + n * pm)
+        assert r[F["q_row0"]] == b.qo_indptr[b0] and r[F["page_base"]] == b.kv_page_indptr[b0]
+        for i in range(n):
+            s = b0 + i
+            assert b.q_lens[s] == 1 and b.kv_lens[s] >= Ks and b.qo_indptr[s] == b.qo_indptr[b0] + i
+            assert 32 * pm >= b.kv_lens[s] - Ks
+            assert (s, hk) not in covered
+            covered[(s, hk)] = True
+    # ungrouped rows keep ordinary tiles: every (token, kv head) exactly once overall
+    cov = np.zeros((b.total_q, b.num_kv_heads), np.int32)
+    for r in t:
+        if r[F["q_count"]] == 0:
+            continue
+        if r[F["kind"]] == 2:
+            cov[r[F["q_row0"]]:r[F["q_row0"]] + r[F["q_count"]], r[F["kv_head"]]] += 1
+        elif r[F["split"]] == 0:
+            cov[r[F["q_row0"]]:r[F["q_row0"]] + r[F["q_count"]], r[F["kv_head"]]] += 1
+    assert (cov == 1).all()
+    return grp
+
+
+def test_shared_prefix_decode_rows_are_grouped():
+    # the shared-prefix decode step: 256 requests, 12 shared pages (192 tokens), kv 231,
+    # 4 query heads per kv head: four requests per tile, 512 tiles instead of 2048
+    b = lengths_batch([1] * 256, [231] * 256, H=32, Hk=8)
+    p = make_plan(b, shared_pages=12)
+    grp = check_groups(b, p, 12)
+    assert len(grp) == 512 and (grp[:, F["q_count"]] == 4).all() and (grp[:, F["pos0"]] == 2).all()
+    assert p.info["num_tiles"] == 512 and p.info["visible_pairs"] == make_plan(b).info["visible_pairs"]
+    # 8 query heads per kv head: pairs; 16 or more: nothing to group
+    assert (check_groups(lengths_batch([1] * 9, [300] * 9), make_plan(lengths_batch([1] * 9, [300] * 9),
+                                                                     shared_pages=5), 5)[:, F["q_count"]] <= 2).all()
+    b16 = lengths_batch([1] * 8, [300] * 8, H=16, Hk=1)
+    assert not (make_plan(b16, shared_pages=5).tiles()[:, F["kind"]] == 2).any()
+    # the VALU decode kernel does not take group tiles
+    assert not (make_plan(b, shared_pages=12, narrow_kernel="valu").tiles()[:, F["kind"]] == 2).any()
+
+
+def test_shared_prefix_grouping_rules():
+    # prefill rows, rows that do not see the whole prefix, and lone rows keep ordinary
+    # tiles; a group ends rather than pad a short member to a long one
+    q = [1, 1, 30, 1, 1, 1, 1, 1, 1, 1, 1, 1]
+    kv = [231, 240, 230, 231, 100, 231, 232, 900, 231, 233, 235, 1500]
+    b = lengths_batch(q, kv, H=32, Hk=8)
+    p = make_plan(b, shared_pages=12)
+    grp = check_groups(b, p, 12)
+    members = sorted({int(r[F["seq"]]) + i for r in grp for i in range(int(r[F["q_count"]]))})
+    assert 2 not in members and 4 not in members  # prefill; kv_len below the prefix
+    assert 7 not in members or 6 not in members  # 900 keys padded beside 232 wastes too much
+    for extra in (0, 3):
+        bb = lengths_batch([1] * 40, [16 * 7 + 5 + (i * extra) % 200 for i in range(40)], H=8, Hk=2)
+        check_groups(bb, make_plan(bb, shared_pages=7), 7)
+    # odd prefix page counts: the last shared step holds 16 keys
+    bo = lengths_batch([1] * 12, [16 * 5 + 9] * 12, H=16, Hk=4)
+    go = check_groups(bo, make_plan(bo, shared_pages=5), 5)
+    assert len(go) > 0 and (go[:, F["kv_end"]] == 32 * (3 + go[:, F["q_count"]] * 1)).all()
+
+
+def test_shared_prefix_plan_update_and_bounds():
+    b0 = lengths_batch([1] * 256, [231] * 256, H=32, Hk=8)
+    b1 = lengths_batch([1] * 256, [232] * 256, H=32, Hk=8)
+    p = make_plan(b0, shared_pages=12)
+    p.update(b1.qo_indptr, b1.kv_page_indptr, b1.kv_last_page_len)
+    assert np.array_equal(p.tiles(), make_plan(b1, shared_pages=12).tiles())
+    for b in (b0, b1, lengths_batch([1, 1, 40, 1], [300, 200, 250, 999], H=32, Hk=8)):
+        need = make_plan(b, shared_pages=12).info["workspace_bytes"]
+        assert need <= bound_of(b)
+    with pytest.raises(rpa.RPAError) as e:
+        make_plan(b0, shared_pages=-1)
+    assert e.value.status == "RPA_E_ARG"

@@ -1,5 +1,5 @@
 // Sanitizer driver for the library's host code: random ragged batches (and invalid
-// ones) through rpa_plan_create / info / tiles / update / destroy,
+// ones) through rpa_plan_create(_shared) / info / tiles / update / destroy,
 // rpa_workspace_bytes, rpa_trim_page_table, rpa_validate_page_table and the size
 // check of rpa_run_noalloc, built with AddressSanitizer and UndefinedBehaviorSanitizer.
 // Exits 0 when every call behaved; any sanitizer report aborts the run.
@@ -55,7 +55,10 @@ int main(int argc, char** argv) {
         }
         if (rng() % 25 == 0) kl[rng() % B] = 17;  // invalid last-page length
         rpa_plan* plan = nullptr;
-        const rpa_status st = rpa_plan_create(&p, B, qo.data(), kp.data(), kl.data(), &plan);
+        const int shared_pages = rng() % 3 == 0 ? int(rng() % 20) : 0;  // a declared common prefix
+        const rpa_status st = shared_pages
+                                  ? rpa_plan_create_shared(&p, B, qo.data(), kp.data(), kl.data(), shared_pages, &plan)
+                                  : rpa_plan_create(&p, B, qo.data(), kp.data(), kl.data(), &plan);
         size_t bound = 0;
         const rpa_status bs = rpa_workspace_bytes(&p, B, qo[B], kp[B], &bound);
         CHECK(bs == RPA_OK);

@@ -360,6 +360,16 @@ def bench_decode(args, floors):
     return res, b
 
 
+def walked_keys(b):
+    """Keys the plan's tiles walk, summed over tiles (a host-only plan)."""
+    import paged_kv_attention_ragged_amd as rpa
+    p = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
+                 num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal)
+    t = p.tiles()
+    p.close()
+    return float((t[:, 7].astype(np.int64) - t[:, 6]).sum())
+
+
 def bench_prefill(args, floors):
     """Long causal prompts: 4 x 8192, 64 qo / 8 kv heads, bf16 (every tile wide)."""
     import workloads as W
@@ -368,8 +378,20 @@ def bench_prefill(args, floors):
     rf = roofline(r["algorithmic"]["flops"], r["algorithmic"]["bytes"], r["kernel_ms"], floors, bound="mfma",
                   kernel="attn_wide_kernel")
     rf["algorithmic_flops_per_launch"] = r["algorithmic"]["flops"]
+    # A/B: the same prompts with the causal tail skip switched off (tiles walk to kv_len
+    # and mask); same results, so the time difference is what the skip saves
+    log("long prompts without the tail skip")
+    keys_on = walked_keys(b)
+    os.environ["RPA_DISABLE_TAIL_SKIP"] = "1"
+    try:
+        ns = measure(b, steps=max(3, args.steps // 10), warmup=1, floors=floors)
+        keys_off = walked_keys(b)
+    finally:
+        del os.environ["RPA_DISABLE_TAIL_SKIP"]
+    ab = {"skip_kernel_ms": r["kernel_ms"], "no_skip_kernel_ms": ns["kernel_ms"],
+          "no_skip_over_skip": ns["kernel_ms"] / r["kernel_ms"], "keys_walked_no_skip_over_skip": keys_off / keys_on}
     return {"workload": "mixed_long_prompts_4x8192", "ms_per_step": r["mean_ms"], "median_ms": r["median_ms"],
-            "tflops": r["tflops"], "roofline": rf, "dtype": b.dtype}
+            "tflops": r["tflops"], "roofline": rf, "dtype": b.dtype, "tail_skip_ab": ab}
 
 
 # ----------------------------------------------------------------------------------------------

@@ -39,6 +39,17 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   - Kernel faults are asynchronous and surface at the caller's next
  *     synchronisation, as usual for HIP.
+ *
+ * Environment (read by rpa_plan_create / rpa_plan_create_shared; for tests and
+ * measurement, off by default):
+ *   RPA_DISABLE_TAIL_SKIP=1  causal query tiles walk every key up to kv_len and
+ *                            mask the fully masked tail instead of skipping it
+ *                            (the skip of llama.cpp discussion #15958, switched
+ *                            off to time what it saves); results are unchanged.
+ *                            rpa_plan_update keeps the plan's setting.
+ *   RPA_LOG=1                one summary line per created or updated plan on
+ *                            stderr: tiles by kind, split groups, partial rows,
+ *                            workspace bytes.
  */
 #ifndef RPA_H
 #define RPA_H

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -21,6 +22,7 @@ struct rpa_plan {
     rpa_params params{};
     int32_t batch = 0;
     int32_t shared_pages = 0;  // declared shared prefix (rpa_plan_create_shared)
+    int32_t tail_skip = 1;     // RPA_DISABLE_TAIL_SKIP at create time, kept by update
     rpa::Schedule sched;
     rpa::WorkspaceLayout ws_layout{};  // byte offsets within the workspace
     // bound state
@@ -62,6 +64,34 @@ hipEvent_t prof_event() {
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
+}
+
+// Test and measurement switches, read from the environment when a plan is created.
+//   RPA_DISABLE_TAIL_SKIP=1  causal query tiles walk every key up to kv_len and mask
+//                            the tail instead of skipping it: the same results, at the
+//                            cost the skip saves (for A/B timing)
+//   RPA_LOG=1                one line per created or updated plan on stderr
+bool env_on(const char* name) {
+    const char* v = std::getenv(name);
+    return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+rpa::PlanParams plan_params(const rpa_params& P, int32_t shared_pages, int32_t tail_skip) {
+    rpa::PlanParams pp{P.num_qo_heads, P.num_kv_heads, P.head_dim,      P.page_size,  P.causal,
+                       P.max_kv_splits,  P.num_cus,      P.narrow_kernel, shared_pages};
+    pp.tail_skip = tail_skip;
+    return pp;
+}
+
+void log_plan(const char* what, const rpa_plan* plan) {
+    if (!env_on("RPA_LOG")) return;
+    const auto& S = plan->sched;
+    std::fprintf(stderr,
+                 "rpa: %s batch=%d total_q=%lld tiles=%zu (wide %lld, narrow %lld, group %lld%s) "
+                 "split_groups=%zu max_splits=%d partial_rows=%lld workspace=%zu B tail_skip=%d\n",
+                 what, plan->batch, (long long)S.total_q, S.tiles.size(), (long long)S.wide_tiles,
+                 (long long)S.narrow_tiles, (long long)S.group_tiles, S.fused ? ", one mixed launch" : "",
+                 S.merges.size(), S.max_splits, (long long)S.partial_rows, plan->ws_layout.bytes, plan->tail_skip);
 }
 
 // The schedule's part of a workspace image: tile records and the sequence table (the
@@ -181,9 +211,8 @@ rpa_status rpa_plan_create_shared(const rpa_params* params, int32_t batch, const
         return set_err(RPA_E_ARG, "narrow_kernel must be 0 (MFMA) or 1 (VALU)");
     if (params->kv_shared != 0 && params->kv_shared != 1) return set_err(RPA_E_ARG, "kv_shared must be 0 or 1");
     if (shared_pages < 0) return set_err(RPA_E_ARG, "shared_pages must be >= 0");
-    rpa::PlanParams pp{params->num_qo_heads, params->num_kv_heads, params->head_dim, params->page_size,
-                       params->causal,       params->max_kv_splits, params->num_cus,  params->narrow_kernel,
-                       shared_pages};
+    const int32_t tail_skip = env_on("RPA_DISABLE_TAIL_SKIP") ? 0 : 1;
+    const rpa::PlanParams pp = plan_params(*params, shared_pages, tail_skip);
     rpa_plan* plan = new (std::nothrow) rpa_plan();
     if (!plan) return set_err(RPA_E_ARG, "out of host memory");
     std::string err;
@@ -201,10 +230,12 @@ rpa_status rpa_plan_create_shared(const rpa_params* params, int32_t batch, const
     plan->params = *params;
     plan->batch = batch;
     plan->shared_pages = shared_pages;
+    plan->tail_skip = tail_skip;
     const auto& S = plan->sched;
     plan->ws_layout = rpa::workspace_layout(int64_t(S.tiles.size()), int64_t(S.seqtab.size()),
                                             int64_t(S.merges.size()), S.partial_rows, params->head_dim);
     plan->staging_bytes = plan->ws_layout.off_part_lse;  // tiles, then the zeroed counters and error word
+    log_plan("create", plan);
     *out = plan;
     return RPA_OK;
 }
@@ -230,9 +261,7 @@ rpa_status rpa_workspace_bytes(const rpa_params* params, int32_t batch, int64_t 
                                size_t* bytes_out) {
     if (!params || !bytes_out) return set_err(RPA_E_ARG, "params and bytes_out must be non-NULL");
     *bytes_out = 0;
-    rpa::PlanParams pp{params->num_qo_heads, params->num_kv_heads, params->head_dim, params->page_size,
-                       params->causal,       params->max_kv_splits, params->num_cus,  params->narrow_kernel,
-                       0};
+    const rpa::PlanParams pp = plan_params(*params, 0, 1);
     rpa::ScheduleBound B{};
     std::string err;
     const int rc = rpa::schedule_bound(pp, batch, total_q, total_pages, &B, &err);
@@ -290,8 +319,7 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
                            const int32_t* kv_last_page_len_h) {
     if (!plan) return set_err(RPA_E_ARG, "plan must be non-NULL");
     const rpa_params& P = plan->params;
-    rpa::PlanParams pp{P.num_qo_heads, P.num_kv_heads, P.head_dim,      P.page_size,       P.causal,
-                       P.max_kv_splits,  P.num_cus,      P.narrow_kernel, plan->shared_pages};
+    const rpa::PlanParams pp = plan_params(P, plan->shared_pages, plan->tail_skip);
     rpa::Schedule S;
     std::string err;
     int rc = 0;
@@ -322,6 +350,7 @@ rpa_status rpa_plan_update(rpa_plan* plan, const int32_t* qo_indptr_h, const int
     std::swap(plan->sched, S);
     rpa::recycle_schedule(&S);  // the previous schedule's buffers serve the next update
     if (plan->staging) write_image(plan, static_cast<char*>(plan->staging));
+    log_plan("update", plan);
     return RPA_OK;
 }
 

@@ -182,6 +182,15 @@ __device__ __forceinline__ float xor32(float x) {
     return __builtin_bit_cast(uint32_t, a) == __builtin_bit_cast(uint32_t, x) ? b : a;
 }
 
+// max(x[l], x[l ^ 32]) in every lane: v_permlane32_swap of x with itself leaves each
+// lane the pair {x[l], x[l ^ 32]} (in one order or the other), whose max needs no
+// selection.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 // Lazy-rescale threshold (log2 units): P never exceeds 2^kLazy = 256.
 constexpr float kLazy = 8.0f;
 
@@ -514,8 +523,9 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     auto ring = [](int x) { return x >= C::NS ? x - C::NS : x; };  // x mod NS, x < 2 NS
     constexpr int NS = C::NS;
 
-    // One unit u in slot u % NS: scores of u are in S; Q K^T of u + 1 goes to Sn.
-    auto unit = [&](int u, int slot_u, f32x16& S, f32x16& Sn) {
+    // One unit u in slot u % NS: S holds the scores of u on entry and those of u + 1
+    // (Q K^T, accumulated once the exponentials have used up u's) on exit.
+    auto unit = [&](int u, int slot_u, f32x16& S) {
         const int SL = slot_u;  // u % NS
         const int kv0 = T.kv_begin + C::UK * u;
         // V of unit u + 1 (landed and made visible by the last barrier) goes to fp16
@@ -535,7 +545,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         float bmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, S[r]);
-        bmax = fmaxf(bmax, xor32(bmax));
+        bmax = pair_max(bmax);
         const float bx = bmax * A.c_log2;
         if (__builtin_amdgcn_ballot_w64(bx > m_run + kLazy)) {
             const float m_new = bx > m_run + kLazy ? bx : m_run;
@@ -554,8 +564,8 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         }
         v_fp16_write(ring(SL + 1), vcv, u + 1 < nunits);
 
-        // ---- one basic block: Q K^T (next unit) | exponentials | P V ----
-        qk(ring(SL + 1), Sn);
+        // ---- one basic block: exponentials of unit u, then Q K^T of unit u + 1 and P V of
+        //      unit u, MFMA by MFMA, each operand read from LDS ahead of its MFMA ----
         u32x4 pf[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -567,19 +577,33 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
                 lsum = __builtin_amdgcn_fdot2(ph, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum, false);
                 pf[h][e] = __builtin_bit_cast(uint32_t, ph);
             }
-        const char* vp = smem + SL * SLOT + v_lane;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
+        {
+            static_assert(DK == 2 * DB, "as many Q K^T as P V steps");
+            const char* kp = smem + ring(SL + 1) * SLOT + k_lane;
+            const char* vp = smem + SL * SLOT + v_lane;
+            auto kread = [&](int kk) { return *(const u32x4*)(kp + 32 * R * kk); };
+            auto vread = [&](int i) {  // P V step i: keys 16 (i / DB) .., d block i % DB
+                const int h = i / DB, db = i % DB;
                 const u32x2 lo = ds_read_tr16((const uint16_t*)(vp + ((16 * h) / R) * GS + 64 * R * db));
                 const u32x2 hi = ds_read_tr16((const uint16_t*)(vp + ((16 * h + 8) / R) * GS + 64 * R * db));
-                const u32x4 va = {lo[0], lo[1], hi[0], hi[1]};
-                oacc[db] = mfma_pv(va, pf[h], oacc[db]);
+                return u32x4{lo[0], lo[1], hi[0], hi[1]};
+            };
+            constexpr int PF = 2;  // operands in flight ahead of the MFMA that uses them
+            u32x4 kb[DK], vb[DK];
+#pragma unroll
+            for (int i = 0; i < PF; ++i) {
+                kb[i] = kread(i);
+                vb[i] = vread(i);
             }
-        // scheduling hint for this basic block: the compiler's MFMA / LDS-read
-        // interleave for single-wave small GEMMs
-        __builtin_amdgcn_iglp_opt(1);
+            S = f32x16{};
+#pragma unroll
+            for (int i = 0; i < DK; ++i) {
+                if (i + PF < DK) kb[i + PF] = kread(i + PF);
+                S = mfma_qk(kb[i], qf[i], S, BF16);
+                if (i + PF < DK) vb[i + PF] = vread(i + PF);
+                oacc[i % DB] = mfma_pv(vb[i], pf[i / DB], oacc[i % DB]);
+            }
+        }
 
         // pages of unit u + NS (their latency overlaps the wait below)
         if (u + NS < nunits) pages_of(u + NS, pg_next);
@@ -631,14 +655,11 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             }
             barrier();
         }
-        f32x16 sa, sb;
-        qk(0, sa);
-        // (not unrolled: unrolled copies keep more registers live than the two waves
-        // per SIMD allow)
-        for (int u = 0, sl = 0; u < nunits; ++u, sl = ring(sl + 1)) {
-            unit(u, sl, sa, sb);
-            sa = sb;
-        }
+        // one score buffer: unit u's scores are spent on its exponentials before Q K^T
+        // of unit u + 1 accumulates into the same registers
+        f32x16 sc;
+        qk(0, sc);
+        for (int u = 0, sl = 0; u < nunits; ++u, sl = ring(sl + 1)) unit(u, sl, sc);
     }
 
     if (bad_any && lane == 0) raise_flag(A.err_flag, kErrPage);

@@ -118,10 +118,11 @@ WorkspaceLayout workspace_layout(int64_t tiles, int64_t seqtab_entries, int64_t 
 //  * query tiles: sequence b has ceil(q_b / TQ) <= floor(q_b / TQ) + 1 of them per kv
 //    head, and at most min(batch, total_q) sequences have queries, so there are at
 //    most H_kv (floor(total_q / TQ) + min(batch, total_q));
-//  * key ranges are split only when the query tiles number fewer than 2 N (N compute
-//    units).  The piece size C is then 256 keys if that gives fewer than 2 N pieces,
-//    else the largest multiple of 256 still giving at least 2 N; since
-//    ceil(k / C) <= 2 ceil(k / (C + 256)) for C >= 256, that is fewer than 4 N pieces.
+//  * key ranges are split only when the query tiles number fewer than the target, at
+//    most 2 N (N compute units).  The piece size C is then 256 keys if that gives fewer
+//    pieces than the target, else the largest multiple of 256 still giving at least the
+//    target; since ceil(k / C) <= 2 ceil(k / (C + 256)) for C >= 256, that is fewer
+//    than twice the target, so fewer than 4 N pieces (the bound below takes 2 N).
 //    Pieces therefore number at most max(query tiles, 4 N - 1), split groups fewer
 //    than 2 N, and partial rows at most (pieces) x (rows of the largest tile);
 //  * XCD padding lays the wide tiles out in 8 runs padded to the longest, so the launch
@@ -227,7 +228,7 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
                 t.kv_len = kv_len;
                 t.page_base = kv_page_indptr[b];
                 // keys past the last query's position are masked for every row: skip them
-                t.kv_end = p.causal ? std::min(kv_len, t.pos0 + t.q_count) : kv_len;
+                t.kv_end = p.causal && p.tail_skip ? std::min(kv_len, t.pos0 + t.q_count) : kv_len;
                 // The path is chosen per sequence, not per tile: a sequence whose rows
                 // all fit one narrow tile (decode rows, a few tokens of few heads) is
                 // narrow; every tile of a longer sequence is wide, its partial last tile
@@ -336,14 +337,27 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
         return fail(err, E_ARG, "batch too large");
 
     // ---- split-KV decision -------------------------------------------------------------
-    // When the query tiles alone are fewer than two per CU, cut the longest key ranges
-    // into pieces of C keys (C a multiple of kChunkKeys; pieces start at absolute key
-    // positions that are multiples of C), choosing the largest C that still gives two
-    // work items per CU (measured best for decode: 4 pieces of 256 keys beat 2, 6 or 8).
+    // A split costs a merge at the end of the launch (partials written, counted and read
+    // back by the last piece), so it is made only when the tiles are unbalanced: when the
+    // longest key range is more than twice a CU's fair share of all keys (the keys of
+    // every tile over num_cus).  Then the longest key ranges are cut into pieces of C
+    // keys (C a multiple of kChunkKeys; pieces start at absolute key positions that are
+    // multiples of C), the largest C that still gives `target` work items: one per CU
+    // when every tile is narrow (measured on decode batches of 16 to 256 sequences of
+    // 1024 to 8192 keys: one piece per CU beat two, and an unsplit batch of 128 x 1024
+    // keys beat every split of it), two per CU with wide tiles.
     const int32_t num_cus = p.num_cus > 0 ? p.num_cus : 256;
-    const int64_t target = 2LL * num_cus;
     int32_t max_keys = kChunkKeys;
-    for (auto& t : base) max_keys = std::max(max_keys, t.kv_end);
+    int64_t total_keys = 0;
+    bool any_wide = false;
+    for (auto& t : base) {
+        max_keys = std::max(max_keys, t.kv_end);
+        total_keys += t.kv_end;
+        any_wide = any_wide || t.kind == kWide;
+    }
+    for (auto& g : group) total_keys += g.t.kv_end;
+    const int64_t target = (any_wide ? 2LL : 1LL) * num_cus;
+    const bool balanced = 2 * total_keys >= int64_t(max_keys) * num_cus;
     const int32_t max_chunks = int32_t(ceil_div(max_keys, kChunkKeys));
     auto units = [&](int64_t chunk_keys) {
         int64_t u = int64_t(group.size());  // kGroup tiles: one work item each, never split
@@ -351,7 +365,7 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
         return u;
     };
     int64_t C = int64_t(max_chunks) * kChunkKeys;
-    if (p.max_kv_splits != 1 && int64_t(base.size() + group.size()) < target && max_chunks > 1) {
+    if (p.max_kv_splits != 1 && !balanced && int64_t(base.size() + group.size()) < target && max_chunks > 1) {
         if (units(kChunkKeys) < target) {
             C = kChunkKeys;
         } else {  // largest c in [1, max_chunks] with units(c * kChunkKeys) >= target

@@ -86,6 +86,8 @@ struct PlanParams {
     int32_t narrow_valu;    // 1: narrow tiles (<= kValuRows rows) run on the VALU kernel
     int32_t shared_pages;   // > 0: every sequence's first shared_pages page ids are the same
                             // pages; decode rows are grouped into kGroup tiles
+    int32_t tail_skip = 1;  // 0: causal query tiles walk every key up to kv_len, masking the
+                            // fully masked tail instead of skipping it (cost measurement)
 };
 
 struct Schedule {

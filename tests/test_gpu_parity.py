@@ -359,3 +359,24 @@ def test_out_of_range_page_reads_as_zero(head_dim, dtype, splits):
     assert e.value.status == "RPA_E_PAGE_OOB"
     plan.close()
     assert_close(o.double().cpu().numpy(), lse.double().cpu().numpy(), ro, rl, what="bad page as zeros")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_tail_skip_switch_changes_no_result(dtype, monkeypatch):
+    """With RPA_DISABLE_TAIL_SKIP=1 the wide tiles of causal prompts walk to kv_len and
+    mask the keys the skip would leave out (whole units masked for every row).  Masked
+    keys add exact zeros, so without splits (the same pieces either way) the output is
+    bitwise that of the skipping plan; with splits (other piece boundaries) it is held
+    to the oracle."""
+    b = W.make_batch("tailskip", [700, 300, 129, 1], [700, 450, 129, 600], num_qo_heads=8, num_kv_heads=1,
+                     head_dim=128, dtype=dtype, seed=41)
+    ro, rl = oracle.run(**b.oracle_kwargs())
+    dev = on_device(b)
+    o_on, l_on, _ = run(b, max_kv_splits=1, dev=dev, label="skip")
+    monkeypatch.setenv("RPA_DISABLE_TAIL_SKIP", "1")
+    o_off, l_off, _ = run(b, max_kv_splits=1, dev=dev, label="no skip")
+    assert np.array_equal(o_on, o_off) and np.array_equal(l_on, l_off)
+    o_sp, l_sp, info = run(b, num_cus=4096, dev=dev, label="no skip, split")
+    assert info["num_split_groups"] > 0
+    assert_close(o_sp, l_sp, ro, rl, what="no tail skip, split")
+    assert_close(o_off, l_off, ro, rl, what="no tail skip")

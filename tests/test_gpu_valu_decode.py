@@ -38,8 +38,11 @@ def test_valu_decode_b128_kv1024():
     b = W.decode_b128_kv1024()
     ro, rl = ref(b)
     o, l, info = run(b, narrow_kernel="valu")
-    assert info["num_split_groups"] == 128
+    assert info["num_split_groups"] == 0  # 128 equal rows: balanced, not split
     assert_close(o, l, ro, rl, what="valu decode_b128_kv1024")
+    o, l, info = run(b, narrow_kernel="valu", num_cus=1024)
+    assert info["num_split_groups"] == 128
+    assert_close(o, l, ro, rl, what="valu decode_b128_kv1024 split")
 
 
 def test_valu_mixed_batch_decode_rows():

@@ -225,11 +225,35 @@ def test_schedule_properties(case, max_kv_splits):
         assert (t[:, F["n_splits"]] <= 3).all()
 
 
-def test_decode_batch_is_split_to_fill_the_machine():
-    b = lengths_batch([1] * 128, [1024] * 128)
+@pytest.mark.parametrize("B,L,tiles,groups", [
+    (128, 1024, 128, 0),   # balanced: the longest range is twice the fair share -> no split
+    (256, 1024, 256, 0),
+    (256, 4096, 256, 0),
+    (127, 1024, 508, 127),  # just unbalanced: 256-key pieces, at least one per CU
+    (64, 1024, 256, 64),    # one piece per CU: 4 x 256 keys each
+    (64, 4096, 256, 64),    # 4 x 1024
+    (32, 8192, 256, 32),    # 8 x 1024
+    (16, 1024, 64, 16),     # 256-key pieces cannot make more
+])
+def test_decode_batch_split_rule(B, L, tiles, groups):
+    b = lengths_batch([1] * B, [L] * B)
     info = make_plan(b).info
-    assert info["num_tiles"] >= 512 and info["num_split_groups"] == 128
-    assert make_plan(b, max_kv_splits=1).info["num_tiles"] == 128
+    assert (info["num_tiles"], info["num_split_groups"]) == (tiles, groups)
+    check_schedule(b, make_plan(b))
+    assert make_plan(b, max_kv_splits=1).info["num_tiles"] == B
+
+
+def test_unbalanced_batches_are_split():
+    # one long decode row among short ones: its range is far above a CU's share
+    b = lengths_batch([1] * 200, [8192] + [64] * 199)
+    t = make_plan(b).tiles()
+    assert t[t[:, F["seq"]] == 0, F["n_splits"]].max() > 1
+    assert (t[t[:, F["seq"]] != 0, F["n_splits"]] == 1).all()
+    # a single 2048-token prompt (128 wide tiles, the last one walking every key): split
+    p = make_plan(lengths_batch([2048], [2048])).info
+    assert p["num_split_groups"] > 0
+    # the long prompts of a mixed batch are balanced by themselves: never split
+    assert make_plan(lengths_batch([8192] * 4, [8192] * 4, H=64, Hk=8)).info["num_split_groups"] == 0
 
 
 def test_schedule_depends_only_on_lengths():
@@ -329,8 +353,8 @@ def test_plan_update_keeps_the_launch_shape():
     assert np.array_equal(p.tiles(), fresh.tiles())
     check_schedule(b1, p)
     # lengths that need another launch shape are refused; the plan is left as it was
-    b2 = lengths_batch([1] * 128, [1024] * 128)
-    b3 = lengths_batch([1] * 128, [1100] * 128)  # 5 split pieces per sequence instead of 4
+    b2 = lengths_batch([1] * 64, [1024] * 64)
+    b3 = lengths_batch([1] * 64, [1100] * 64)  # 5 split pieces per sequence instead of 4
     p2 = make_plan(b2)
     before = p2.tiles().copy()
     with pytest.raises(rpa.RPAError) as e:

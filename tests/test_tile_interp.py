@@ -1,0 +1,211 @@
+"""The planner's schedules, executed in binary64 on the CPU (tests/tile_interp.py),
+against the oracle.
+
+Each case plans a batch with the C-ABI planner (host-only, no GPU), runs every
+work item the plan lists over the batch's own inputs, merges the split pieces,
+and requires the oracle's O and LSE to within 1e-12 (summation order is the
+only difference).  This checks, over whole schedules, that every (row, head)
+sees exactly its visible keys once: no piece dropped or repeated, no key range
+cut short, no mask or page base wrong, the kGroup members' private keys all
+walked.  The last tests plant mistakes in a schedule and require the executor
+to notice them.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_attention_ragged_amd as rpa
+import workloads as W
+
+from tests.tile_interp import execute, ScheduleError, KIND, KGROUP, N_SPLITS, KV_END, KV_BEGIN, KV_LEN, Q_COUNT, PART
+
+TOL = 1e-12
+
+
+def plan_for(b, **kw):
+    return rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=b.num_qo_heads,
+                    num_kv_heads=b.num_kv_heads, head_dim=b.head_dim, dtype=b.dtype, causal=b.causal, **kw)
+
+
+def assert_schedule_matches_oracle(b, plan):
+    recs = plan.tiles()
+    O, LSE = execute(b, recs)
+    Oo, Lo = oracle.run(**b.oracle_kwargs())
+    assert np.all(np.isfinite(O)) and np.all(np.isfinite(LSE))
+    eo = np.abs(O - Oo) / (1 + np.abs(Oo))
+    el = np.abs(LSE - Lo) / (1 + np.abs(Lo))
+    assert eo.max() <= TOL, eo.max()
+    assert el.max() <= TOL, el.max()
+    return recs
+
+
+def test_tiny_ragged_prefill_schedules():
+    b = W.tiny_ragged_prefill(poison=True, spare_pages=5)
+    for kw in ({}, {"num_cus": 4096}, {"narrow_kernel": "valu"}):
+        assert_schedule_matches_oracle(b, plan_for(b, **kw))
+
+
+def test_decode_batch_split_and_valu():
+    b = W.make_batch("decode", [1] * 12, [1024, 17, 300, 1, 999, 512, 513, 64, 2000, 31, 257, 700],
+                     num_qo_heads=8, num_kv_heads=1, head_dim=128, dtype="f16", seed=11, poison=True, spare_pages=3)
+    r = assert_schedule_matches_oracle(b, plan_for(b))
+    assert (r[:, N_SPLITS] > 1).any()
+    assert_schedule_matches_oracle(b, plan_for(b, narrow_kernel="valu"))
+    assert_schedule_matches_oracle(b, plan_for(b, max_kv_splits=1))
+
+
+def test_short_prompt_batch():
+    b = W.make_batch("short", W.short_prompt_lengths(24, hi=200, seed=5), W.short_prompt_lengths(24, hi=200, seed=5),
+                     num_qo_heads=16, num_kv_heads=4, head_dim=64, dtype="bf16", seed=12, poison=True)
+    assert_schedule_matches_oracle(b, plan_for(b))
+    assert_schedule_matches_oracle(b, plan_for(b, num_cus=2048))
+
+
+def test_mixed_prompts_and_decode_rows_one_launch():
+    q = [700, 1] + [1] * 20 + [333]
+    kv = [700, 1500] + [40 + 37 * i for i in range(20)] + [333]
+    b = W.make_batch("mixed", q, kv, num_qo_heads=8, num_kv_heads=1, head_dim=128, dtype="bf16", seed=13)
+    for cus in (0, 8):
+        p = plan_for(b, num_cus=cus)
+        r = assert_schedule_matches_oracle(b, p)
+    kinds = set(r[r[:, Q_COUNT] > 0, KIND].tolist())
+    assert kinds <= {0, 1}
+
+
+def test_suffix_rows_after_a_cached_prefix():
+    # q_len < kv_len prefill (a suffix after cached tokens), several tiles per sequence
+    b = W.make_batch("suffix", [30, 200, 5, 129], [230, 260, 500, 129], num_qo_heads=4, num_kv_heads=2,
+                     head_dim=128, dtype="f16", seed=14, poison=True, spare_pages=2)
+    for kw in ({}, {"num_cus": 4096}, {"narrow_kernel": "valu"}):
+        assert_schedule_matches_oracle(b, plan_for(b, **kw))
+
+
+def test_non_causal_queries_outnumbering_keys():
+    b = W.make_batch("cascade_prefix", [40, 3, 300], [25, 200, 16], num_qo_heads=8, num_kv_heads=2,
+                     head_dim=64, dtype="f16", seed=15, causal=False)
+    assert_schedule_matches_oracle(b, plan_for(b))
+    assert_schedule_matches_oracle(b, plan_for(b, num_cus=4096))
+
+
+@pytest.mark.parametrize("G,Hk,D", [(1, 2, 64), (4, 1, 128), (16, 1, 64), (2, 3, 128)])
+def test_random_ragged_batches(G, Hk, D):
+    rng = np.random.default_rng(100 * G + Hk + D)
+    for trial in range(3):
+        B = int(rng.integers(1, 9))
+        kv = rng.integers(1, 600, B)
+        q = np.array([int(rng.integers(1, k + 1)) if rng.random() < 0.6 else 1 for k in kv])
+        b = W.make_batch("rand", q.tolist(), kv.tolist(), num_qo_heads=G * Hk, num_kv_heads=Hk, head_dim=D,
+                         dtype=("f16", "bf16")[trial % 2], seed=int(rng.integers(1 << 30)), poison=True,
+                         spare_pages=int(rng.integers(0, 4)))
+        for kw in ({}, {"num_cus": int(rng.choice([1, 4, 4096]))}, {"max_kv_splits": 2, "num_cus": 4096}):
+            assert_schedule_matches_oracle(b, plan_for(b, **kw))
+
+
+def _shared_decode(n_req=12, G=8, Hk=2, D=64):
+    base = W.shared_prefix_suffix(n_req=n_req, prefix=200, suffix=30, decode_steps=70, num_qo_heads=G * Hk,
+                                  num_kv_heads=Hk, head_dim=D, dtype="f16")
+    return base
+
+
+def test_grouped_decode_over_a_shared_prefix():
+    base = _shared_decode()
+    for step in (1, 40):
+        d = W.decode_step(base, step)
+        p = plan_for(d, shared_pages=12)
+        r = assert_schedule_matches_oracle(d, p)
+        assert (r[:, KIND] == KGROUP).any()
+
+
+def test_grouped_members_of_different_lengths():
+    # members' own keys differ: trim some sequences so the group pads its private steps
+    base = _shared_decode(n_req=10, G=4, Hk=1, D=128)
+    d = W.decode_step(base, 50)
+    lens = d.kv_lens.copy()
+    lens[1::3] -= 37
+    lens[2::4] -= 5
+    q_lens = [1] * d.batch
+    qo, kp, ki, last = [0], [0], [], []
+    for s in range(d.batch):
+        n = W.pages_for(lens[s])
+        ki.extend(d.kv_page_indices[d.kv_page_indptr[s]:d.kv_page_indptr[s] + n])
+        kp.append(kp[-1] + n)
+        qo.append(qo[-1] + q_lens[s])
+        last.append(W.last_page_len_for(lens[s]))
+    t = W.Batch("trimmed", np.array(qo, np.int32), np.array(kp, np.int32), np.array(ki, np.int32),
+                np.array(last, np.int32), d.q, d.kv_cache, d.num_qo_heads, d.num_kv_heads, d.head_dim, d.dtype)
+    r = assert_schedule_matches_oracle(t, plan_for(t, shared_pages=12))
+    assert (r[:, KIND] == KGROUP).any()
+
+
+def test_tail_skip_switch(monkeypatch):
+    b = W.make_batch("prompts", [400, 129, 77], [400, 300, 77], num_qo_heads=8, num_kv_heads=1, head_dim=128,
+                     dtype="bf16", seed=16, poison=True)
+    on = plan_for(b, max_kv_splits=1).tiles()
+    monkeypatch.setenv("RPA_DISABLE_TAIL_SKIP", "1")
+    p_off = plan_for(b, max_kv_splits=1)
+    off = assert_schedule_matches_oracle(b, p_off)
+    assert_schedule_matches_oracle(b, plan_for(b))
+    real_on, real_off = on[on[:, Q_COUNT] > 0], off[off[:, Q_COUNT] > 0]
+    # without the skip every tile walks to kv_len; with it, the earlier tiles of a prompt stop sooner
+    assert (real_off[:, KV_END] == real_off[:, KV_LEN]).all()
+    assert (real_on[:, KV_END] - real_on[:, KV_BEGIN]).sum() < (real_off[:, KV_END] - real_off[:, KV_BEGIN]).sum()
+    assert_schedule_matches_oracle(b, plan_for(b, num_cus=4096))
+    # update keeps the setting of the plan it updates, whatever the environment says now
+    monkeypatch.delenv("RPA_DISABLE_TAIL_SKIP")
+    p_off.update(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len)
+    assert (p_off.tiles() == off).all()
+
+
+def test_plan_log_line(capfd, monkeypatch):
+    b = W.tiny_ragged_prefill()
+    plan_for(b)
+    assert "rpa:" not in capfd.readouterr().err
+    monkeypatch.setenv("RPA_LOG", "1")
+    p = plan_for(b, num_cus=4096)
+    err = capfd.readouterr().err
+    assert err.startswith("rpa: create batch=4 total_q=26 tiles=%d " % p.info["num_tiles"])
+    assert "split_groups=%d " % p.info["num_split_groups"] in err
+    assert "workspace=%d B" % p.info["workspace_bytes"] in err
+    p.update(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len)
+    assert capfd.readouterr().err.startswith("rpa: update batch=4")
+
+
+# ---- the executor notices a broken schedule ---------------------------------------------
+
+def _broken(recs, how):
+    r = recs.copy()
+    real = np.nonzero(r[:, Q_COUNT] > 0)[0]
+    if how == "drop_piece":
+        i = real[np.nonzero(r[real, N_SPLITS] > 1)[0][1]]
+        return np.delete(r, i, axis=0)
+    if how == "repeat_tile":
+        return np.concatenate([r, r[real[:1]]])
+    if how == "short_range":
+        i = real[np.argmax(r[real, KV_END] - r[real, KV_BEGIN])]
+        r[i, KV_END] -= 16
+        return r
+    if how == "shifted_range":
+        i = real[np.argmax(r[real, KV_END] - r[real, KV_BEGIN])]
+        r[i, KV_BEGIN] += 1
+        r[i, KV_END] += 1
+        return r
+    if how == "part_overlap":
+        sp = real[r[real, N_SPLITS] > 1]
+        r[sp[-1], PART] = r[sp[0], PART]
+        return r
+    raise ValueError(how)
+
+
+@pytest.mark.parametrize("how", ["drop_piece", "repeat_tile", "short_range", "shifted_range", "part_overlap"])
+def test_executor_rejects_broken_schedules(how):
+    b = W.make_batch("dec", [1, 1, 3, 40], [900, 700, 600, 800], num_qo_heads=8, num_kv_heads=1, head_dim=64,
+                     dtype="f16", seed=17)
+    recs = plan_for(b, num_cus=4096).tiles()
+    assert (recs[:, N_SPLITS] > 1).sum() >= 4
+    Oo, Lo = oracle.run(**b.oracle_kwargs())
+    try:
+        O, L = execute(b, _broken(recs, how))
+    except (ScheduleError, IndexError):
+        return
+    err = max(np.nanmax(np.abs(O - Oo)), np.nanmax(np.abs(L - Lo)))
+    assert err > 1e-6 or np.isnan(O).any()

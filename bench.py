@@ -20,7 +20,8 @@ on the box (floors.hbm_stream_gbs).  traffic = HBM bytes per launch from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/, while it was taken on
 the current kernel source.
 floors = measured on the box in this run: an empty launch, a plain HBM read
-stream, the decode kernel's paged gather alone (same grid, no arithmetic), and
+stream, the decode kernel's paged gather alone (its page table, no arithmetic;
+on the headline plan's grid of 128 workgroups and on a split grid of 512), and
 dense bf16 MFMA throughput.
 prefill = the long prompts of the mixed workload (4 causal prompts x 8192, 64 qo /
 8 kv heads, bf16) against the 2.5 PFLOP/s dense bf16 MFMA peak.
@@ -245,16 +246,17 @@ def measure(b, steps, warmup=3, rotate=1, unique_kv_tokens=None, floors=None, **
 # ----------------------------------------------------------------------------------------------
 
 def bench_floors(steps=20):
-    """Empty launch, plain HBM read, the decode batch's paged gather alone (same grid
-    and page table as the decode kernel: 128 sequences x 4 pieces of 256 keys), and
-    dense bf16 MFMA throughput."""
+    """Empty launch, plain HBM read, the decode batch's paged gather alone with the
+    page table of the decode kernel on two grids (the headline plan's 128 workgroups
+    of 1024 keys, and a split grid of 128 x 4 pieces of 256 keys), and dense bf16
+    MFMA throughput."""
     import torch
     import workloads as W
     lib = ctypes.CDLL(FLOORS_LIB)
     P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     lib.rpa_floor_empty.argtypes = [i32, P]
     lib.rpa_floor_stream.argtypes = [P, i64, P, i32, P]
-    lib.rpa_floor_gather.argtypes = [P, P, i32, i32, i32, i32, P, P]
+    lib.rpa_floor_gather.argtypes = [P, P, i32, i32, i32, i32, i32, P, P]
     lib.rpa_floor_mfma.argtypes = [P, i32, i32, P]
 
     def ok(rc):
@@ -284,11 +286,17 @@ def bench_floors(steps=20):
     gsink = torch.empty(512 * 256, dtype=torch.int32, device="cuda")
     it = iter(range(1 << 40))
     gb = 128 * 1024 * 128 * 2 * 2.0
-    t = per_call_ms(lambda: ok(lib.rpa_floor_gather(kvs[next(it) % 8].data_ptr(), idx.data_ptr(), 128, 64, 4, 1,
+    # split grid: 512 workgroups of 256 keys (every CU busy)
+    t = per_call_ms(lambda: ok(lib.rpa_floor_gather(kvs[next(it) % 8].data_ptr(), idx.data_ptr(), 128, 64, 4, 1, 1,
                                                     gsink.data_ptr(), st())), steps * 5, 5)
     out["decode_gather_us"] = t["mean_ms"] * 1e3
     out["decode_gather_per_call_us"] = t["median_ms"] * 1e3
     out["decode_gather_gbs"] = gb / (t["mean_ms"] * 1e-3) / 1e9
+    # the headline plan's grid: 128 workgroups, one per sequence, each 4 runs of 256 keys
+    t = per_call_ms(lambda: ok(lib.rpa_floor_gather(kvs[next(it) % 8].data_ptr(), idx.data_ptr(), 128, 64, 1, 4, 1,
+                                                    gsink.data_ptr(), st())), steps * 5, 5)
+    out["decode_gather_unsplit_us"] = t["mean_ms"] * 1e3
+    out["decode_gather_unsplit_gbs"] = gb / (t["mean_ms"] * 1e-3) / 1e9
     del kvs, b
     # dense MFMA: 1024 workgroups x 4 waves x 4 chains x iters 32x32x16 bf16 products
     msink = torch.empty(1024 * 256, dtype=torch.float32, device="cuda")

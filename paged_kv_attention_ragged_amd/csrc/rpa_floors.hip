@@ -32,32 +32,34 @@ __global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ s
 }
 
 // The decode kernel's memory traffic without its arithmetic: workgroup w reads the K
-// and V rows of kv head 0 for the 256 keys [256 piece, 256 piece + 256) of sequence
-// seq (w = seq * pieces + piece) through the page table, with non-temporal 16-byte
-// loads; cache layout [page][2][16][kv_heads][128] of 16-bit values.  The piece's 16
-// page ids are wave-uniform (scalar loads); lane t then reads slot t / 16, chunk t % 16
-// of every page, all 32 loads in flight at once.
+// and V rows of kv head 0 for `chunks` consecutive runs of 256 keys of sequence seq,
+// starting at key 256 chunks piece (w = seq * pieces + piece), through the page table,
+// with non-temporal 16-byte loads; cache layout [page][2][16][kv_heads][128] of 16-bit
+// values.  A run's 16 page ids are wave-uniform (scalar loads); lane t then reads slot
+// t / 16, chunk t % 16 of every page, all 32 loads of a run in flight at once.
 __global__ __launch_bounds__(256) void gather_kernel(const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-                                                     int32_t pages_per_seq, int32_t pieces, int32_t kv_heads,
-                                                     uint32_t* out) {
+                                                     int32_t pages_per_seq, int32_t pieces, int32_t chunks,
+                                                     int32_t kv_heads, uint32_t* out) {
     typedef __attribute__((address_space(4))) const int32_t const_i32;
     const int w = blockIdx.x, seq = w / pieces, piece = w - seq * pieces;
     const int slot = threadIdx.x >> 4, ch = threadIdx.x & 15;
-    const int64_t pbase = int64_t(seq) * pages_per_seq + piece * 16;
     const int64_t ss = int64_t(kv_heads) * 128;  // elements between token slots
-    int pg[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pg[i] = ((const_i32*)idx)[pbase + i];
-    u32x4 v[32];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint16_t* b = kv + (int64_t(pg[i]) * 32 + slot) * ss + 8 * ch;
-        v[2 * i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b));
-        v[2 * i + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + 16 * ss));
-    }
     uint32_t acc = 0;
+    for (int c = 0; c < chunks; ++c) {
+        const int64_t pbase = int64_t(seq) * pages_per_seq + (int64_t(piece) * chunks + c) * 16;
+        int pg[16];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+        for (int i = 0; i < 16; ++i) pg[i] = ((const_i32*)idx)[pbase + i];
+        u32x4 v[32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint16_t* b = kv + (int64_t(pg[i]) * 32 + slot) * ss + 8 * ch;
+            v[2 * i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b));
+            v[2 * i + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b + 16 * ss));
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc ^= v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+    }
     out[int64_t(w) * 256 + threadIdx.x] = acc;
 }
 
@@ -106,16 +108,17 @@ int rpa_floor_stream(const void* src, int64_t bytes, uint32_t* out, int32_t grid
     return int(hipGetLastError());
 }
 
-// The decode gather: batch * pieces workgroups, each reading 256 keys (K and V, kv
-// head 0, head_dim 128) of its sequence; page table idx [batch][pages_per_seq], every
-// index a valid page of kv; 16 * pieces <= pages_per_seq.  out holds
+// The decode gather: batch * pieces workgroups, each reading chunks x 256 keys (K and
+// V, kv head 0, head_dim 128) of its sequence; page table idx [batch][pages_per_seq],
+// every index a valid page of kv; 16 * pieces * chunks <= pages_per_seq.  out holds
 // batch * pieces * 256 words.
 int rpa_floor_gather(const void* kv, const int32_t* idx, int32_t batch, int32_t pages_per_seq, int32_t pieces,
-                     int32_t kv_heads, uint32_t* out, void* stream) {
-    if (!kv || !idx || !out || batch < 1 || pieces < 1 || kv_heads < 1 || 16 * pieces > pages_per_seq)
+                     int32_t chunks, int32_t kv_heads, uint32_t* out, void* stream) {
+    if (!kv || !idx || !out || batch < 1 || pieces < 1 || chunks < 1 || kv_heads < 1 ||
+        int64_t(16) * pieces * chunks > pages_per_seq)
         return int(hipErrorInvalidValue);
     hipLaunchKernelGGL(gather_kernel, dim3(batch * pieces), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       static_cast<const uint16_t*>(kv), idx, pages_per_seq, pieces, kv_heads, out);
+                       static_cast<const uint16_t*>(kv), idx, pages_per_seq, pieces, chunks, kv_heads, out);
     return int(hipGetLastError());
 }
 

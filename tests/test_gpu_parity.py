@@ -255,6 +255,30 @@ def test_mixed_long_batch_sampled():
     assert_close(o, l, ro, rl, rows=rows, what="mixed long (sampled)")
 
 
+def test_long_prompts_alone_and_in_the_mixed_batch():
+    """The mixed batch's 4 x 8192 prompts planned alone (the wide kernel by itself, as
+    the benchmark's prefill leg runs them) against the oracle on sampled rows, and
+    bitwise against the same rows of the whole batch's one mixed launch: a prompt's
+    rows do not depend on what else the batch holds."""
+    say("generate mixed_long_batch on cuda")
+    b = W.mixed_long_batch(device="cuda")
+    idx = torch.from_numpy(b.kv_page_indices).cuda()
+    n = 4
+    T = int(b.qo_indptr[n])
+    sub = W.Batch("mixed_long_prompts_of_all", b.qo_indptr[:n + 1].copy(), b.kv_page_indptr[:n + 1].copy(),
+                  b.kv_page_indices[:int(b.kv_page_indptr[n])].copy(), b.kv_last_page_len[:n].copy(),
+                  b.q[:T], b.kv_cache, b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype)
+    o_all, l_all, info_all = run(b, dev=(b.q, b.kv_cache, idx), label="whole batch")
+    o, l, info = run(sub, dev=(sub.q, sub.kv_cache, idx[:len(sub.kv_page_indices)]), label="prompts alone")
+    assert info["num_split_groups"] == 0 and info_all["num_split_groups"] == 0
+    assert np.array_equal(o, o_all[:T]) and np.array_equal(l, l_all[:T])
+    rows = sorted(set(r for s in range(n) for r in list(range(int(sub.qo_indptr[s]), int(sub.qo_indptr[s + 1]), 509))
+                      + list(range(int(sub.qo_indptr[s + 1]) - 16, int(sub.qo_indptr[s + 1])))))
+    say("oracle on %d sampled prompt rows" % len(rows))
+    ro, rl = ref(sub, rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="long prompts alone (sampled)")
+
+
 # ----------------------------------------------------------------------------------------------
 # Bitwise invariances and error handling.
 # ----------------------------------------------------------------------------------------------

@@ -279,6 +279,30 @@ def test_long_prompts_alone_and_in_the_mixed_batch():
     assert_close(o, l, ro, rl, rows=rows, what="long prompts alone (sampled)")
 
 
+def test_mixed_decode_rows_alone_and_in_the_mixed_batch():
+    """The mixed batch's 256 decode rows (kv_len U[512, 8192]) planned alone (the narrow
+    kernel by itself, as the benchmark's decode-rows leg runs them) against the oracle
+    on sampled rows, and bitwise against the same rows of the whole batch's mixed
+    launch, where the same tiles run beside the prompts' wide tiles."""
+    say("generate mixed_long_batch on cuda")
+    b = W.mixed_long_batch(device="cuda")
+    idx = torch.from_numpy(b.kv_page_indices).cuda()
+    n = 4
+    T0, p0 = int(b.qo_indptr[n]), int(b.kv_page_indptr[n])
+    sub = W.Batch("mixed_long_decode_of_all", (b.qo_indptr[n:] - T0).astype(np.int32),
+                  (b.kv_page_indptr[n:] - p0).astype(np.int32), b.kv_page_indices[p0:].copy(),
+                  b.kv_last_page_len[n:].copy(), b.q[T0:], b.kv_cache, b.num_qo_heads, b.num_kv_heads,
+                  b.head_dim, b.dtype)
+    o_all, l_all, _ = run(b, dev=(b.q, b.kv_cache, idx), label="whole batch")
+    o, l, info = run(sub, dev=(sub.q, sub.kv_cache, idx[p0:]), label="decode rows alone")
+    assert info["num_split_groups"] == 0
+    assert np.array_equal(o, o_all[T0:]) and np.array_equal(l, l_all[T0:])
+    rows = list(range(0, sub.total_q, 5))
+    say("oracle on %d sampled decode rows" % len(rows))
+    ro, rl = ref(sub, rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="mixed decode rows alone (sampled)")
+
+
 # ----------------------------------------------------------------------------------------------
 # Bitwise invariances and error handling.
 # ----------------------------------------------------------------------------------------------

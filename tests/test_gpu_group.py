@@ -67,6 +67,24 @@ def test_shared_prefix_decode_steps_grouped():
             assert_close(o, l, ro, rl, what="grouped decode step %d" % step)
 
 
+def test_long_shared_prefix_decode_step_grouped():
+    """One decode step of 256 requests over a 4096-token shared prefix (256 shared
+    pages; the benchmark's long-prefix leg): grouped tiles against the oracle on
+    sampled rows, and within tolerance of the direct plan on every row."""
+    base = W.shared_prefix_suffix(prefix=4096, decode_steps=1)
+    d = W.decode_step(base, 1)
+    n_sh = len(base.extra["shared"])
+    assert n_sh == 256
+    dev = on_device(d)
+    o, l, kinds = run_grouped(d, n_sh, dev=dev, kv_shared=True)
+    assert (kinds == 2).all()
+    o_direct, l_direct, _ = run(d, dev=dev, label="long prefix direct", kv_shared=True)
+    assert_close(o, l, o_direct, l_direct, what="long prefix grouped vs direct")
+    rows = list(range(0, d.total_q, 7))
+    ro, rl = oracle.run(**d.oracle_kwargs(), rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="long prefix grouped (sampled)")
+
+
 @pytest.mark.parametrize("shape", [(32, 8, 128, "bf16", 12), (16, 2, 128, "f16", 5), (8, 4, 64, "bf16", 3),
                                    (8, 1, 64, "f16", 7)], ids=lambda s: "h%d_kv%d_d%d_%s_p%d" % s)
 def test_grouped_rows_beside_ordinary_tiles(shape):

@@ -303,6 +303,28 @@ def test_mixed_decode_rows_alone_and_in_the_mixed_batch():
     assert_close(o, l, ro, rl, rows=rows, what="mixed decode rows alone (sampled)")
 
 
+@pytest.mark.parametrize("B", [1, 8, 64, 256])
+def test_batch_size_sweep_shapes(B):
+    """The batch-size sweep's batches (B causal prompts of 8192 / B tokens, 32 qo / 8 kv
+    heads, bf16): the ragged call against the oracle on sampled rows, and its first
+    prompt's rows bitwise equal to that prompt's own call (the sweep's one-call-each
+    timing)."""
+    L = 8192 // B
+    b = W.make_batch("sweep_B%d" % B, [L] * B, [L] * B, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                     dtype="bf16", seed=4000 + B, device="cuda")
+    idx = torch.from_numpy(b.kv_page_indices).cuda()
+    o, l, _ = run(b, dev=(b.q, b.kv_cache, idx), label="batched")
+    one = W.Batch("one", np.array([0, L], np.int32), np.array([0, b.kv_page_indptr[1]], np.int32),
+                  b.kv_page_indices[:b.kv_page_indptr[1]].copy(), b.kv_last_page_len[:1].copy(), b.q[:L],
+                  b.kv_cache, b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype)
+    o1, l1, _ = run(one, dev=(one.q, one.kv_cache, idx[:len(one.kv_page_indices)]), label="first prompt alone")
+    assert np.array_equal(o1, o[:L]) and np.array_equal(l1, l[:L])
+    step = max(1, b.total_q // 48)
+    rows = sorted(set(list(range(0, b.total_q, step)) + [L - 1, b.total_q - 1]))
+    ro, rl = ref(b, rows=rows)
+    assert_close(o, l, ro, rl, rows=rows, what="sweep B=%d (sampled)" % B)
+
+
 # ----------------------------------------------------------------------------------------------
 # Bitwise invariances and error handling.
 # ----------------------------------------------------------------------------------------------

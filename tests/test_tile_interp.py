@@ -137,6 +137,50 @@ def test_grouped_members_of_different_lengths():
     assert (r[:, KIND] == KGROUP).any()
 
 
+def _share_prefix(b, pages):
+    """The first `pages` page ids of every sequence with that many pages point at the
+    first sequence's pages (a prefix stored once; layout only)."""
+    idx = b.kv_page_indices.copy()
+    first = idx[:pages].copy()
+    for s in range(b.batch):
+        a = int(b.kv_page_indptr[s])
+        if int(b.kv_page_indptr[s + 1]) - a >= pages:
+            idx[a:a + pages] = first
+    return W.Batch(b.name + "_shared", b.qo_indptr, b.kv_page_indptr, idx, b.kv_last_page_len, b.q, b.kv_cache,
+                   b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype, b.causal)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_grouped_batches(seed):
+    """Random mixes over a declared shared prefix of P pages: decode rows that see the
+    whole prefix (grouped), decode rows shorter than it, prefill rows and suffixes,
+    G from 1 to 8; each plan with and without forced splits."""
+    rng = np.random.default_rng(500 + seed)
+    P = int(rng.integers(1, 7))
+    Ks = 16 * P
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hk = int(rng.choice([1, 2]))
+    B = int(rng.integers(4, 40))
+    q, kv = [1], [Ks + int(rng.integers(0, 80))]
+    for _ in range(B - 1):
+        r = rng.random()
+        if r < 0.6:
+            q.append(1)
+            kv.append(Ks + int(rng.integers(0, 150)))
+        elif r < 0.75:
+            q.append(1)
+            kv.append(int(rng.integers(1, Ks + 1)))
+        else:
+            k = int(rng.integers(1, Ks + 200))
+            q.append(int(rng.integers(1, k + 1)))
+            kv.append(k)
+    b = _share_prefix(W.make_batch("grp_rand", q, kv, num_qo_heads=G * Hk, num_kv_heads=Hk,
+                                   head_dim=int(rng.choice([64, 128])), dtype=("f16", "bf16")[seed % 2],
+                                   seed=600 + seed, poison=True, spare_pages=2), P)
+    for kw in ({}, {"num_cus": 4096}):
+        assert_schedule_matches_oracle(b, plan_for(b, shared_pages=P, **kw))
+
+
 def test_tail_skip_switch(monkeypatch):
     b = W.make_batch("prompts", [400, 129, 77], [400, 300, 77], num_qo_heads=8, num_kv_heads=1, head_dim=128,
                      dtype="bf16", seed=16, poison=True)

@@ -67,6 +67,19 @@ def test_shared_prefix_decode_steps_grouped():
             assert_close(o, l, ro, rl, what="grouped decode step %d" % step)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_grouped_batches_on_the_gpu(seed):
+    """The CPU schedule executor's random shared-prefix mixes, run by the kernels: as
+    planned and with forced splits, against the oracle on every row."""
+    from tests.test_tile_interp import random_grouped_batch
+    b, P = random_grouped_batch(seed)
+    ro, rl = oracle.run(**b.oracle_kwargs())
+    dev = on_device(b)
+    for kw in ({}, {"num_cus": 4096}):
+        o, l, kinds = run_grouped(b, P, dev=dev, **kw)
+        assert_close(o, l, ro, rl, what="random grouped seed %d %s" % (seed, kw))
+
+
 def test_long_shared_prefix_decode_step_grouped():
     """One decode step of 256 requests over a 4096-token shared prefix (256 shared
     pages; the benchmark's long-prefix leg): grouped tiles against the oracle on

@@ -150,11 +150,10 @@ def _share_prefix(b, pages):
                    b.num_qo_heads, b.num_kv_heads, b.head_dim, b.dtype, b.causal)
 
 
-@pytest.mark.parametrize("seed", range(6))
-def test_random_grouped_batches(seed):
-    """Random mixes over a declared shared prefix of P pages: decode rows that see the
-    whole prefix (grouped), decode rows shorter than it, prefill rows and suffixes,
-    G from 1 to 8; each plan with and without forced splits."""
+def random_grouped_batch(seed):
+    """(batch, P): a random mix over a declared shared prefix of P pages -- decode rows
+    that see the whole prefix, decode rows shorter than it, prefill rows and suffixes;
+    G from 1 to 8, poisoned unowned slots.  Also used by the GPU tests."""
     rng = np.random.default_rng(500 + seed)
     P = int(rng.integers(1, 7))
     Ks = 16 * P
@@ -174,9 +173,16 @@ def test_random_grouped_batches(seed):
             k = int(rng.integers(1, Ks + 200))
             q.append(int(rng.integers(1, k + 1)))
             kv.append(k)
-    b = _share_prefix(W.make_batch("grp_rand", q, kv, num_qo_heads=G * Hk, num_kv_heads=Hk,
+    b = _share_prefix(W.make_batch("grp_rand%d" % seed, q, kv, num_qo_heads=G * Hk, num_kv_heads=Hk,
                                    head_dim=int(rng.choice([64, 128])), dtype=("f16", "bf16")[seed % 2],
                                    seed=600 + seed, poison=True, spare_pages=2), P)
+    return b, P
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_grouped_batches(seed):
+    """random_grouped_batch plans, with and without forced splits, executed on the CPU."""
+    b, P = random_grouped_batch(seed)
     for kw in ({}, {"num_cus": 4096}):
         assert_schedule_matches_oracle(b, plan_for(b, shared_pages=P, **kw))
 

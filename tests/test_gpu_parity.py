@@ -303,6 +303,21 @@ def test_mixed_decode_rows_alone_and_in_the_mixed_batch():
     assert_close(o, l, ro, rl, rows=rows, what="mixed decode rows alone (sampled)")
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 64), (4, 1, 128), (16, 1, 64), (2, 3, 128)],
+                         ids=lambda s: "g%d_hk%d_d%d" % s)
+def test_random_ragged_batches_on_the_gpu(shape):
+    """The CPU schedule executor's random ragged batches, run by the kernels with the
+    same plans (as made, another machine size, forced splits) against the oracle on
+    every row; unowned slots hold NaN."""
+    from tests.test_tile_interp import random_ragged_batches
+    for b, kws in random_ragged_batches(*shape):
+        ro, rl = ref(b)
+        dev = on_device(b)
+        for kw in kws:
+            o, l, _ = run(b, dev=dev, label=str(kw), **kw)
+            assert_close(o, l, ro, rl, what="%s %s" % (b.name, kw))
+
+
 @pytest.mark.parametrize("B", [1, 8, 64, 256])
 def test_batch_size_sweep_shapes(B):
     """The batch-size sweep's batches (B causal prompts of 8192 / B tokens, 32 qo / 8 kv

@@ -87,17 +87,31 @@ def test_non_causal_queries_outnumbering_keys():
     assert_schedule_matches_oracle(b, plan_for(b, num_cus=4096))
 
 
-@pytest.mark.parametrize("G,Hk,D", [(1, 2, 64), (4, 1, 128), (16, 1, 64), (2, 3, 128)])
-def test_random_ragged_batches(G, Hk, D):
+RAGGED_SHAPES = [(1, 2, 64), (4, 1, 128), (16, 1, 64), (2, 3, 128)]
+
+
+def random_ragged_batches(G, Hk, D):
+    """[(batch, [plan kwargs ...]), ...]: three random ragged batches (prefill rows,
+    suffixes, decode rows; poisoned unowned slots) with a plan as made, one for a
+    random machine size and one with forced splits of at most 2.  Also used by the
+    GPU tests."""
     rng = np.random.default_rng(100 * G + Hk + D)
+    out = []
     for trial in range(3):
         B = int(rng.integers(1, 9))
         kv = rng.integers(1, 600, B)
         q = np.array([int(rng.integers(1, k + 1)) if rng.random() < 0.6 else 1 for k in kv])
-        b = W.make_batch("rand", q.tolist(), kv.tolist(), num_qo_heads=G * Hk, num_kv_heads=Hk, head_dim=D,
-                         dtype=("f16", "bf16")[trial % 2], seed=int(rng.integers(1 << 30)), poison=True,
-                         spare_pages=int(rng.integers(0, 4)))
-        for kw in ({}, {"num_cus": int(rng.choice([1, 4, 4096]))}, {"max_kv_splits": 2, "num_cus": 4096}):
+        b = W.make_batch("rand_g%d_hk%d_d%d_%d" % (G, Hk, D, trial), q.tolist(), kv.tolist(), num_qo_heads=G * Hk,
+                         num_kv_heads=Hk, head_dim=D, dtype=("f16", "bf16")[trial % 2],
+                         seed=int(rng.integers(1 << 30)), poison=True, spare_pages=int(rng.integers(0, 4)))
+        out.append((b, [{}, {"num_cus": int(rng.choice([1, 4, 4096]))}, {"max_kv_splits": 2, "num_cus": 4096}]))
+    return out
+
+
+@pytest.mark.parametrize("G,Hk,D", RAGGED_SHAPES)
+def test_random_ragged_batches(G, Hk, D):
+    for b, kws in random_ragged_batches(G, Hk, D):
+        for kw in kws:
             assert_schedule_matches_oracle(b, plan_for(b, **kw))
 
 

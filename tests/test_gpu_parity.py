@@ -318,6 +318,21 @@ def test_random_ragged_batches_on_the_gpu(shape):
             assert_close(o, l, ro, rl, what="%s %s" % (b.name, kw))
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations_on_the_gpu(seed):
+    """The CPU schedule executor's random configurations (G 1..16, 1..8 kv heads, D 64 /
+    128, fp16 / bf16, causal or not, sequences without queries, NaN in unowned slots),
+    run by the kernels on the MFMA and VALU narrow paths, cacheable or streamed, as
+    planned or split, against the oracle on every row."""
+    from tests.test_tile_interp import random_config_batch
+    b, kws = random_config_batch(seed)
+    ro, rl = ref(b)
+    dev = on_device(b)
+    for kw in kws:
+        o, l, _ = run(b, dev=dev, label=str(kw), **kw)
+        assert_close(o, l, ro, rl, what="%s %s" % (b.name, kw))
+
+
 @pytest.mark.parametrize("B", [1, 8, 64, 256])
 def test_batch_size_sweep_shapes(B):
     """The batch-size sweep's batches (B causal prompts of 8192 / B tokens, 32 qo / 8 kv

@@ -151,6 +151,48 @@ def test_grouped_members_of_different_lengths():
     assert (r[:, KIND] == KGROUP).any()
 
 
+def random_config_batch(seed):
+    """(batch, [plan kwargs ...]): a random configuration -- G 1..16, 1..8 kv heads,
+    D 64 / 128, fp16 / bf16, causal or not (non-causal rows may outnumber their keys),
+    sequences with no queries among them, poisoned unowned slots -- with plans on the
+    MFMA and the VALU narrow kernel, cacheable or streamed K/V, as made or split.
+    Also used by the GPU tests."""
+    rng = np.random.default_rng(900 + seed)
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hk = int(rng.choice([1, 2, 4, 8]))
+    while G * Hk > 64:
+        Hk //= 2
+    D = int(rng.choice([64, 128]))
+    causal = bool(rng.random() < 0.7)
+    B = int(rng.integers(1, 16))
+    q, kv = [], []
+    for _ in range(B):
+        r = rng.random()
+        k = int(rng.integers(1, 400))
+        if r < 0.1:
+            q.append(0)                          # a sequence with no queries this call
+        elif r < 0.55:
+            q.append(1)                          # decode row
+        elif causal:
+            q.append(int(rng.integers(1, k + 1)))  # prefill or suffix
+        else:
+            q.append(int(rng.integers(1, k + k // 2 + 2)))  # may outnumber the keys
+        kv.append(k)
+    b = W.make_batch("cfg%d" % seed, q, kv, num_qo_heads=G * Hk, num_kv_heads=Hk, head_dim=D,
+                     dtype=("f16", "bf16")[int(rng.integers(0, 2))], seed=1000 + seed, poison=True,
+                     spare_pages=int(rng.integers(0, 3)), causal=causal)
+    kws = [{}, {"narrow_kernel": "valu"}, {"kv_shared": True, "num_cus": int(rng.choice([2, 64, 4096]))}]
+    return b, kws
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_configurations(seed):
+    b, kws = random_config_batch(seed)
+    for kw in kws:
+        kw = {k: v for k, v in kw.items() if k != "kv_shared"}  # a caching hint: no effect on the plan
+        assert_schedule_matches_oracle(b, plan_for(b, **kw))
+
+
 def _share_prefix(b, pages):
     """The first `pages` page ids of every sequence with that many pages point at the
     first sequence's pages (a prefix stored once; layout only)."""

@@ -1,7 +1,7 @@
 // Stand-ins for the HIP runtime and the kernel launchers, for the sanitizer build of
-// the library's host code (planner and C ABI): the host-only paths the driver takes
+// the library's host code (planner and C ABI): the host-only paths the test program takes
 // make no HIP call, and each stand-in counts any call that happens anyway and fails
-// it, so the driver can check that none did.
+// it, so the test program can check that none did.
 #include <hip/hip_runtime.h>
 
 #include "rpa_launch.h"

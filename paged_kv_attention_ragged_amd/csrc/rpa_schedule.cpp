@@ -90,10 +90,12 @@ void order_wide_for_xcds(std::vector<Piece>& wide) {
 // Work vectors of the calling thread, kept between calls: a plan is rebuilt for every
 // decode step (rpa_plan_update), and fresh multi-page buffers each time would cost more
 // in page faults than the planning itself.
+// (build_schedule binds them to references once per call: in the shared library each
+// access to a thread_local goes through the TLS lookup call.)
 thread_local Schedule t_sched;
-thread_local std::vector<QTile> base;
-thread_local std::vector<Piece> wide, narrow, group;
-thread_local std::vector<std::pair<int32_t, int32_t>> elig;  // (sequence, kv_len) of groupable decode rows
+thread_local std::vector<QTile> t_base;
+thread_local std::vector<Piece> t_wide, t_narrow, t_group;
+thread_local std::vector<std::pair<int32_t, int32_t>> t_elig;  // (sequence, kv_len) of groupable decode rows
 
 }  // namespace
 
@@ -188,6 +190,11 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
     if (p.max_kv_splits < 0) return fail(err, E_ARG, "max_kv_splits must be >= 0");
 
     Schedule& S = t_sched;
+    std::vector<QTile>& base = t_base;
+    std::vector<Piece>& wide = t_wide;
+    std::vector<Piece>& narrow = t_narrow;
+    std::vector<Piece>& group = t_group;
+    std::vector<std::pair<int32_t, int32_t>>& elig = t_elig;
     S.tiles.clear();
     S.merges.clear();
     S.seqtab.clear();

@@ -128,6 +128,27 @@ def _dtype_code(dtype) -> int:
     return {torch.float16: 0, torch.bfloat16: 1}[dtype]
 
 
+def _cuda_tensor(t, name, dtype=None, shape=None, min_numel=None):
+    """Raise ValueError unless t is a contiguous CUDA tensor (of `dtype`, of `shape`, with
+    at least `min_numel` elements): the C ABI takes raw device pointers and cannot check
+    sizes, so a wrong tensor would become out-of-bounds device accesses."""
+    import torch
+    ok = (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()
+          and (dtype is None or t.dtype == dtype) and (shape is None or tuple(t.shape) == tuple(shape))
+          and (min_numel is None or t.numel() >= min_numel))
+    if not ok:
+        want = "a contiguous CUDA tensor"
+        if dtype is not None:
+            want += " of %s" % dtype
+        if shape is not None:
+            want += " of shape %s" % (tuple(shape),)
+        if min_numel is not None:
+            want += " with at least %d elements" % min_numel
+        got = ("%s %s on %s" % (t.dtype, tuple(t.shape), t.device)) if isinstance(t, torch.Tensor) else type(t).__name__
+        raise ValueError("%s must be %s (got %s)" % (name, want, got))
+    return t
+
+
 def version() -> str:
     return load().rpa_version().decode()
 
@@ -208,12 +229,12 @@ class Plan:
         """Upload the schedule into `workspace` (a uint8 CUDA tensor; allocated here
         with torch if None) and borrow `kv_page_indices` (int32 CUDA tensor)."""
         import torch
-        if not (isinstance(kv_page_indices, torch.Tensor) and kv_page_indices.is_cuda
-                and kv_page_indices.dtype == torch.int32 and kv_page_indices.is_contiguous()):
-            raise ValueError("kv_page_indices must be a contiguous int32 CUDA tensor")
+        _cuda_tensor(kv_page_indices, "kv_page_indices", torch.int32,
+                     min_numel=int(self._kp[-1]) if self.batch > 0 else 0)
         need = self.info["workspace_bytes"]
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=kv_page_indices.device)
+        _cuda_tensor(workspace, "workspace", torch.uint8)
         if stream is None:
             stream = torch.cuda.current_stream(kv_page_indices.device)
         _check(load().rpa_plan_bind(self._h, kv_page_indices.data_ptr() if kv_page_indices.numel() else None,
@@ -240,10 +261,11 @@ class Plan:
                              % (self.num_pages, P.page_size, P.num_kv_heads, P.head_dim))
         if out is None:
             out = torch.empty_like(q)
-        elif out.shape != q.shape or out.dtype != dt or not out.is_contiguous():
-            raise ValueError("out must match q")
+        _cuda_tensor(out, "out", dt, tuple(q.shape))
         if return_lse and lse is None:
             lse = torch.empty((T, P.num_qo_heads), dtype=torch.float32, device=q.device)
+        if lse is not None:
+            _cuda_tensor(lse, "lse", torch.float32, (T, P.num_qo_heads))
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         _check(load().rpa_run(self._h, q.data_ptr(), kv_cache.data_ptr(), out.data_ptr(),
@@ -256,6 +278,21 @@ class Plan:
         caller's: q, kv_cache, kv_page_indices (int32), out, and optional lse (fp32)
         and err_flag (int32 [1], OR-ed with error bits)."""
         import torch
+        P = self.params
+        dt = torch.float16 if P.dtype == 0 else torch.bfloat16
+        T = int(self._qo[-1]) if self.batch > 0 else 0
+        _cuda_tensor(q, "q", dt, (T, P.num_qo_heads, P.head_dim))
+        _cuda_tensor(kv_cache, "kv_cache", dt)
+        if kv_cache.dim() != 5 or tuple(kv_cache.shape[1:]) != (2, P.page_size, P.num_kv_heads, P.head_dim):
+            raise ValueError("kv_cache must be [num_pages, %d, %d, %d, %d]" % (2, P.page_size, P.num_kv_heads,
+                                                                             P.head_dim))
+        _cuda_tensor(kv_page_indices, "kv_page_indices", torch.int32,
+                     min_numel=int(self._kp[-1]) if self.batch > 0 else 0)
+        _cuda_tensor(out, "out", dt, tuple(q.shape))
+        if lse is not None:
+            _cuda_tensor(lse, "lse", torch.float32, (T, P.num_qo_heads))
+        if err_flag is not None:
+            _cuda_tensor(err_flag, "err_flag", torch.int32, min_numel=1)
         if stream is None:
             stream = torch.cuda.current_stream(q.device)
         ptr = lambda t: t.data_ptr() if t is not None and t.numel() else None
@@ -270,6 +307,9 @@ class Plan:
         qo, kp, kl = _host_i32(qo_indptr), _host_i32(kv_page_indptr), _host_i32(kv_last_page_len)
         if len(qo) != self.batch + 1 or len(kp) != self.batch + 1 or len(kl) != self.batch:
             raise ValueError("update needs the plan's batch size (%d)" % self.batch)
+        if self._keep and self.batch > 0 and self._keep[0].numel() < int(kp[-1]):
+            raise ValueError("the bound kv_page_indices holds %d entries; the new lengths need %d: bind a "
+                             "larger array" % (self._keep[0].numel(), int(kp[-1])))
         p = lambda a: a.ctypes.data if a.size else None
         _check(load().rpa_plan_update(self._h, p(qo), p(kp), p(kl)))
         self._qo, self._kp, self._kl = qo, kp, kl
@@ -316,12 +356,17 @@ def append_kv(new_kv, kv_cache, append_indptr, kv_page_indptr, kv_page_indices, 
     import torch
     n_new = new_kv.shape[0]
     Hk, D = kv_cache.shape[3], kv_cache.shape[4]
-    if (new_kv.dim() != 4 or tuple(new_kv.shape[1:]) != (2, Hk, D) or new_kv.dtype != kv_cache.dtype
-            or not new_kv.is_contiguous() or not kv_cache.is_contiguous()):
-        raise ValueError("new_kv must be a contiguous [n_new, 2, H_kv, D] tensor of the cache's dtype")
-    for t in (append_indptr, kv_page_indptr, kv_page_indices, kv_last_page_len):
-        if not (t.is_cuda and t.dtype == torch.int32 and t.is_contiguous()):
-            raise ValueError("page-table arrays must be contiguous int32 CUDA tensors")
+    _cuda_tensor(kv_cache, "kv_cache")
+    if kv_cache.dim() != 5 or kv_cache.shape[1:3] != (2, 16):
+        raise ValueError("kv_cache must be [num_pages, 2, 16, H_kv, D]")
+    _cuda_tensor(new_kv, "new_kv", kv_cache.dtype, (n_new, 2, Hk, D))
+    for name, t in (("append_indptr", append_indptr), ("kv_page_indptr", kv_page_indptr),
+                    ("kv_page_indices", kv_page_indices), ("kv_last_page_len", kv_last_page_len)):
+        _cuda_tensor(t, name, torch.int32)
+    if kv_page_indptr.numel() != append_indptr.numel() or kv_last_page_len.numel() != append_indptr.numel() - 1:
+        raise ValueError("append_indptr, kv_page_indptr ([batch + 1]) and kv_last_page_len ([batch]) disagree")
+    if err_flag is not None:
+        _cuda_tensor(err_flag, "err_flag", torch.int32, min_numel=1)
     if stream is None:
         stream = torch.cuda.current_stream(kv_cache.device)
     _check(load().rpa_append_kv(append_indptr.numel() - 1, n_new, Hk, D, append_indptr.data_ptr(),
@@ -358,10 +403,10 @@ def merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
             raise ValueError("lse_a and lse_b must be contiguous fp32 CUDA tensors [rows, H]")
     if out is None:
         out = torch.empty_like(o_a)
-    elif out.shape != o_a.shape or out.dtype != o_a.dtype or not out.is_contiguous():
-        raise ValueError("out must match o_a")
+    _cuda_tensor(out, "out", o_a.dtype, tuple(o_a.shape))
     if lse_out is None:
         lse_out = torch.empty_like(lse_a)
+    _cuda_tensor(lse_out, "lse_out", torch.float32, (rows, H))
     if stream is None:
         stream = torch.cuda.current_stream(o_a.device)
     _check(load().rpa_merge_states(rows, H, D, _dtype_code(o_a.dtype), o_a.data_ptr(), lse_a.data_ptr(),

@@ -480,3 +480,31 @@ def test_tail_skip_switch_changes_no_result(dtype, monkeypatch):
     assert info["num_split_groups"] > 0
     assert_close(o_sp, l_sp, ro, rl, what="no tail skip, split")
     assert_close(o_off, l_off, ro, rl, what="no tail skip")
+
+
+def test_binding_checks_sizes_the_library_cannot():
+    """Sizes the C ABI cannot see: a page-index array shorter than the plan's page
+    table (at bind, and after an update that grows the table), a wrong-shaped LSE
+    buffer, and a wrong-sized output on the allocation-free path are refused in the
+    binding, before any launch."""
+    b = W.tiny_ragged_prefill()
+    q, kv, idx = on_device(b)
+    plan = rpa.Plan(b.qo_indptr, b.kv_page_indptr, b.kv_last_page_len, num_qo_heads=8, num_kv_heads=1,
+                    head_dim=64, dtype="f16")
+    with pytest.raises(ValueError, match="kv_page_indices"):
+        plan.bind(idx[:-1], num_pages=kv.shape[0])
+    plan.bind(idx, num_pages=kv.shape[0])
+    with pytest.raises(ValueError, match="lse"):
+        plan.run(q, kv, lse=torch.empty((q.shape[0], 7), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError, match="out"):
+        plan.run_noalloc(q, kv, idx, torch.empty((q.shape[0] - 1,) + tuple(q.shape[1:]), dtype=q.dtype,
+                                                 device="cuda"))
+    grown = b.kv_page_indptr.copy()
+    grown[-1] += 1  # the last sequence one page longer: more entries than the bound array holds
+    with pytest.raises(ValueError, match="bind a larger array"):
+        plan.update(b.qo_indptr, grown, b.kv_last_page_len)
+    o = plan.run(q, kv)  # the plan is unchanged and still runs
+    torch.cuda.synchronize()
+    plan.check()
+    plan.close()
+    assert torch.isfinite(o.float()).all()

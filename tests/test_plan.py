@@ -650,3 +650,27 @@ def test_shared_prefix_plan_update_and_bounds():
     with pytest.raises(rpa.RPAError) as e:
         make_plan(b0, shared_pages=-1)
     assert e.value.status == "RPA_E_ARG"
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """The C ABI takes raw device pointers; the binding refuses host (CPU) tensors and
+    wrong shapes itself, before anything reaches the library."""
+    b = W.tiny_ragged_prefill()
+    plan = make_plan(b)
+    T, H, D = b.total_q, b.num_qo_heads, b.head_dim
+    idx = torch.from_numpy(b.kv_page_indices.astype(np.int32))
+    with pytest.raises(ValueError, match="kv_page_indices"):
+        plan.bind(idx, num_pages=b.num_pages)
+    with pytest.raises(ValueError, match="q must be"):
+        plan.run(b.q, b.kv_cache)
+    with pytest.raises(ValueError, match="q must be"):
+        plan.run_noalloc(b.q, b.kv_cache, idx, torch.empty_like(b.q))
+    new = torch.zeros((1, 2, 1, D), dtype=b.kv_cache.dtype)
+    i32 = lambda *v: torch.tensor(v, dtype=torch.int32)
+    with pytest.raises(ValueError, match="kv_cache"):
+        rpa.append_kv(new, b.kv_cache, i32(0, 1), i32(0, 2), i32(0, 1), i32(5))
+    o = torch.zeros((T, H, D), dtype=torch.float16)
+    l = torch.zeros((T, H), dtype=torch.float32)
+    with pytest.raises(ValueError, match="o_a and o_b"):
+        rpa.merge_states(o, l, o, l)
+    plan.close()

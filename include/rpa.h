@@ -142,10 +142,15 @@ rpa_status rpa_workspace_bytes(const rpa_params* params, int32_t batch, int64_t 
  * (wide tiles of up to 128 rows, or narrow decode tiles of up to 16) is chosen
  * per sequence: a sequence whose q_len * G rows fit one narrow tile is narrow,
  * every tile of a longer one is wide; narrow tiles whose K/V total at most 8 MiB
- * run as wide tiles when the batch has wide tiles.  A ragged prefill batch and
- * its twin padded to equal lengths (llama.cpp discussion #15958, "Pad for
- * prefill stage?") thus give bit-identical real rows when the ragged batch has a
- * sequence of more than 16 rows and neither run splits key ranges.
+ * run as wide tiles when the batch has wide tiles.  Key ranges are split into
+ * pieces (merged inside the launch; flashinfer issue #323's kv-parallel decode)
+ * only when the tiles are unbalanced -- the longest range above twice the batch's
+ * keys per compute unit (num_cus) -- and then toward one piece per compute unit
+ * (two when the batch has wide tiles); max_kv_splits caps the pieces of a tile.
+ * A ragged prefill batch and its twin padded to equal lengths (llama.cpp
+ * discussion #15958, "Pad for prefill stage?") give bit-identical real rows when
+ * the ragged batch has a sequence of more than 16 rows and neither run splits key
+ * ranges.
  *   qo_indptr_h        host int32 [batch+1]; [0] == 0, non-decreasing
  *   kv_page_indptr_h   host int32 [batch+1]; [0] == 0, non-decreasing
  *   kv_last_page_len_h host int32 [batch]; in [1, page_size] for a sequence with pages

@@ -668,6 +668,30 @@ def oracle_time(b, rows, threads, q_host, kv_host):
     return time.perf_counter() - t0
 
 
+def oracle_full(parts):
+    """The oracle, once, over every row of the mixed long batch (C5), in parts that each
+    fit a bounded run: part k is prompt k's 8192 rows (part 0 also the 256 decode rows),
+    timed in chunks of 1024 rows with a line per chunk; the parts' seconds add up to the
+    full timing.  Not part of the default run (about 29 minutes on 16 cores)."""
+    import oracle
+    import workloads as W
+    b = W.mixed_long_batch()
+    q_host, kv_host = oracle._u16(b.q), oracle._u16(b.kv_cache)
+    threads = len(os.sched_getaffinity(0))
+    model = next((l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")), "?")
+    for k in parts:
+        a, e = int(b.qo_indptr[k]), int(b.qo_indptr[k + 1])
+        rows = list(range(a, e)) + (list(range(int(b.qo_indptr[4]), b.total_q)) if k == 0 else [])
+        total = 0.0
+        for c in range(0, len(rows), 1024):
+            chunk = rows[c:c + 1024]
+            total += oracle_time(b, chunk, threads, q_host, kv_host)
+            log("oracle part %d: rows %d..%d done, %.1f s so far" % (k, chunk[0], chunk[-1], total))
+        flops = 4.0 * b.head_dim * b.num_qo_heads * visible_of_rows(b, rows)
+        print(json.dumps({"oracle_full_part": k, "rows": len(rows), "seconds": total,
+                          "fp64_gflops": flops / total / 1e9, "threads": threads, "cpu_model": model}), flush=True)
+
+
 def visible_of_rows(b, rows):
     """Visible keys of each listed row (causal: its position + 1), summed."""
     seq = np.searchsorted(b.qo_indptr, np.asarray(rows), side="right") - 1
@@ -743,6 +767,10 @@ def main():
                     help="kernel for the headline decode tiles (default: the MFMA one)")
     ap.add_argument("--sweep", action="store_true",
                     help="only the full batch-size sweep at constant total tokens (one JSON line per batch size)")
+    ap.add_argument("--oracle-full", type=str, default=None, metavar="PARTS",
+                    help="only time the fp64 oracle over every row of the mixed long batch on the host "
+                         "cores, for the listed parts (comma-separated of 0-3: prompt k, part 0 also the "
+                         "decode rows; about 7 minutes each on 16 cores); one JSON line per part")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 256 MiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -750,6 +778,9 @@ def main():
         print("bench.py measures one GPU only: the library has no multi-GPU path (the path shards by "
               "sequence or kv head without communication); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.oracle_full is not None:
+        oracle_full([int(x) for x in args.oracle_full.split(",")])
+        return
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     import paged_kv_attention_ragged_amd as rpa

@@ -329,9 +329,12 @@ struct NarrowLds {
 // K^T operand reads (16-byte chunks of 16 rows) and the transposing V reads (8-byte
 // pieces of 4 rows) fall on distinct banks.  V is read with ds_read_b64_tr_b16,
 // which hands each lane 4 keys of one d: the V^T operand, with no transposing store.
-// Each wave software-pipelines: the basic block that computes the exponentials and
-// P V of unit u also issues Q K^T of unit u + 1.  P V runs on fp16: bf16 V is
-// converted in LDS, one unit ahead, by the wave that loaded it.
+// Each wave software-pipelines with one unit of lag between its two products: it
+// issues Q K^T of unit u + 1, then P V of unit u with the softmax of unit u + 1
+// interleaved product by product, so that its own exponentials run beside its own
+// matrix work (a second probability buffer holds the next unit's).  P V runs on fp16: bf16 V is
+// converted in LDS, one unit ahead, by the wave that loaded it, and a barrier makes
+// every wave's share visible before any wave's P V reads it.
 template <int D, bool BF16>
 __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char* smem) {
     using C = WideCfg<D>;
@@ -523,17 +526,10 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     auto ring = [](int x) { return x >= C::NS ? x - C::NS : x; };  // x mod NS, x < 2 NS
     constexpr int NS = C::NS;
 
-    // One unit u in slot u % NS: S holds the scores of u on entry and those of u + 1
-    // (Q K^T, accumulated once the exponentials have used up u's) on exit.
-    auto unit = [&](int u, int slot_u, f32x16& S) {
-        const int SL = slot_u;  // u % NS
-        const int kv0 = T.kv_begin + C::UK * u;
-        // V of unit u + 1 (landed and made visible by the last barrier) goes to fp16
-        // before the next barrier; past the last unit this converts a slot no one reads
-        // again
-        u32x4 vcv[IPW];
-        v_fp16_read(ring(SL + 1), vcv);
-        // mask (boundary units only)
+    // Mask of unit t's scores S: keys past kv_len or past a row's position (boundary
+    // units only).
+    auto mask_unit = [&](int t, f32x16& S) {
+        const int kv0 = T.kv_begin + C::UK * t;
         if ((kv0 + C::UK > T.kv_len) || (A.causal && kv0 + C::UK - 1 > wpos_min)) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -541,32 +537,24 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
                 if (key >= T.kv_len || (A.causal && key > pos)) S[r] = -INFINITY;
             }
         }
-        // row max of the raw scores; lazy rescaling (see kLazy)
+    };
+    // Softmax of a unit's masked scores S, without a branch: the row max, the new
+    // reference max (lazy: a row's moves only when its block max exceeds it by more
+    // than kLazy) and the factor alpha that rescales what was accumulated against the
+    // old one, the probabilities P = exp2(S c - m) in fp16 into pf, and the row sums
+    // lsum = alpha lsum + sum P.  Returns alpha; O is rescaled by the caller once the
+    // P V products that still use the old reference have been issued.
+    auto softmax_unit = [&](f32x16& S, u32x4 (&pf)[2]) -> float {
         float bmax = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) bmax = fmaxf(bmax, S[r]);
         bmax = pair_max(bmax);
         const float bx = bmax * A.c_log2;
-        if (__builtin_amdgcn_ballot_w64(bx > m_run + kLazy)) {
-            const float m_new = bx > m_run + kLazy ? bx : m_run;
-            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            lsum *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-        }
+        const float m_new = bx > m_run + kLazy ? bx : m_run;
+        const float alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        lsum *= alpha;
         const float nm = m_run == -INFINITY ? 0.f : -m_run;
-
-        // request unit u + NS - 1 into the slot unit u - 1 has left
-        const bool more_req = u + NS - 1 < nunits;
-        if (more_req) {
-            load_unit(ring(SL + NS - 1), pg_next);
-        }
-        v_fp16_write(ring(SL + 1), vcv, u + 1 < nunits);
-
-        // ---- one basic block: exponentials of unit u, then Q K^T of unit u + 1 and P V of
-        //      unit u, MFMA by MFMA, each operand read from LDS ahead of its MFMA ----
-        u32x4 pf[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -577,40 +565,134 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
                 lsum = __builtin_amdgcn_fdot2(ph, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum, false);
                 pf[h][e] = __builtin_bit_cast(uint32_t, ph);
             }
-        {
-            static_assert(DK == 2 * DB, "as many Q K^T as P V steps");
-            const char* kp = smem + ring(SL + 1) * SLOT + k_lane;
-            const char* vp = smem + SL * SLOT + v_lane;
-            auto kread = [&](int kk) { return *(const u32x4*)(kp + 32 * R * kk); };
-            auto vread = [&](int i) {  // P V step i: keys 16 (i / DB) .., d block i % DB
-                const int h = i / DB, db = i % DB;
-                const u32x2 lo = ds_read_tr16((const uint16_t*)(vp + ((16 * h) / R) * GS + 64 * R * db));
-                const u32x2 hi = ds_read_tr16((const uint16_t*)(vp + ((16 * h + 8) / R) * GS + 64 * R * db));
-                return u32x4{lo[0], lo[1], hi[0], hi[1]};
-            };
-            constexpr int PF = 2;  // operands in flight ahead of the MFMA that uses them
-            u32x4 kb[DK], vb[DK];
+        return alpha;
+    };
+    // P V of the unit in slot sl with probabilities pf, each V operand read from LDS
+    // ahead of its MFMA.
+    constexpr int PF = 2;  // operands in flight ahead of the MFMA that uses them
+    static_assert(DK == 2 * DB, "as many Q K^T as P V steps");
+    auto pv_unit = [&](int sl, const u32x4 (&pf)[2]) {
+        const char* vp = smem + sl * SLOT + v_lane;
+        auto vread = [&](int i) {  // P V step i: keys 16 (i / DB) .., d block i % DB
+            const int h = i / DB, db = i % DB;
+            const u32x2 lo = ds_read_tr16((const uint16_t*)(vp + ((16 * h) / R) * GS + 64 * R * db));
+            const u32x2 hi = ds_read_tr16((const uint16_t*)(vp + ((16 * h + 8) / R) * GS + 64 * R * db));
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        u32x4 vb[DK];
 #pragma unroll
-            for (int i = 0; i < PF; ++i) {
-                kb[i] = kread(i);
-                vb[i] = vread(i);
+        for (int i = 0; i < PF; ++i) vb[i] = vread(i);
+#pragma unroll
+        for (int i = 0; i < DK; ++i) {
+            if (i + PF < DK) vb[i + PF] = vread(i + PF);
+            oacc[i % DB] = mfma_pv(vb[i], pf[i / DB], oacc[i % DB]);
+        }
+    };
+
+    // P V of the unit in slot sl with probabilities pc, interleaved with the softmax
+    // of the next unit's masked scores S into pn (the same arithmetic, in the same
+    // order, as softmax_unit): after each product the wave issues the product's next
+    // V operand reads and one slice of the softmax, which runs while the product does.
+    // The fences keep the compiler from regrouping the slices.
+    auto pv_softmax = [&](int sl, const u32x4 (&pc)[2], f32x16& S, u32x4 (&pn)[2]) -> float {
+        const char* vp = smem + sl * SLOT + v_lane;
+        auto vread = [&](int i) {
+            const int h = i / DB, db = i % DB;
+            const u32x2 lo = ds_read_tr16((const uint16_t*)(vp + ((16 * h) / R) * GS + 64 * R * db));
+            const u32x2 hi = ds_read_tr16((const uint16_t*)(vp + ((16 * h + 8) / R) * GS + 64 * R * db));
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        u32x4 vb[DK];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) vb[i] = vread(i);
+        float bmax = -INFINITY, alpha = 1.f, nm = 0.f;
+        // softmax slice k of DK: the row max over S[0..7], then over S[8..15] and the new
+        // reference, then the exponentials of the 8 score pairs, spread over the DK - 2
+        // remaining slices (pairs [8 (k - 2) / NE, 8 (k - 1) / NE))
+        constexpr int NE = DK - 2;
+        static_assert(NE >= 1, "at least one slice of exponentials");
+        auto slice = [&](int k) {
+            if (k == 0) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) bmax = fmaxf(bmax, S[r]);
+            } else if (k == 1) {
+#pragma unroll
+                for (int r = 8; r < 16; ++r) bmax = fmaxf(bmax, S[r]);
+                bmax = pair_max(bmax);
+                const float bx = bmax * A.c_log2;
+                const float m_new = bx > m_run + kLazy ? bx : m_run;
+                alpha = m_new == m_run ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                lsum *= alpha;
+                nm = m_run == -INFINITY ? 0.f : -m_run;
+            } else {
+#pragma unroll
+                for (int q = 8 * (k - 2) / NE; q < 8 * (k - 1) / NE; ++q) {
+                    const int h = q / 4, e = q % 4;
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * h + 2 * e], A.c_log2, nm));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * h + 2 * e + 1], A.c_log2, nm));
+                    const fp16x2 ph = __builtin_amdgcn_cvt_pkrtz(p0, p1);
+                    lsum = __builtin_amdgcn_fdot2(ph, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum, false);
+                    pn[h][e] = __builtin_bit_cast(uint32_t, ph);
+                }
             }
+        };
+#pragma unroll
+        for (int i = 0; i < DK; ++i) {
+            if (i + PF < DK) vb[i + PF] = vread(i + PF);
+            oacc[i % DB] = mfma_pv(vb[i], pc[i / DB], oacc[i % DB]);
+            __builtin_amdgcn_sched_barrier(0);
+            slice(i);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return alpha;
+    };
+
+    // Iteration u (slot SL = u % NS, unit u + 1 exists) enters with unit u's
+    // probabilities in pc (its row sums already in lsum), K of unit u + 1 and V of unit
+    // u (fp16) in LDS, and V of unit u + 1 landed as loaded:
+    //   A: request unit u + NS - 1 into the slot unit u - 1 has left; Q K^T of unit
+    //      u + 1 into S, beside the fp16 conversion of V of unit u + 1;
+    //   B: P V of unit u, beside the softmax of unit u + 1 into pn: one basic block, so
+    //      a wave's exponentials issue while its own matrix products run;
+    //   then O is rescaled where a row's reference moved, and the wave waits for its
+    //   loads of unit u + 2 and meets the others at the barrier, which also makes the
+    //   converted V of unit u + 1 visible to every wave.
+    auto unit = [&](int u, int SL, f32x16& S, const u32x4 (&pc)[2], u32x4 (&pn)[2]) {
+        u32x4 vcv[IPW];
+        v_fp16_read(ring(SL + 1), vcv);
+        if (u + NS - 1 < nunits) load_unit(ring(SL + NS - 1), pg_next);
+        {
+            const char* kp = smem + ring(SL + 1) * SLOT + k_lane;
+            auto kread = [&](int kk) { return *(const u32x4*)(kp + 32 * R * kk); };
+            u32x4 kb[DK];
+#pragma unroll
+            for (int i = 0; i < PF; ++i) kb[i] = kread(i);
             S = f32x16{};
 #pragma unroll
             for (int i = 0; i < DK; ++i) {
                 if (i + PF < DK) kb[i + PF] = kread(i + PF);
                 S = mfma_qk(kb[i], qf[i], S, BF16);
-                if (i + PF < DK) vb[i + PF] = vread(i + PF);
-                oacc[i % DB] = mfma_pv(vb[i], pf[i / DB], oacc[i % DB]);
             }
         }
-
+        v_fp16_write(ring(SL + 1), vcv, true);
+        mask_unit(u + 1, S);
+        const float alpha = pv_softmax(SL, pc, S, pn);
+        // (keeps the exponentials in this block, beside the P V products, rather than
+        // sunk past the rescale branch below)
+        asm volatile("" ::"v"(pn[0]), "v"(pn[1]), "v"(lsum));
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+        }
         // pages of unit u + NS (their latency overlaps the wait below)
         if (u + NS < nunits) pages_of(u + NS, pg_next);
-        // unit u + 2 must be in LDS (and slot SL free) before unit u + 1 starts
         if (u + 2 < nunits) {
+            // unit u + 2 must be in LDS (and slot SL free) before unit u + 1's iteration
             sync_unit(u + 2, ring(SL + 2), younger_than(u + 2, u + NS - 1));
             barrier();
+        } else if (BF16) {
+            barrier();  // the last unit's V, converted above by every wave
         }
     };
 
@@ -655,11 +737,22 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             }
             barrier();
         }
-        // one score buffer: unit u's scores are spent on its exponentials before Q K^T
-        // of unit u + 1 accumulates into the same registers
+        // One score buffer (unit u + 1's Q K^T starts once unit u's exponentials have
+        // used its scores up) and two probability buffers: unit u + 1's are formed while
+        // unit u's products still read theirs, then copied over (alternating the buffers
+        // by unrolling kept more registers live than three waves per SIMD allow).
         f32x16 sc;
+        u32x4 pa[2], pb[2];
         qk(0, sc);
-        for (int u = 0, sl = 0; u < nunits; ++u, sl = ring(sl + 1)) unit(u, sl, sc);
+        mask_unit(0, sc);
+        softmax_unit(sc, pa);  // nothing accumulated yet: no rescale
+        int u = 0, sl = 0;
+        for (; u + 1 < nunits; ++u, sl = ring(sl + 1)) {
+            unit(u, sl, sc, pa, pb);
+            pa[0] = pb[0];
+            pa[1] = pb[1];
+        }
+        pv_unit(sl, pa);
     }
 
     if (bad_any && lane == 0) raise_flag(A.err_flag, kErrPage);

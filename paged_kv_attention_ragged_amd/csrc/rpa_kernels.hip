@@ -332,7 +332,7 @@ struct NarrowLds {
 // Each wave software-pipelines with one unit of lag between its two products: it
 // issues Q K^T of unit u + 1, then P V of unit u with the softmax of unit u + 1
 // interleaved product by product, so that its own exponentials run beside its own
-// matrix work (a second probability buffer holds the next unit's).  P V runs on fp16: bf16 V is
+// matrix work.  P V runs on fp16: bf16 V is
 // converted in LDS, one unit ahead, by the wave that loaded it, and a barrier makes
 // every wave's share visible before any wave's P V reads it.
 template <int D, bool BF16>
@@ -589,12 +589,15 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         }
     };
 
-    // P V of the unit in slot sl with probabilities pc, interleaved with the softmax
-    // of the next unit's masked scores S into pn (the same arithmetic, in the same
-    // order, as softmax_unit): after each product the wave issues the product's next
-    // V operand reads and one slice of the softmax, which runs while the product does.
-    // The fences keep the compiler from regrouping the slices.
-    auto pv_softmax = [&](int sl, const u32x4 (&pc)[2], f32x16& S, u32x4 (&pn)[2]) -> float {
+    // P V of the unit in slot sl with its probabilities p, interleaved with the softmax
+    // of the next unit's masked scores S, whose probabilities replace them in p (the
+    // same arithmetic, in the same order, as softmax_unit): after each product the
+    // wave issues the product's next V operand reads and one slice of the softmax,
+    // which runs while the product does.  The exponentials overwrite S; they are
+    // packed into p[0] once the products that read p[0] have been issued, and into
+    // p[1] after the last product.  The fences keep the compiler from regrouping the
+    // slices.
+    auto pv_softmax = [&](int sl, f32x16& S, u32x4 (&p)[2]) -> float {
         const char* vp = smem + sl * SLOT + v_lane;
         auto vread = [&](int i) {
             const int h = i / DB, db = i % DB;
@@ -608,9 +611,20 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         float bmax = -INFINITY, alpha = 1.f, nm = 0.f;
         // softmax slice k of DK: the row max over S[0..7], then over S[8..15] and the new
         // reference, then the exponentials of the 8 score pairs, spread over the DK - 2
-        // remaining slices (pairs [8 (k - 2) / NE, 8 (k - 1) / NE))
+        // remaining slices (pairs [8 (k - 2) / NE, 8 (k - 1) / NE)); slice K0, the first
+        // after the products of p[0] and after the exponentials of pairs 0..3, packs them
         constexpr int NE = DK - 2;
-        static_assert(NE >= 1, "at least one slice of exponentials");
+        constexpr int K3 = 1 + (NE + 1) / 2;  // slice whose exponentials end with pair 3
+        constexpr int K0 = DB > K3 ? DB : K3;
+        static_assert(NE >= 1 && K0 < DK, "a slice of exponentials, and pairs 0..3 packed in the loop");
+        auto pack = [&](int h) {  // pairs 4h .. 4h + 3 to fp16 into p[h], row sums in order
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const fp16x2 ph = __builtin_amdgcn_cvt_pkrtz(S[8 * h + 2 * e], S[8 * h + 2 * e + 1]);
+                lsum = __builtin_amdgcn_fdot2(ph, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum, false);
+                p[h][e] = __builtin_bit_cast(uint32_t, ph);
+            }
+        };
         auto slice = [&](int k) {
             if (k == 0) {
 #pragma unroll
@@ -628,37 +642,35 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             } else {
 #pragma unroll
                 for (int q = 8 * (k - 2) / NE; q < 8 * (k - 1) / NE; ++q) {
-                    const int h = q / 4, e = q % 4;
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * h + 2 * e], A.c_log2, nm));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[8 * h + 2 * e + 1], A.c_log2, nm));
-                    const fp16x2 ph = __builtin_amdgcn_cvt_pkrtz(p0, p1);
-                    lsum = __builtin_amdgcn_fdot2(ph, fp16x2{(__fp16)1.0f, (__fp16)1.0f}, lsum, false);
-                    pn[h][e] = __builtin_bit_cast(uint32_t, ph);
+                    S[2 * q] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * q], A.c_log2, nm));
+                    S[2 * q + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * q + 1], A.c_log2, nm));
                 }
             }
+            if (k == K0) pack(0);
         };
 #pragma unroll
         for (int i = 0; i < DK; ++i) {
             if (i + PF < DK) vb[i + PF] = vread(i + PF);
-            oacc[i % DB] = mfma_pv(vb[i], pc[i / DB], oacc[i % DB]);
+            oacc[i % DB] = mfma_pv(vb[i], p[i / DB], oacc[i % DB]);
             __builtin_amdgcn_sched_barrier(0);
             slice(i);
             __builtin_amdgcn_sched_barrier(0);
         }
+        pack(1);
         return alpha;
     };
 
     // Iteration u (slot SL = u % NS, unit u + 1 exists) enters with unit u's
-    // probabilities in pc (its row sums already in lsum), K of unit u + 1 and V of unit
+    // probabilities in p (its row sums already in lsum), K of unit u + 1 and V of unit
     // u (fp16) in LDS, and V of unit u + 1 landed as loaded:
     //   A: request unit u + NS - 1 into the slot unit u - 1 has left; Q K^T of unit
     //      u + 1 into S, beside the fp16 conversion of V of unit u + 1;
-    //   B: P V of unit u, beside the softmax of unit u + 1 into pn: one basic block, so
+    //   B: P V of unit u, beside the softmax of unit u + 1 into p: one basic block, so
     //      a wave's exponentials issue while its own matrix products run;
     //   then O is rescaled where a row's reference moved, and the wave waits for its
     //   loads of unit u + 2 and meets the others at the barrier, which also makes the
     //   converted V of unit u + 1 visible to every wave.
-    auto unit = [&](int u, int SL, f32x16& S, const u32x4 (&pc)[2], u32x4 (&pn)[2]) {
+    auto unit = [&](int u, int SL, f32x16& S, u32x4 (&p)[2]) {
         u32x4 vcv[IPW];
         v_fp16_read(ring(SL + 1), vcv);
         if (u + NS - 1 < nunits) load_unit(ring(SL + NS - 1), pg_next);
@@ -677,10 +689,10 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         }
         v_fp16_write(ring(SL + 1), vcv, true);
         mask_unit(u + 1, S);
-        const float alpha = pv_softmax(SL, pc, S, pn);
+        const float alpha = pv_softmax(SL, S, p);
         // (keeps the exponentials in this block, beside the P V products, rather than
         // sunk past the rescale branch below)
-        asm volatile("" ::"v"(pn[0]), "v"(pn[1]), "v"(lsum));
+        asm volatile("" ::"v"(p[0]), "v"(p[1]), "v"(lsum));
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
@@ -738,21 +750,16 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             barrier();
         }
         // One score buffer (unit u + 1's Q K^T starts once unit u's exponentials have
-        // used its scores up) and two probability buffers: unit u + 1's are formed while
-        // unit u's products still read theirs, then copied over (alternating the buffers
-        // by unrolling kept more registers live than three waves per SIMD allow).
+        // used its scores up) and one probability buffer (each half refilled once the
+        // products that read it have been issued).
         f32x16 sc;
-        u32x4 pa[2], pb[2];
+        u32x4 pf[2];
         qk(0, sc);
         mask_unit(0, sc);
-        softmax_unit(sc, pa);  // nothing accumulated yet: no rescale
+        softmax_unit(sc, pf);  // nothing accumulated yet: no rescale
         int u = 0, sl = 0;
-        for (; u + 1 < nunits; ++u, sl = ring(sl + 1)) {
-            unit(u, sl, sc, pa, pb);
-            pa[0] = pb[0];
-            pa[1] = pb[1];
-        }
-        pv_unit(sl, pa);
+        for (; u + 1 < nunits; ++u, sl = ring(sl + 1)) unit(u, sl, sc, pf);
+        pv_unit(sl, pf);
     }
 
     if (bad_any && lane == 0) raise_flag(A.err_flag, kErrPage);

@@ -199,8 +199,9 @@ rpa_status rpa_plan_info(const rpa_plan* plan, rpa_plan_info_t* out);
  *   [8] first partial row (-1: writes O directly), [9] sequence, [10] split
  *   index, [11] split count, [12] kind (0: wide, up to 128 rows; 1: narrow, up to
  *   16 rows; 2: a group of [1] decode rows of sequences [9].. over a shared prefix
- *   of [3] keys, then [2] private 32-key steps per member), [13] split group (-1 if
- *   not split), [14..15] reserved.
+ *   of [3] keys, then [2] private 16-key pages per member, two pages per 32-key
+ *   step, so [7] = 32 ceil(([3] / 16 + [1] [2]) / 2)), [13] split group (-1 if not
+ *   split), [14..15] reserved.
  * *n_out receives the number of records in the plan.
  */
 rpa_status rpa_plan_tiles(const rpa_plan* plan, int32_t* out_h, int64_t cap, int64_t* n_out);

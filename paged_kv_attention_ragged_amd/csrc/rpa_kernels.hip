@@ -816,11 +816,14 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
 }
 
 
-// Keys of one 32-key step of a narrow tile (wave-uniform): first key's position, keys
-// that exist from it (masked at or past this count), offset of its first page id in
-// kv_page_indices, and the kGroup member whose rows alone see it (-1: all rows).
+// Keys of one 32-key step of a narrow tile (wave-uniform).  An ordinary tile: first
+// key's position, keys that exist from it (masked at or past this count), offset of
+// its first page id in kv_page_indices.  A kGroup tile, per 16-key block b: keys that
+// exist in it (bv), the offset of its page id (bp) and the member whose rows alone
+// see it (bo; -1: all rows).
 struct StepKeys {
-    int key0, valid, pidx, owner;
+    int key0, valid, pidx;
+    int bv[2], bp[2], bo[2];
 };
 
 // Combine of the 4 waves of a narrow tile (each walked its own keys) and the tile's
@@ -952,35 +955,45 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     // its keys are masked and their V zeroed once landed); a page index outside
     // [0, num_pages) raises the error flag and its keys read as zero K and V.
     constexpr int STRIDE = kWaves * KW;
-    // The keys of the step at (virtual) key v, wave-uniform: the first key's position,
-    // how many of its keys exist (at or past `valid` they are masked and their V
-    // zeroed), where its page ids start in kv_page_indices, and, in a kGroup tile, the
-    // member whose rows alone see it (-1: every row).  An ordinary tile walks its own
-    // keys: v is the key.  A kGroup tile walks S0 shared steps, then pos0 steps per
-    // member over that member's keys past the prefix (page base and length from the
-    // sequence table, scalar loads).
-    const int S0 = GROUP ? (T.kv_len + KW - 1) / KW : 0;
+    // The keys of the step at (virtual) key v, wave-uniform.  An ordinary tile walks
+    // its own keys: v is the key; keys at or past `valid` are masked and their V
+    // zeroed.  A kGroup tile walks 16-key page slots, blocks 2 v / 32 and 2 v / 32 + 1:
+    // the kv_len / 16 shared pages, then pos0 pages per member over that member's keys
+    // past the prefix (page base and length from the sequence table, scalar loads);
+    // slots past a member's keys or past the last member are empty.
+    static_assert(KB == 2, "two 16-key blocks per step");
     auto step_keys = [&](int v) -> StepKeys {
         if constexpr (!GROUP) {
-            return StepKeys{v, T.kv_len - v, T.page_base + (v >> 4), -1};
+            return StepKeys{v, T.kv_len - v, T.page_base + (v >> 4), {0, 0}, {0, 0}, {-1, -1}};
         } else {
+            StepKeys sk{v, 0, 0, {0, 0}, {0, 0}, {-1, -1}};
             // past the last step (the first step of a wave with no keys): nothing to read
-            if (v >= T.kv_end) return StepKeys{v, 0, 0, -1};
-            const int st = v / KW;
-            if (st < S0) return StepKeys{v, min(KW, T.kv_len - v), T.page_base + (v >> 4), -1};
-            // here pos0 > 0, since kv_end = 32 (S0 + q_count pos0) > v; i < q_count
-            const int i = (st - S0) / T.pos0, j = st - S0 - i * T.pos0;
-            const int pb = ((const_i32*)A.seqtab)[2 * (T.seq + i)];
-            const int kvl = ((const_i32*)A.seqtab)[2 * (T.seq + i) + 1];
-            const int key = T.kv_len + KW * j;
-            return StepKeys{key, min(KW, kvl - key), pb + (key >> 4), i};
+            if (v >= T.kv_end) return sk;
+            const int SP = T.kv_len >> 4, NP = T.q_count * T.pos0;  // shared pages, private slots
+#pragma unroll
+            for (int b = 0; b < KB; ++b) {
+                const int slot = (v >> 4) + b;
+                if (slot < SP) {
+                    sk.bv[b] = 16;
+                    sk.bp[b] = T.page_base + slot;
+                } else if (slot < SP + NP) {  // here pos0 > 0
+                    const int i = (slot - SP) / T.pos0, pp = slot - SP - i * T.pos0;
+                    const int pb = ((const_i32*)A.seqtab)[2 * (T.seq + i)];
+                    const int kvl = ((const_i32*)A.seqtab)[2 * (T.seq + i) + 1];
+                    const int key = T.kv_len + 16 * pp;
+                    sk.bv[b] = min(16, kvl - key);
+                    sk.bp[b] = pb + (key >> 4);
+                    sk.bo[b] = i;
+                }
+            }
+            return sk;
         }
     };
     auto pages_of = [&](const StepKeys& sk, int (&pg)[KB]) {
 #pragma unroll
         for (int b = 0; b < KB; ++b) {
             if constexpr (GROUP)
-                pg[b] = 16 * b < sk.valid ? ((const_i32*)A.page_idx)[sk.pidx + b] : 0;
+                pg[b] = sk.bv[b] > 0 ? ((const_i32*)A.page_idx)[sk.bp[b]] : 0;
             else
                 pg[b] = sk.key0 + 16 * b < T.kv_len ? ((const_i32*)A.page_idx)[T.page_base + (sk.key0 >> 4) + b] : 0;
         }
@@ -1031,7 +1044,8 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
     auto fix_v = [&](const StepKeys& sk, int bad) {
 #pragma unroll
         for (int j = 0; j < VJ; ++j) {
-            const bool past = GROUP ? j * KPJ + vkey >= sk.valid : sk.key0 + j * KPJ + vkey >= T.kv_len;
+            const bool past = GROUP ? ((j * KPJ + vkey) & 15) >= sk.bv[(j * KPJ) >> 4]
+                                    : sk.key0 + j * KPJ + vkey >= T.kv_len;
             const bool z = (bad & (1 << ((j * KPJ) >> 4))) || past;
             const uint32_t keep = z ? 0u : ~0u;
             vf[j] &= u32x4{keep, keep, keep, keep};
@@ -1057,7 +1071,8 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
         pages_of(sk_nxt, pg_nxt);
     }
     // (kGroup tiles carry the descriptors of the current and next steps, which cost
-    // scalar loads; an ordinary tile recomputes its own from the key position) through the wave's LDS area (free until its first
+    // scalar loads; an ordinary tile recomputes its own from the key position.)
+    // Q into the MFMA operand layout through the wave's LDS area (free until its first
     // step), while those loads are in flight.
     static_assert(16 * KS <= KW * VS, "Q staging fits the wave's area");
 #pragma unroll
@@ -1105,7 +1120,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
         }
 
         // ---- stage V (fp16, natural layout) ----
-        if (bad_cur || (GROUP ? cur.valid < KW : kbase + KW > T.kv_len)) fix_v(cur, bad_cur);
+        if (bad_cur || (GROUP ? cur.bv[0] < 16 || cur.bv[1] < 16 : kbase + KW > T.kv_len)) fix_v(cur, bad_cur);
         u16x2 vmax = {0, 0};  // largest fp16 |V| pattern of this step (bf16 only)
 #pragma unroll
         for (int j = 0; j < VJ; ++j) {
@@ -1134,7 +1149,7 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
         // ---- online softmax (lane: row `col`, keys 16b + 4grp + i) ----
         // (kGroup rows are decode rows: every key of their steps is at or before their
         // position, so only members and the valid count mask them)
-        const bool need_mask = GROUP ? cur.valid < KW || cur.owner >= 0
+        const bool need_mask = GROUP ? cur.bv[0] < 16 || cur.bv[1] < 16 || cur.bo[0] >= 0 || cur.bo[1] >= 0
                                      : (kbase + KW > T.kv_len) || (A.causal && kbase + KW - 1 > pos_min);
         float bmax = -INFINITY;
 #pragma unroll
@@ -1144,8 +1159,8 @@ __device__ __forceinline__ void narrow_tile(const AttnArgs& A, const Tile& T, ch
                 float x = s[b][i] * A.c_log2;
                 if (need_mask) {
                     if constexpr (GROUP) {
-                        const int koff = 16 * b + 4 * grp + i;
-                        if (koff >= cur.valid || (cur.owner >= 0 && tok != cur.owner)) x = -INFINITY;
+                        const int koff = 4 * grp + i;  // within block b
+                        if (koff >= cur.bv[b] || (cur.bo[b] >= 0 && tok != cur.bo[b])) x = -INFINITY;
                     } else {
                         const int key = kbase + 16 * b + 4 * grp + i;
                         if (key >= T.kv_len || (A.causal && key > pos)) x = -INFINITY;

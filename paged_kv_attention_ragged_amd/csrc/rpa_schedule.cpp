@@ -285,19 +285,21 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
 
     // ---- kGroup tiles: consecutive decode rows over a shared prefix -----------------------
     // Up to group_rows (16 / G) consecutive sequences per tile, so that the prefix is read
-    // once for all of them.  Members' own keys are walked in whole 32-key steps padded to
-    // the longest member; a group ends early rather than pad more than a quarter of its
-    // private steps.  A lone sequence keeps an ordinary narrow tile.
+    // once for all of them.  Members' own keys are walked in 16-key pages, each member's
+    // padded to the longest member's count and two pages per 32-key step, so that a step
+    // may hold the last page of one member and the first of the next; a group ends early
+    // rather than pad more than a quarter of its private pages.  A lone sequence keeps an
+    // ordinary narrow tile.
     if (!elig.empty()) {
-        const int32_t S0 = int32_t(ceil_div(shared_keys, 32));
-        auto priv_steps = [&](int32_t kv_len) { return int32_t(ceil_div(kv_len - shared_keys, 32)); };
+        const int64_t SP = shared_keys / kPageSize;  // shared pages
+        auto priv_pages = [&](int32_t kv_len) { return int32_t(ceil_div(kv_len - shared_keys, kPageSize)); };
         size_t i = 0;
         while (i < elig.size()) {
             size_t j = i + 1;
-            int64_t sum = priv_steps(elig[i].second);
+            int64_t sum = priv_pages(elig[i].second);
             int32_t pmax = int32_t(sum);
             while (j < elig.size() && int64_t(j - i) < group_rows && elig[j].first == elig[j - 1].first + 1) {
-                const int32_t pj = priv_steps(elig[j].second);
+                const int32_t pj = priv_pages(elig[j].second);
                 const int32_t pm = std::max(pmax, pj);
                 if (4 * (sum + pj) < 3 * int64_t(j - i + 1) * pm) break;  // padding would waste > 1/4
                 sum += pj;
@@ -312,12 +314,12 @@ int build_schedule(const PlanParams& p, int32_t batch, const int32_t* qo_indptr,
                     Tile t{};
                     t.q_row0 = qo_indptr[b0];
                     t.q_count = n;
-                    t.pos0 = pmax;  // private steps per member
+                    t.pos0 = pmax;  // private pages per member
                     t.kv_len = int32_t(shared_keys);
                     t.page_base = kv_page_indptr[b0];
                     t.kv_head = hk;
                     t.kv_begin = 0;
-                    t.kv_end = 32 * (S0 + n * pmax);
+                    t.kv_end = int32_t(32 * ceil_div(SP + int64_t(n) * pmax, 2));
                     t.part = -1;
                     t.seq = b0;
                     t.split = 0;

@@ -39,12 +39,13 @@ enum TileKind : int32_t {
 
 // A kGroup tile holds the decode rows (q_len 1) of q_count consecutive sequences
 // seq .. seq + q_count - 1 whose first kv_len keys (the shared prefix, a multiple of
-// 16) lie in the same physical pages.  Its keys are walked as virtual 32-key steps:
-// S0 = ceil(kv_len / 32) shared steps (pages from page_base = the first sequence's
-// kv_page_indptr), visible to every row, then pos0 steps per member sequence i (its
-// own keys kv_len + 32 j, pages from its own page table), visible to its rows only;
-// kv_end = 32 (S0 + q_count pos0).  The members' page bases and lengths come from the
-// per-sequence table (Schedule::seqtab).  Never split.
+// 16) lie in the same physical pages.  Its keys are walked as virtual 16-key page
+// slots, two per 32-key step: slots 0 .. kv_len / 16 - 1 are the shared pages (from
+// page_base = the first sequence's kv_page_indptr), visible to every row; then pos0
+// slots per member sequence i (its own keys kv_len + 16 p, p < pos0, pages from its own
+// page table), visible to its rows only, masked past its length; kv_end = 32 ceil(
+// (kv_len / 16 + q_count pos0) / 2).  The members' page bases and lengths come from
+// the per-sequence table (Schedule::seqtab).  Never split.
 
 // One unit of attention work: the rows (tokens q_row0 .. q_row0+q_count-1, all
 // qo heads of kv head `kv_head`) against keys [kv_begin, kv_end) of one sequence.

@@ -578,14 +578,13 @@ def check_groups(b, plan, shared_pages):
     for r in grp:
         n, b0, hk = int(r[F["q_count"]]), int(r[F["seq"]]), int(r[F["kv_head"]])
         assert 2 <= n and n * G <= 16 and r[F["kv_len"]] == Ks and r[F["n_splits"]] == 1 and r[F["part"]] == -1
-        pm = int(r[F["pos0"]])
-        S0 = -(-Ks // 32)
-        assert r[F["kv_begin"]] == 0 and r[F["kv_end"]] == 32 * (S0 + n * pm)
+        pm = int(r[F["pos0"]])  # private 16-key pages per member, two pages per 32-key step
+        assert r[F["kv_begin"]] == 0 and r[F["kv_end"]] == 32 * -(-(shared_pages + n * pm) // 2)
         assert r[F["q_row0"]] == b.qo_indptr[b0] and r[F["page_base"]] == b.kv_page_indptr[b0]
         for i in range(n):
             s = b0 + i
             assert b.q_lens[s] == 1 and b.kv_lens[s] >= Ks and b.qo_indptr[s] == b.qo_indptr[b0] + i
-            assert 32 * pm >= b.kv_lens[s] - Ks
+            assert 16 * pm >= b.kv_lens[s] - Ks
             assert (s, hk) not in covered
             covered[(s, hk)] = True
     # ungrouped rows keep ordinary tiles: every (token, kv head) exactly once overall
@@ -607,7 +606,9 @@ def test_shared_prefix_decode_rows_are_grouped():
     b = lengths_batch([1] * 256, [231] * 256, H=32, Hk=8)
     p = make_plan(b, shared_pages=12)
     grp = check_groups(b, p, 12)
-    assert len(grp) == 512 and (grp[:, F["q_count"]] == 4).all() and (grp[:, F["pos0"]] == 2).all()
+    # 39 own keys per request: 3 pages, so 12 shared + 4 x 3 private pages = 12 steps
+    assert len(grp) == 512 and (grp[:, F["q_count"]] == 4).all() and (grp[:, F["pos0"]] == 3).all()
+    assert (grp[:, F["kv_end"]] == 32 * 12).all()
     assert p.info["num_tiles"] == 512 and p.info["visible_pairs"] == make_plan(b).info["visible_pairs"]
     # 8 query heads per kv head: pairs; 16 or more: nothing to group
     assert (check_groups(lengths_batch([1] * 9, [300] * 9), make_plan(lengths_batch([1] * 9, [300] * 9),
@@ -632,10 +633,10 @@ def test_shared_prefix_grouping_rules():
     for extra in (0, 3):
         bb = lengths_batch([1] * 40, [16 * 7 + 5 + (i * extra) % 200 for i in range(40)], H=8, Hk=2)
         check_groups(bb, make_plan(bb, shared_pages=7), 7)
-    # odd prefix page counts: the last shared step holds 16 keys
+    # odd prefix page counts: the last shared page and the first private one share a step
     bo = lengths_batch([1] * 12, [16 * 5 + 9] * 12, H=16, Hk=4)
     go = check_groups(bo, make_plan(bo, shared_pages=5), 5)
-    assert len(go) > 0 and (go[:, F["kv_end"]] == 32 * (3 + go[:, F["q_count"]] * 1)).all()
+    assert len(go) > 0 and (go[:, F["kv_end"]] == 32 * ((5 + go[:, F["q_count"]] * 1 + 1) // 2)).all()
 
 
 def test_shared_prefix_plan_update_and_bounds():

@@ -133,12 +133,16 @@ class Executor:
     def _run_group(self, rec, hk, n):
         """kGroup tile: n consecutive decode sequences from rec[SEQ]; the first rec[KV_LEN]
         keys (the declared shared prefix) through the first member's page table, then
-        rec[POS0] 32-key steps of each member's own keys through its own."""
+        rec[POS0] 16-key pages of each member's own keys through its own, all of them
+        walked two pages per 32-key step up to rec[KV_END]."""
         seq0 = int(rec[SEQ])
         shared = int(rec[KV_LEN])
-        steps = int(rec[POS0])
+        pages = int(rec[POS0])
         if rec[PART] != -1:
             raise ScheduleError("kGroup tiles are never split")
+        if shared % 16 or int(rec[KV_END]) != 32 * -(-(shared // 16 + n * pages) // 2):
+            raise ScheduleError("kGroup tile's key range %d does not hold its %d shared keys and %d x %d pages"
+                                % (rec[KV_END], shared, n, pages))
         for mbr in range(n):
             s = seq0 + mbr
             if self.q_lens[s] != 1:
@@ -147,8 +151,10 @@ class Executor:
             if row != int(rec[Q_ROW0]) + mbr:
                 raise ScheduleError("kGroup member %d is not at row %d" % (s, int(rec[Q_ROW0]) + mbr))
             L = int(self.kv_lens[s])
+            if shared + 16 * pages < L:
+                raise ScheduleError("kGroup member %d: %d pages do not cover its %d own keys" % (s, pages, L - shared))
             js = np.arange(0, shared)
-            jp = np.arange(shared, min(L, shared + 32 * steps))
+            jp = np.arange(shared, min(L, shared + 16 * pages))
             K0, V0 = self._kv(int(rec[PAGE_BASE]), js, hk)
             K1, V1 = self._kv(int(self.b.kv_page_indptr[s]), jp, hk)
             K, V = np.concatenate([K0, K1]), np.concatenate([V0, V1])

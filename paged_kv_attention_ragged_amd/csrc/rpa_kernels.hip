@@ -332,9 +332,9 @@ struct NarrowLds {
 // Each wave software-pipelines with one unit of lag between its two products: it
 // issues Q K^T of unit u + 1, then P V of unit u with the softmax of unit u + 1
 // interleaved product by product, so that its own exponentials run beside its own
-// matrix work.  P V runs on fp16: bf16 V is
-// converted in LDS, one unit ahead, by the wave that loaded it, and a barrier makes
-// every wave's share visible before any wave's P V reads it.
+// matrix work.  P V runs on fp16: bf16 V is converted in LDS, one unit ahead, by the
+// wave that loaded it, and a barrier makes every wave's share visible before any
+// wave's P V reads it.
 template <int D, bool BF16>
 __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char* smem) {
     using C = WideCfg<D>;
@@ -567,24 +567,25 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
             }
         return alpha;
     };
-    // P V of the unit in slot sl with probabilities pf, each V operand read from LDS
-    // ahead of its MFMA.
     constexpr int PF = 2;  // operands in flight ahead of the MFMA that uses them
     static_assert(DK == 2 * DB, "as many Q K^T as P V steps");
-    auto pv_unit = [&](int sl, const u32x4 (&pf)[2]) {
+    // V^T operand of P V step i (keys 16 (i / DB) .., d block i % DB) of the unit in slot sl
+    auto vread = [&](int sl, int i) {
         const char* vp = smem + sl * SLOT + v_lane;
-        auto vread = [&](int i) {  // P V step i: keys 16 (i / DB) .., d block i % DB
-            const int h = i / DB, db = i % DB;
-            const u32x2 lo = ds_read_tr16((const uint16_t*)(vp + ((16 * h) / R) * GS + 64 * R * db));
-            const u32x2 hi = ds_read_tr16((const uint16_t*)(vp + ((16 * h + 8) / R) * GS + 64 * R * db));
-            return u32x4{lo[0], lo[1], hi[0], hi[1]};
-        };
+        const int h = i / DB, db = i % DB;
+        const u32x2 lo = ds_read_tr16((const uint16_t*)(vp + ((16 * h) / R) * GS + 64 * R * db));
+        const u32x2 hi = ds_read_tr16((const uint16_t*)(vp + ((16 * h + 8) / R) * GS + 64 * R * db));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    // P V of the unit in slot sl with probabilities pf, each V operand read from LDS
+    // ahead of its MFMA.
+    auto pv_unit = [&](int sl, const u32x4 (&pf)[2]) {
         u32x4 vb[DK];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) vb[i] = vread(i);
+        for (int i = 0; i < PF; ++i) vb[i] = vread(sl, i);
 #pragma unroll
         for (int i = 0; i < DK; ++i) {
-            if (i + PF < DK) vb[i + PF] = vread(i + PF);
+            if (i + PF < DK) vb[i + PF] = vread(sl, i + PF);
             oacc[i % DB] = mfma_pv(vb[i], pf[i / DB], oacc[i % DB]);
         }
     };
@@ -598,16 +599,9 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
     // p[1] after the last product.  The fences keep the compiler from regrouping the
     // slices.
     auto pv_softmax = [&](int sl, f32x16& S, u32x4 (&p)[2]) -> float {
-        const char* vp = smem + sl * SLOT + v_lane;
-        auto vread = [&](int i) {
-            const int h = i / DB, db = i % DB;
-            const u32x2 lo = ds_read_tr16((const uint16_t*)(vp + ((16 * h) / R) * GS + 64 * R * db));
-            const u32x2 hi = ds_read_tr16((const uint16_t*)(vp + ((16 * h + 8) / R) * GS + 64 * R * db));
-            return u32x4{lo[0], lo[1], hi[0], hi[1]};
-        };
         u32x4 vb[DK];
 #pragma unroll
-        for (int i = 0; i < PF; ++i) vb[i] = vread(i);
+        for (int i = 0; i < PF; ++i) vb[i] = vread(sl, i);
         float bmax = -INFINITY, alpha = 1.f, nm = 0.f;
         // softmax slice k of DK: the row max over S[0..7], then over S[8..15] and the new
         // reference, then the exponentials of the 8 score pairs, spread over the DK - 2
@@ -650,7 +644,7 @@ __device__ __forceinline__ void wide_tile(const AttnArgs& A, const Tile& T, char
         };
 #pragma unroll
         for (int i = 0; i < DK; ++i) {
-            if (i + PF < DK) vb[i + PF] = vread(i + PF);
+            if (i + PF < DK) vb[i + PF] = vread(sl, i + PF);
             oacc[i % DB] = mfma_pv(vb[i], p[i / DB], oacc[i % DB]);
             __builtin_amdgcn_sched_barrier(0);
             slice(i);

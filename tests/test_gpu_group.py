@@ -80,6 +80,18 @@ def test_random_grouped_batches_on_the_gpu(seed):
         assert_close(o, l, ro, rl, what="random grouped seed %d %s" % (seed, kw))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_grouped_page_slot_edges_on_the_gpu(dtype):
+    """Group tiles with no private pages and with steps whose two 16-key blocks belong
+    to different members (or to a member's empty padding page), against the oracle."""
+    from tests.test_tile_interp import grouped_page_edges_batch
+    b, P = grouped_page_edges_batch(dtype)
+    ro, rl = oracle.run(**b.oracle_kwargs())
+    o, l, kinds = run_grouped(b, P)
+    assert (kinds == 2).any()
+    assert_close(o, l, ro, rl, what="grouped page-slot edges %s" % dtype)
+
+
 def test_long_shared_prefix_decode_step_grouped():
     """One decode step of 256 requests over a 4096-token shared prefix (256 shared
     pages; the benchmark's long-prefix leg): grouped tiles against the oracle on

@@ -17,7 +17,7 @@ import oracle
 import paged_kv_attention_ragged_amd as rpa
 import workloads as W
 
-from tests.tile_interp import execute, ScheduleError, KIND, KGROUP, N_SPLITS, KV_END, KV_BEGIN, KV_LEN, Q_COUNT, PART
+from tests.tile_interp import execute, ScheduleError, KIND, KGROUP, POS0, N_SPLITS, KV_END, KV_BEGIN, KV_LEN, Q_COUNT, PART
 
 TOL = 1e-12
 
@@ -233,6 +233,33 @@ def random_grouped_batch(seed):
                                    head_dim=int(rng.choice([64, 128])), dtype=("f16", "bf16")[seed % 2],
                                    seed=600 + seed, poison=True, spare_pages=2), P)
     return b, P
+
+
+def grouped_page_edges_batch(dtype="bf16"):
+    """(batch, P): decode rows over an odd shared prefix (P = 5 pages, 80 keys), 4 query
+    heads per kv head, so 4 requests per group tile: a group with no keys of its own
+    (no private page slots: the last shared page shares its step with nothing), and
+    groups whose members own 1, 2, 15, 16, 17, 30-33 or 47 keys, so that a 32-key step
+    holds the last page of one member and the first of the next, or a member's empty
+    padding page.  Also used by the GPU tests."""
+    P = 5
+    own = [0, 0, 0, 0, 16, 17, 20, 30, 1, 16, 2, 15, 31, 32, 33, 47]
+    b = W.make_batch("grp_edges_" + dtype, [1] * len(own), [16 * P + k for k in own], num_qo_heads=8,
+                     num_kv_heads=2, head_dim=128, dtype=dtype, seed=77, poison=True, spare_pages=3)
+    return _share_prefix(b, P), P
+
+
+def test_grouped_page_slot_edges():
+    """grouped_page_edges_batch on the CPU executor: group tiles with zero and with
+    several private pages per member, each against the oracle."""
+    b, P = grouped_page_edges_batch()
+    plan = plan_for(b, shared_pages=P)
+    r = plan.tiles()
+    grp = r[r[:, KIND] == KGROUP]
+    assert len(grp) > 0 and (grp[:, POS0] == 0).any() and (grp[:, POS0] >= 2).any()
+    # no private pages: the 5 shared pages take 3 steps
+    assert (grp[grp[:, POS0] == 0][:, KV_END] == 96).all()
+    assert_schedule_matches_oracle(b, plan)
 
 
 @pytest.mark.parametrize("seed", range(6))

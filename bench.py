@@ -16,10 +16,10 @@ value = KV GB/s = unique KV bytes of valid tokens / step time.
 roofline = the decode kernel's algorithmic bytes per launch (KV + Q + O + LSE +
 page table) / its average duration from HIP events stamped by each dispatch on
 the launch stream, against 8 TB/s HBM; also against the HBM read rate measured
-on the box (floors.hbm_stream_gbs).  traffic = HBM bytes per launch from the
+on this machine (floors.hbm_stream_gbs).  traffic = HBM bytes per launch from the
 rocprofv3 FETCH_SIZE / WRITE_SIZE summary in profiles/, while it was taken on
 the current kernel source.
-floors = measured on the box in this run: an empty launch, a plain HBM read
+floors = measured on this machine in this run: an empty launch, a plain HBM read
 stream, the decode kernel's paged gather alone (its page table, no arithmetic;
 on the headline plan's grid of 128 workgroups and on a split grid of 512), and
 dense bf16 MFMA throughput.
@@ -242,7 +242,7 @@ def measure(b, steps, warmup=3, rotate=1, unique_kv_tokens=None, floors=None, **
 
 
 # ----------------------------------------------------------------------------------------------
-# Floors measured on the box
+# Floors measured on this machine
 # ----------------------------------------------------------------------------------------------
 
 def bench_floors(steps=20):
@@ -656,7 +656,7 @@ def bench_sweep(total_tokens=8192, batches=(1, 2, 4, 8, 16, 32, 64, 128, 256), s
 
 
 # ----------------------------------------------------------------------------------------------
-# CPU baseline: the oracle as it stands, on the machine's host cores
+# CPU baseline: the oracle as it stands, on this machine's host cores
 # ----------------------------------------------------------------------------------------------
 
 def oracle_time(b, rows, threads, q_host, kv_host):

@@ -16,7 +16,7 @@ __global__ __launch_bounds__(256) void empty_kernel() {}
 
 // Plain HBM read: workgroup w reads its own contiguous share of the buffer, 4 KiB
 // per workgroup-wide load, four loads in flight per lane, non-temporal (the fastest
-// of the read shapes measured on the box), and folds the data into one word per lane,
+// of the read shapes measured on MI355X), and folds the data into one word per lane,
 // stored once so that the loads are not dropped.  per16: 16-byte chunks per
 // workgroup, a multiple of 1024.
 __global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ src, int64_t per16, uint32_t* out) {

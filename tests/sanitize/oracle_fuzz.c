@@ -1,4 +1,4 @@
-/* Sanitizer driver for the oracle (test infrastructure): random small ragged batches,
+/* Sanitizer test program for the oracle (test infrastructure): random small ragged batches,
  * valid and invalid, through rpa_oracle_run on 1 and 3 threads, built with
  * AddressSanitizer and UndefinedBehaviorSanitizer.  Exits 0 when every call behaved
  * and outputs of the two thread counts agree bit for bit. */
@@ -70,6 +70,6 @@ int main(void) {
         }
         free(idx); free(q); free(kv); free(o1); free(o3); free(l1); free(l3);
     }
-    printf("oracle driver: %d batches run, %d refused, %d failures\n", ran, refused, failures);
+    printf("oracle fuzz: %d batches run, %d refused, %d failures\n", ran, refused, failures);
     return failures == 0 ? 0 : 1;
 }

@@ -1,4 +1,4 @@
-// Sanitizer driver for the library's host code: random ragged batches (and invalid
+// Sanitizer test program for the library's host code: random ragged batches (and invalid
 // ones) through rpa_plan_create(_shared) / info / tiles / update / destroy,
 // rpa_workspace_bytes, rpa_trim_page_table, rpa_validate_page_table and the size
 // check of rpa_run_noalloc, built with AddressSanitizer and UndefinedBehaviorSanitizer.
@@ -117,7 +117,7 @@ int main(int argc, char** argv) {
     CHECK(rpa_workspace_bytes(&p, 4, -1, 0, &bytes) == RPA_E_ARG);
     rpa_plan_destroy(nullptr);
     CHECK(g_hip_calls == 0);
-    std::printf("planner driver: %lld plans, %lld refused, %d failures, %d HIP calls\n", (long long)plans,
+    std::printf("planner fuzz: %lld plans, %lld refused, %d failures, %d HIP calls\n", (long long)plans,
                 (long long)refused, failures, g_hip_calls);
     return failures == 0 ? 0 : 1;
 }

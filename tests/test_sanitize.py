@@ -27,15 +27,15 @@ def build_and_run(tmp_path, cmd, exe, args=()):
 def test_planner_and_host_abi_under_sanitizers(tmp_path):
     cmd = (["g++", "-std=c++17"] + SAN + ["-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include",
                                           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                                          os.path.join(HERE, "sanitize", "planner_driver.cpp"),
+                                          os.path.join(HERE, "sanitize", "planner_fuzz.cpp"),
                                           os.path.join(HERE, "sanitize", "hip_stubs.cpp"),
                                           os.path.join(CSRC, "rpa_schedule.cpp"), os.path.join(CSRC, "rpa_api.cpp")])
-    out = build_and_run(tmp_path, cmd, "planner_driver", ["300"])
+    out = build_and_run(tmp_path, cmd, "planner_fuzz", ["300"])
     assert "0 failures, 0 HIP calls" in out
 
 
 def test_oracle_under_sanitizers(tmp_path):
     cmd = (["gcc", "-std=c11", "-pthread", "-ffp-contract=off"] + SAN +
-           [os.path.join(HERE, "sanitize", "oracle_driver.c"), os.path.join(ROOT, "oracle", "rpa_oracle.c"), "-lm"])
-    out = build_and_run(tmp_path, cmd, "oracle_driver")
+           [os.path.join(HERE, "sanitize", "oracle_fuzz.c"), os.path.join(ROOT, "oracle", "rpa_oracle.c"), "-lm"])
+    out = build_and_run(tmp_path, cmd, "oracle_fuzz")
     assert "0 failures" in out
